@@ -1,0 +1,171 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts layer forward for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the layer computes, per token t (row of x):
+ *   logits  l[t,e] = sum_h x[t,h] * router_w[e,h] + router_b[e]
+ *   probs   p[t,:] = softmax(l[t,:])
+ *   top-k   S_t    = the top_k experts with the largest logits (descending;
+ *                    equal logits go to the lower expert index)
+ *   weights w[t,j] = p[t,S_tj] / sum_j' p[t,S_tj']
+ *   expert  FFN_e(v) = w_down[e] (silu(w_gate[e] v) * (w_up[e] v)),
+ *           silu(z) = z / (1 + exp(-z))
+ *   out[t]  = sum_j w[t,j] FFN_{S_tj}(x[t]) + sum_s FFN^shared_s(x[t])
+ *
+ * Sources: "Fused MoE kernel on Triton: 5 launches vs 24" (ai-manual.ru),
+ * section "Fused kernel: one operation instead of twenty-four" (the four
+ * fused steps: top-k routing weights, dispatch, engaged-expert compute,
+ * weighted aggregation) and section "Megablocks? It has been obsolete for two
+ * years" (top-k chosen at run time); "llama.cpp: fusing shared experts into
+ * MMVQ" (ai-manual.ru), sections "Shared experts in MoE: what they are and
+ * why they exist" (router + top-k experts; always-on shared experts) and
+ * "How fusing shared experts into MMVQ can speed up inference" (shared experts
+ * computed in the same pass as the routed ones, weights untouched).  The FFN
+ * form (SwiGLU), the softmax scoring, the renormalisation, the weight 1 of
+ * shared experts and the optional router bias are readings: the pages name
+ * the steps but never write their formulas.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *     every buffer; the library allocates no memory and keeps no state.
+ *   - Every device pointer must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  No call synchronises or copies device data to the
+ *     host.  Results are valid once the caller has synchronised the stream.
+ *   - Arguments are validated before anything is enqueued: on any error code
+ *     other than MOE_ERR_HIP nothing has been launched.
+ *   - Calls that share one workspace must not overlap in time (use one
+ *     workspace per stream).
+ *
+ * Workspace contract: the first MOE_WS_ZERO_BYTES bytes of a workspace must
+ * be zero before the workspace is used for the first time (allocate it
+ * zero-filled).  They hold completion counters; every successful call leaves
+ * them at zero again.  After a MOE_ERR_HIP return, zero them again.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2 };
+
+/* execution path (moe_shape_t.path) */
+enum {
+  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill */
+  MOE_PATH_DECODE = 1,  /* weight-streaming mat-vec kernels, any supported dtype, any T */
+  MOE_PATH_PREFILL = 2  /* bf16 MFMA grouped GEMMs; needs x, experts bf16 */
+};
+
+/* return codes */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,       /* a required pointer is NULL, or a forbidden one is not */
+  MOE_ERR_SHAPE = -2,      /* sizes out of range (see moe_shape_t) */
+  MOE_ERR_DTYPE = -3,      /* unsupported dtype or dtype/path combination */
+  MOE_ERR_ALIGN = -4,      /* a device pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,  /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -6         /* a HIP launch failed (hipGetLastError) */
+};
+
+#define MOE_WS_ZERO_BYTES 32768
+
+/*
+ * Layer shape and dtypes.
+ *   T         tokens (rows of x), 0 <= T <= 1048576; T == 0 is a no-op.
+ *   H         hidden size, 32 <= H <= 65536, H % 32 == 0.
+ *   E         routed experts, 1 <= E <= 256.
+ *   I         routed-expert intermediate size, 32 <= I <= 1048576, I % 32 == 0.
+ *   top_k     experts per token, 1 <= top_k <= E, T * top_k <= 16777216.
+ *   n_shared  always-on shared experts, 0 <= n_shared <= 16.
+ *   I_shared  shared-expert intermediate size (same rules as I); ignored
+ *             when n_shared == 0.
+ *   x_dtype   MOE_F32 | MOE_BF16; `out` has the same dtype.
+ *   w_dtype   MOE_F32 | MOE_BF16 | MOE_Q4_0, for routed and shared experts.
+ *   router_dtype  MOE_F32 | MOE_BF16.
+ *   path      MOE_PATH_*.
+ *
+ * Weight layouts (row-major, K contiguous):
+ *   router_w [E, H]; router_b f32 [E] (optional);
+ *   w_gate, w_up [E, I, H]; w_down [E, H, I];
+ *   ws_gate, ws_up [n_shared, I_shared, H]; ws_down [n_shared, H, I_shared].
+ * A MOE_Q4_0 stack [E, N, K] (K % 32 == 0) is one buffer: all nibble bytes
+ * [E, N, K/2] first, then, starting at the next multiple of 256 bytes from
+ * the buffer start, all fp16 scales [E, N, K/32].  In each block of 32 values
+ * along K, value j < 16 is the low nibble of byte j and value j + 16 the high
+ * nibble of byte j; the value is d * (q - 8).  The stored d must satisfy
+ * 8 * |d| <= 65504.
+ */
+typedef struct {
+  int32_t T, H, E, I, top_k;
+  int32_t n_shared, I_shared;
+  int32_t x_dtype, w_dtype, router_dtype;
+  int32_t path;
+} moe_shape_t;
+
+/*
+ * Routing outputs of moe_route.  Flat assignment id f = t * top_k + j.
+ *   topk_ids    int32 [T*top_k]   required; expert of assignment f
+ *   topk_w      f32   [T*top_k]   required; renormalised weight of f
+ *   counts      int32 [E]         or NULL; assignments per expert
+ *   offsets     int32 [E+1]       or NULL; start of each expert's segment in
+ *               the expert-sorted order; segments are padded to multiples of
+ *               tile_m (moe_dispatch_dims)
+ *   sorted_ids  int32 [capacity]  or NULL; flat ids in expert-sorted order,
+ *               ascending f inside a segment; padding and the tail up to
+ *               capacity hold the sentinel T*top_k
+ *   tile_expert int32 [n_tiles]   or NULL; expert owning rows
+ *               [i*tile_m, (i+1)*tile_m) of the sorted order, -1 past offsets[E]
+ *   inv         int32 [T*top_k]   or NULL; position of f in sorted_ids
+ *   active      int32 [E+1]       or NULL; active[0] = number of experts with
+ *               counts > 0, followed by those experts in ascending order
+ */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_ids;
+  int32_t* tile_expert;
+  int32_t* inv;
+  int32_t* active;
+} moe_route_out_t;
+
+/* Bytes of workspace moe_forward / moe_route need for shape *s (host call,
+ * no GPU access).  Returns MOE_OK and writes *bytes, or a validation error. */
+int moe_workspace_size(const moe_shape_t* s, size_t* bytes /* host */);
+
+/* Dimensions of the expert-sorted order for shape *s (host call):
+ * tile_m (padding multiple), capacity = roundup(T*top_k + E*(tile_m-1), tile_m),
+ * n_tiles = capacity / tile_m.  Any output pointer may be NULL. */
+int moe_dispatch_dims(const moe_shape_t* s, int32_t* tile_m /* host */,
+                      int32_t* capacity /* host */, int32_t* n_tiles /* host */);
+
+/* Router and dispatch only: logits, softmax, top-k, renormalisation, and the
+ * expert-sorted order.  x [T,H] (x_dtype), router_w [E,H] (router_dtype),
+ * router_b f32 [E] or NULL.  The expert weights and `path` are not used. */
+int moe_route(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+              const moe_route_out_t* out /* host struct of device pointers */,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* The whole layer forward.  x [T,H] (x_dtype); out [T,H] (x_dtype), which
+ * must not overlap x; router_b may be NULL; ws_gate/ws_up/ws_down must be
+ * NULL exactly when n_shared == 0. */
+int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                const void* w_gate, const void* w_up, const void* w_down,
+                const void* ws_gate, const void* ws_up, const void* ws_down,
+                void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a return code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

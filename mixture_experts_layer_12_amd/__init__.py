@@ -1,0 +1,149 @@
+"""Python binding of the MoE layer C ABI (``include/moe.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``lib/libmoe.so``.  Functions carry the C names (``moe_workspace_size``,
+``moe_dispatch_dims``, ``moe_route``, ``moe_forward``, ``moe_strerror``) and
+accept torch tensors (their ``data_ptr()`` is passed) or raw integer device
+addresses.  PyTorch only provides device memory and the current stream.
+
+There is no fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib")
+LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
+
+# enums of moe.h
+MOE_F32, MOE_BF16, MOE_Q4_0 = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+MOE_WS_ZERO_BYTES = 32768
+
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0}
+EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_strerror")
+
+
+class moe_shape_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "H", "E", "I", "top_k", "n_shared", "I_shared", "x_dtype", "w_dtype", "router_dtype", "path")]
+
+
+class moe_route_out_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_ids", "topk_w", "counts", "offsets", "sorted_ids", "tile_expert", "inv", "active")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {moe_strerror(code)} ({code})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises FileNotFoundError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    lib.moe_workspace_size.argtypes = [P(moe_shape_t), P(sz)]
+    lib.moe_workspace_size.restype = ctypes.c_int
+    lib.moe_dispatch_dims.argtypes = [P(moe_shape_t), P(i32), P(i32), P(i32)]
+    lib.moe_dispatch_dims.restype = ctypes.c_int
+    lib.moe_route.argtypes = [P(moe_shape_t), vp, vp, vp, P(moe_route_out_t), vp, sz, vp]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_strerror.argtypes = [ctypes.c_int]
+    lib.moe_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_shape(T, H, E, I, top_k, n_shared=0, I_shared=0, x_dtype="bf16", w_dtype="bf16",
+               router_dtype="bf16", path=MOE_PATH_AUTO) -> moe_shape_t:
+    conv = lambda d: DTYPES[d] if isinstance(d, str) else int(d)
+    return moe_shape_t(int(T), int(H), int(E), int(I), int(top_k), int(n_shared), int(I_shared),
+                       conv(x_dtype), conv(w_dtype), conv(router_dtype), int(path))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def moe_strerror(code: int) -> str:
+    return load_library().moe_strerror(int(code)).decode()
+
+
+def moe_workspace_size(shape: moe_shape_t) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_workspace_size")
+    return n.value
+
+
+def moe_dispatch_dims(shape: moe_shape_t):
+    """(tile_m, capacity, n_tiles) of the expert-sorted order."""
+    a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().moe_dispatch_dims(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if rc:
+        raise MoeError(rc, "moe_dispatch_dims")
+    return a.value, b.value, c.value
+
+
+def moe_route(shape: moe_shape_t, x, router_w, router_b, out: dict, workspace, ws_bytes=None, stream=None,
+              check=True) -> int:
+    """``out`` maps moe_route_out_t field names to int32/float32 device tensors (or None)."""
+    ro = moe_route_out_t(*[_ptr(out.get(n)) for n, _ in moe_route_out_t._fields_])
+    nb = _nbytes(workspace) if ws_bytes is None else ws_bytes
+    rc = load_library().moe_route(ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b), ctypes.byref(ro),
+                                  _ptr(workspace), nb, _stream(stream))
+    if check and rc:
+        raise MoeError(rc, "moe_route")
+    return rc
+
+
+def moe_forward(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                out, workspace, ws_bytes=None, stream=None, check=True) -> int:
+    nb = _nbytes(workspace) if ws_bytes is None else ws_bytes
+    rc = load_library().moe_forward(ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b),
+                                    _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up),
+                                    _ptr(ws_down), _ptr(out), _ptr(workspace), nb, _stream(stream))
+    if check and rc:
+        raise MoeError(rc, "moe_forward")
+    return rc
+
+
+def alloc_workspace(shape: moe_shape_t, device="cuda"):
+    """A zero-filled workspace of moe_workspace_size(shape) bytes (torch uint8 tensor)."""
+    import torch
+    return torch.zeros(max(moe_workspace_size(shape), MOE_WS_ZERO_BYTES), dtype=torch.uint8, device=device)

@@ -1,0 +1,307 @@
+// C ABI of the MoE layer forward: argument validation, workspace layout, path
+// choice and kernel launches.  Host code only; the kernels live in
+// router.hip, decode.hip and prefill.hip.  See include/moe.h for the contract.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "common.hpp"
+
+namespace moe {
+hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st);
+}  // namespace moe
+
+namespace {
+
+constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (prefill row tile)
+constexpr int kDecodeMaxT = 64;      // tokens per decode pass
+constexpr size_t kAlign = 256;
+constexpr size_t kCounterRouter = 0;          // byte offset in the zero region
+constexpr size_t kCounterDown = 256;          // H/16 <= 4096 ints
+
+size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+long roundup(long n, long m) { return (n + m - 1) / m * m; }
+
+struct Layout {
+  int path;            // MOE_PATH_DECODE | MOE_PATH_PREFILL
+  int Tr;              // tokens per routing pass
+  int cap, n_tiles;    // sorted-order capacity and tiles for Tr tokens
+  size_t logits, topk_ids, topk_w, counts, offsets, cprefix, active, sorted_ids, tile_expert, inv;
+  size_t h, partials, acc;
+  long h_plane;
+  int h_stride;
+  int nsplit;
+  int t_pad;
+  size_t total;
+};
+
+int check_shape(const moe_shape_t* s) {
+  if (!s) return MOE_ERR_NULL;
+  const long T = s->T, H = s->H, E = s->E, I = s->I, k = s->top_k, S = s->n_shared, Is = s->I_shared;
+  if (T < 0 || T > 1048576) return MOE_ERR_SHAPE;
+  if (H < 32 || H > 65536 || H % 32) return MOE_ERR_SHAPE;
+  if (E < 1 || E > 256) return MOE_ERR_SHAPE;
+  if (I < 32 || I > 1048576 || I % 32) return MOE_ERR_SHAPE;
+  if (k < 1 || k > E || T * k > 16777216) return MOE_ERR_SHAPE;
+  if (S < 0 || S > 16) return MOE_ERR_SHAPE;
+  if (S > 0 && (Is < 32 || Is > 1048576 || Is % 32)) return MOE_ERR_SHAPE;
+  if (s->x_dtype != MOE_F32 && s->x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (s->router_dtype != MOE_F32 && s->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_Q4_0) return MOE_ERR_DTYPE;
+  if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_PREFILL) return MOE_ERR_SHAPE;
+  if (s->path == MOE_PATH_PREFILL && (s->x_dtype != MOE_BF16 || s->w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
+  // index arithmetic of the largest buffers stays in 32-bit ranges
+  if (roundup(T * k + E * (kTileM - 1), kTileM) + S * roundup(T, kTileM) > 2147483647L / 8) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int choose_path(const moe_shape_t* s) {
+  if (s->path != MOE_PATH_AUTO) return s->path;
+  if (s->x_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 && s->T > kDecodeMaxT) return MOE_PATH_PREFILL;
+  return MOE_PATH_DECODE;
+}
+
+int decode_steps(int w_dtype, int K) {
+  if (w_dtype == MOE_Q4_0) return (K / 32 + 3) / 4;
+  return w_dtype == MOE_F32 ? K / 16 : K / 32;
+}
+
+// route_only: buffers for moe_route over all T tokens.
+Layout make_layout(const moe_shape_t* s, bool route_only) {
+  Layout L{};
+  L.path = route_only ? MOE_PATH_DECODE : choose_path(s);
+  const int T = s->T, H = s->H, E = s->E, k = s->top_k, S = s->n_shared;
+  const int I = s->I, Is = S > 0 ? s->I_shared : 0;
+  L.Tr = (route_only || L.path == MOE_PATH_PREFILL) ? T : std::min(T, kDecodeMaxT);
+  const int Tr = std::max(L.Tr, 1);
+  L.cap = int(roundup(long(Tr) * k + long(E) * (kTileM - 1), kTileM));
+  L.n_tiles = L.cap / kTileM;
+  size_t off = MOE_WS_ZERO_BYTES;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  L.logits = take(size_t(Tr) * E * 4);
+  L.topk_ids = take(size_t(Tr) * k * 4);
+  L.topk_w = take(size_t(Tr) * k * 4);
+  L.counts = take(size_t(E) * 4);
+  L.offsets = take(size_t(E + 1) * 4);
+  L.cprefix = take(size_t(E + 1) * 4);
+  L.active = take(size_t(E + 1) * 4);
+  L.sorted_ids = take(size_t(L.cap) * 4);
+  L.tile_expert = take(size_t(L.n_tiles) * 4);
+  L.inv = take(size_t(Tr) * k * 4);
+  L.h_stride = std::max(I, Is);
+  if (!route_only && L.path == MOE_PATH_DECODE) {
+    const long rows = long(Tr) * k + long(S) * Tr;
+    L.h_plane = rows * L.h_stride;
+    const size_t elem = s->w_dtype == MOE_Q4_0 ? 2 : 4;   // fp16 | fp32 | bf16 hi + lo planes
+    L.h = take(size_t(L.h_plane) * elem);
+    const int n_rt = H / 16;
+    const long slots = std::min<long>(E, long(Tr) * k);
+    const long steps_max = slots * decode_steps(s->w_dtype, I) + long(S) * (S ? decode_steps(s->w_dtype, Is) : 0);
+    int nsplit = int((2048 + 4L * n_rt - 1) / (4L * n_rt));
+    nsplit = std::max(1, std::min(nsplit, 32));
+    nsplit = int(std::max<long>(1, std::min<long>(nsplit, steps_max / 16)));
+    L.nsplit = nsplit;
+    L.partials = nsplit > 1 ? take(size_t(nsplit) * H * Tr * 4) : 0;
+  }
+  if (!route_only && L.path == MOE_PATH_PREFILL) {
+    L.t_pad = int(roundup(T, kTileM));
+    const long rows = long(L.cap) + long(S) * L.t_pad;
+    L.h_plane = rows * L.h_stride;
+    L.h = take(size_t(L.h_plane) * 2);
+    L.acc = take(size_t(T) * H * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int router_waves(int nblocks) { return nblocks < 64 ? 16 : (nblocks < 256 ? 8 : 4); }
+
+moe::RouteBufs route_bufs(uint8_t* ws, const Layout& L) {
+  moe::RouteBufs rb;
+  rb.logits = reinterpret_cast<float*>(ws + L.logits);
+  rb.topk_ids = reinterpret_cast<int32_t*>(ws + L.topk_ids);
+  rb.topk_w = reinterpret_cast<float*>(ws + L.topk_w);
+  rb.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  rb.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  rb.cprefix = reinterpret_cast<int32_t*>(ws + L.cprefix);
+  rb.active = reinterpret_cast<int32_t*>(ws + L.active);
+  rb.sorted_ids = reinterpret_cast<int32_t*>(ws + L.sorted_ids);
+  rb.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_expert);
+  rb.inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  rb.counter = reinterpret_cast<int*>(ws + kCounterRouter);
+  return rb;
+}
+
+moe::RouterArgs router_args(const moe_shape_t* s, int T, const void* x, const void* wr, const float* b,
+                            const moe::RouteBufs& rb) {
+  moe::RouterArgs a{};
+  a.x = x; a.wr = wr; a.bias = b;
+  a.T = T; a.H = s->H; a.E = s->E; a.k = s->top_k;
+  a.tile_m = kTileM;
+  a.capacity = int(roundup(long(T) * s->top_k + long(s->E) * (kTileM - 1), kTileM));
+  a.n_row_tiles = (s->E + 15) / 16;
+  a.n_col_tiles = (T + 15) / 16;
+  a.zero_f32 = nullptr; a.zero_n = 0;
+  a.rb = rb;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL (or a pointer that must be NULL is not)";
+    case MOE_ERR_SHAPE: return "shape out of range";
+    case MOE_ERR_DTYPE: return "unsupported dtype or dtype/path combination";
+    case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failure";
+    default: return "unknown error code";
+  }
+}
+
+int moe_workspace_size(const moe_shape_t* s, size_t* bytes) {
+  if (!s || !bytes) return MOE_ERR_NULL;
+  int rc = check_shape(s);
+  if (rc) return rc;
+  const Layout a = make_layout(s, false), b = make_layout(s, true);
+  *bytes = std::max(a.total, b.total);
+  return MOE_OK;
+}
+
+int moe_dispatch_dims(const moe_shape_t* s, int32_t* tile_m, int32_t* capacity, int32_t* n_tiles) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  const long cap = roundup(long(s->T) * s->top_k + long(s->E) * (kTileM - 1), kTileM);
+  if (tile_m) *tile_m = kTileM;
+  if (capacity) *capacity = int32_t(cap);
+  if (n_tiles) *n_tiles = int32_t(cap / kTileM);
+  return MOE_OK;
+}
+
+int moe_route(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+              const moe_route_out_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!out || !out->topk_ids || !out->topk_w) return MOE_ERR_NULL;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !router_w || !workspace) return MOE_ERR_NULL;
+  const void* ptrs[] = {x, router_w, router_b, out->topk_ids, out->topk_w, out->counts, out->offsets,
+                        out->sorted_ids, out->tile_expert, out->inv, out->active, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  const Layout L = make_layout(s, true);
+  size_t need = 0;
+  moe_workspace_size(s, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  moe::RouteBufs rb = route_bufs(ws, L);
+  rb.topk_ids = out->topk_ids;
+  rb.topk_w = out->topk_w;
+  if (out->counts) rb.counts = out->counts;
+  if (out->offsets) rb.offsets = out->offsets;
+  if (out->sorted_ids) rb.sorted_ids = out->sorted_ids;
+  if (out->tile_expert) rb.tile_expert = out->tile_expert;
+  if (out->inv) rb.inv = out->inv;
+  if (out->active) rb.active = out->active;
+  moe::RouterArgs a = router_args(s, s->T, x, router_w, router_b, rb);
+  const int nblocks = a.n_row_tiles * a.n_col_tiles;
+  return hip_status(moe::launch_router(a, s->router_dtype, s->x_dtype, router_waves(nblocks),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                const void* w_gate, const void* w_up, const void* w_down,
+                const void* ws_gate, const void* ws_up, const void* ws_down,
+                void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !router_w || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL;
+  const bool has_shared = s->n_shared > 0;
+  if (has_shared != (ws_gate != nullptr) || has_shared != (ws_up != nullptr) || has_shared != (ws_down != nullptr))
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  size_t need = 0;
+  moe_workspace_size(s, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const Layout L = make_layout(s, false);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int xb = s->x_dtype == MOE_F32 ? 4 : 2;
+  const moe::RouteBufs rb = route_bufs(ws, L);
+
+  if (L.path == MOE_PATH_PREFILL) {
+    moe::RouterArgs ra = router_args(s, s->T, x, router_w, router_b, rb);
+    ra.zero_f32 = reinterpret_cast<float*>(ws + L.acc);
+    ra.zero_n = long(s->T) * s->H;
+    const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
+      return MOE_ERR_HIP;
+    moe::PrefillArgs p{};
+    p.x = x;
+    p.wg = static_cast<const uint16_t*>(w_gate); p.wu = static_cast<const uint16_t*>(w_up);
+    p.wd = static_cast<const uint16_t*>(w_down);
+    p.sg = static_cast<const uint16_t*>(ws_gate); p.su = static_cast<const uint16_t*>(ws_up);
+    p.sd = static_cast<const uint16_t*>(ws_down);
+    p.T = s->T; p.H = s->H; p.E = s->E; p.I = s->I; p.k = s->top_k; p.S = s->n_shared;
+    p.Is = has_shared ? s->I_shared : 0;
+    p.capacity = L.cap; p.tile_m = kTileM; p.t_pad = L.t_pad;
+    p.n_row_tiles = L.cap / kTileM + s->n_shared * (L.t_pad / kTileM);
+    p.tile_expert = rb.tile_expert; p.sorted_ids = rb.sorted_ids; p.topk_w = rb.topk_w; p.offsets = rb.offsets;
+    p.h = reinterpret_cast<uint16_t*>(ws + L.h);
+    p.h_stride = L.h_stride;
+    p.acc = reinterpret_cast<float*>(ws + L.acc);
+    p.out = out;
+    return hip_status(moe::launch_prefill(p, s->x_dtype, st));
+  }
+
+  // decode: passes of at most kDecodeMaxT tokens (each token's output depends on that token only)
+  for (int t0 = 0; t0 < s->T; t0 += kDecodeMaxT) {
+    const int Tc = std::min(kDecodeMaxT, s->T - t0);
+    const uint8_t* xc = static_cast<const uint8_t*>(x) + size_t(t0) * s->H * xb;
+    uint8_t* oc = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
+    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb);
+    const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
+      return MOE_ERR_HIP;
+    moe::DecodeArgs d{};
+    d.x = xc;
+    d.wg = static_cast<const uint8_t*>(w_gate); d.wu = static_cast<const uint8_t*>(w_up);
+    d.wd = static_cast<const uint8_t*>(w_down);
+    d.sg = static_cast<const uint8_t*>(ws_gate); d.su = static_cast<const uint8_t*>(ws_up);
+    d.sd = static_cast<const uint8_t*>(ws_down);
+    d.T = Tc; d.H = s->H; d.E = s->E; d.I = s->I; d.k = s->top_k; d.S = s->n_shared;
+    d.Is = has_shared ? s->I_shared : 0;
+    d.n_routed_slots = std::min(s->E, Tc * s->top_k);
+    d.nsplit = L.nsplit;
+    d.active = rb.active; d.counts = rb.counts; d.offsets = rb.offsets; d.cprefix = rb.cprefix;
+    d.sorted_ids = rb.sorted_ids; d.topk_w = rb.topk_w;
+    d.h = ws + L.h;
+    d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
+    d.h_stride = L.h_stride;
+    d.partials = reinterpret_cast<float*>(ws + L.partials);
+    d.counters = reinterpret_cast<int*>(ws + kCounterDown);
+    d.out = oc;
+    const int n_gu_rt = (L.h_stride + 15) / 16;
+    d.n_row_tiles = n_gu_rt;
+    if (moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Device helpers shared by the MoE kernels: vector types, bf16/fp16
+// conversions, CDNA4 MFMA wrappers, Q4_0 dequantisation, and the argument
+// blocks the host passes to each kernel.
+//
+// MFMA operand layout used everywhere (16x16 tiles, wave64):
+//   A operand: lane l supplies row (l % 16) and a k-group g = l / 16;
+//   B operand: lane l supplies column (l % 16) and the same k-group g;
+//   D (4 floats): lane l holds column (l % 16), rows 4*(l/16) + i, i = 0..3.
+// Within one MFMA the k positions a lane supplies are the same for A and B,
+// so any assignment of physical k indices to (g, element) works as long as
+// both operands use it; the kernels pick assignments that keep global loads
+// 16 bytes wide and contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q4 = 2 };
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------ conversions --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// float -> fp16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// 8 floats -> two bf16x8 operands hi + lo with hi + lo == v to ~2^-17 relative.
+__device__ __forceinline__ void split_bf16x8(const float* v, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+    float r0 = v[2 * i] - __uint_as_float(h0 << 16);
+    float r1 = v[2 * i + 1] - __uint_as_float(h1 << 16);
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
+  }
+}
+
+// bf16 pair word -> fp16 pair word (exact for |v| within fp16 range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(bf16_lo(w), bf16_hi(w));
+}
+
+// ------------------------------------------------------------------ MFMA --
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ Q4_0 --
+// One 16-byte block (32 codes, value j < 16 in the low nibble of byte j, value
+// j + 16 in the high nibble) and its fp16 scale d -> four fp16x8 operands:
+// frag 0 = values 0..7, 1 = 8..15, 2 = 16..23, 3 = 24..31, each d * (q - 8).
+// (1024 + q) is formed exactly in fp16 by OR-ing q into the mantissa of 1024;
+// subtracting 1032 then gives q - 8 exactly, and one fp16 multiply by d
+// rounds once.
+
+__device__ __forceinline__ uint32_t q4_pair(uint32_t v) {       // v holds the two codes at bits 0-3, 16-19
+  return (v & 0x000F000Fu) | 0x64006400u;
+}
+
+__device__ __forceinline__ uint32_t q4_scale_pair(uint32_t magic, f16x2_t d2) {
+  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - off;
+  return __builtin_bit_cast(uint32_t, v * d2);
+}
+
+__device__ __forceinline__ void q4_dequant_block(u32x4_t raw, uint16_t d_bits, u32x4_t frag[4]) {
+  _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+  f16x2_t d2 = {d, d};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {           // bytes 0..7 -> frags 0/2, bytes 8..15 -> frags 1/3
+#pragma unroll
+    for (int wi = 0; wi < 2; ++wi) {
+      // reorder bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3] so that the low nibbles of
+      // b0,b1 sit at bits 0-3 / 16-19 and those of b2,b3 at bits 8-11 / 24-27
+      uint32_t w = __builtin_amdgcn_perm(raw[2 * half + wi], raw[2 * half + wi], 0x03010200u);
+      frag[half][2 * wi + 0] = q4_scale_pair(q4_pair(w), d2);
+      frag[half][2 * wi + 1] = q4_scale_pair(q4_pair(w >> 8), d2);
+      frag[half + 2][2 * wi + 0] = q4_scale_pair(q4_pair(w >> 4), d2);
+      frag[half + 2][2 * wi + 1] = q4_scale_pair(q4_pair(w >> 12), d2);
+    }
+  }
+}
+
+// Byte offset of the scale array of a Q4_0 stack [n_mat, N, K].
+__host__ __device__ __forceinline__ size_t q4_scale_offset(long n_mat, long N, long K) {
+  size_t nib = size_t(n_mat) * size_t(N) * size_t(K / 2);
+  return (nib + 255) / 256 * 256;
+}
+
+// ------------------------------------------------------------ utilities --
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ u32x4_t ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x2_t ldg8(const void* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+
+// Device-scope completion counter: returns true in exactly one work-group,
+// the last of `n` to arrive.  Release: every thread's global writes before
+// the call are visible to the last group after it returns true.
+__device__ __forceinline__ bool arrive_last(int* counter, int n, int* lds_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (old == n - 1);
+  }
+  __syncthreads();
+  bool last = *lds_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ void reset_counter(int* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------ kernel arguments --
+
+// Routing state inside the workspace (or caller buffers for moe_route).
+struct RouteBufs {
+  float* logits;        // [T, E]
+  int32_t* topk_ids;    // [T*k]
+  float* topk_w;        // [T*k]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1] padded
+  int32_t* cprefix;     // [E+1] unpadded prefix of counts
+  int32_t* active;      // [E+1]
+  int32_t* sorted_ids;  // [capacity]
+  int32_t* tile_expert; // [n_tiles]
+  int32_t* inv;         // [T*k]
+  int* counter;         // completion counter (zero region)
+};
+
+struct RouterArgs {
+  const void* x;
+  const void* wr;
+  const float* bias;
+  int T, H, E, k;
+  int tile_m, capacity;
+  int n_row_tiles, n_col_tiles;
+  float* zero_f32;      // optional buffer to clear (prefill accumulator), or null
+  long zero_n;          // its length in floats (multiple of 4)
+  RouteBufs rb;
+};
+
+struct DecodeArgs {
+  const void* x;        // [T, H]
+  const uint8_t* wg; const uint8_t* wu; const uint8_t* wd;     // routed stacks
+  const uint8_t* sg; const uint8_t* su; const uint8_t* sd;     // shared stacks
+  int T, H, E, I, k, S, Is;
+  int n_routed_slots;   // min(E, T*k)
+  int n_row_tiles;      // gate/up: ceil(max(I, Is) / 16); down: H / 16
+  int nsplit;           // down: work-groups per output row tile
+  const int32_t* active; const int32_t* counts; const int32_t* offsets; const int32_t* cprefix;
+  const int32_t* sorted_ids; const float* topk_w;
+  void* h;              // activations between the two launches
+  long h_plane;         // elements per plane (bf16 hi/lo planes)
+  int h_stride;         // elements per h row
+  float* partials;      // down: [nsplit][H/16][16][T]
+  int* counters;        // down: per row tile
+  void* out;            // [T, H]
+};
+
+struct PrefillArgs {
+  const void* x;
+  const uint16_t* wg; const uint16_t* wu; const uint16_t* wd;
+  const uint16_t* sg; const uint16_t* su; const uint16_t* sd;
+  int T, H, E, I, k, S, Is;
+  int capacity, tile_m, t_pad;        // routed rows, padding tile, shared rows per expert
+  int n_row_tiles, n_col_tiles;
+  const int32_t* tile_expert; const int32_t* sorted_ids; const float* topk_w; const int32_t* offsets;
+  uint16_t* h;           // [capacity + S*t_pad, h_stride] bf16
+  int h_stride;
+  float* acc;            // [T, H] fp32
+  void* out;
+};
+
+}  // namespace moe

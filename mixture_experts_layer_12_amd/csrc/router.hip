@@ -1,0 +1,327 @@
+// Router: logits GEMV/GEMM on MFMA, then (in the last work-group to finish)
+// softmax, top-k with renormalisation and the dispatch into expert-sorted
+// order.
+//
+// Sources: "Fused MoE kernel on Triton: 5 launches vs 24" (ai-manual.ru),
+// section "Fused kernel: one operation instead of twenty-four": routing
+// (top-k weights) and dispatch each take one launch in the fused design; here
+// both sit in one launch.  "Why MoE on RTX 5090 falls short: a bandwidth
+// measurement" (news.malakhovai.ru), paragraph on the kernel-time split:
+// top-k plus row gathering are a small share of decode time, so this kernel
+// favours few launches and full-chip parallelism for the logits read over
+// cleverness in the top-k.
+//
+// Logits: rows = experts (A operand, router weights), columns = tokens
+// (B operand, x).  One work-group owns a 16-expert x 16-token tile; its waves
+// split H and reduce through LDS.  Accumulation is fp32: bf16 x bf16 products
+// are exact in fp32; fp32 activations against bf16 weights are split into a
+// bf16 hi + lo pair (two MFMAs); fp32 x fp32 uses the fp32 MFMA.
+#include "common.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------- logits ----
+
+template <int RT, int XT>
+__device__ __forceinline__ f32x4_t router_dot(const RouterArgs& a, int rtile, int ctile, int wave, int NW,
+                                              int lane) {
+  const int H = a.H;
+  const int row = rtile * 16 + (lane & 15);
+  const int tok = ctile * 16 + (lane & 15);
+  const int g = lane >> 4;
+  const bool arow = row < a.E;
+  const bool btok = tok < a.T;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (RT == DT_F32) {
+    // 16x16x4 fp32 MFMA; one 16-byte load = 4 k values; step covers 16 k.
+    const int nsteps = H / 16;
+    const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
+    const float* wrow = reinterpret_cast<const float*>(a.wr) + size_t(row) * H;
+    for (int s = s0; s < s1; ++s) {
+      const int k0 = s * 16 + g * 4;
+      u32x4_t av = arow ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (btok) {
+        if constexpr (XT == DT_F32) {
+          u32x4_t t = ldg16(reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) bv[m] = __uint_as_float(t[m]);
+        } else {
+          u32x2_t t = ldg8(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0);
+          bv[0] = bf16_lo(t[0]); bv[1] = bf16_hi(t[0]); bv[2] = bf16_lo(t[1]); bv[3] = bf16_hi(t[1]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma_f32(__uint_as_float(av[m]), bv[m], acc);
+    }
+  } else {
+    // 16x16x32 bf16 MFMA; one 16-byte load = 8 k values; step covers 32 k.
+    const int nsteps = H / 32;
+    const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
+    const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.wr) + size_t(row) * H;
+    for (int s = s0; s < s1; ++s) {
+      const int k0 = s * 32 + g * 8;
+      u32x4_t av = arow ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+      if constexpr (XT == DT_BF16) {
+        u32x4_t bv = btok ? ldg16(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0)
+                          : u32x4_t{0, 0, 0, 0};
+        acc = mfma_bf16(av, bv, acc);
+      } else {
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (btok) {
+          const float* xp = reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0;
+          u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) { v[m] = __uint_as_float(t0[m]); v[m + 4] = __uint_as_float(t1[m]); }
+        }
+        u32x4_t hi, lo;
+        split_bf16x8(v, hi, lo);
+        acc = mfma_bf16(av, hi, acc);
+        acc = mfma_bf16(av, lo, acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------- top-k -----
+
+// Candidate order: larger logit first; equal logits -> lower expert index.
+// NaN logits are treated as -inf so every selected index is a real expert.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ float sanitize(float v) { return v != v ? -__builtin_inff() : v; }
+
+// One thread selects the top-k of one token (E <= 32).
+__device__ void topk_thread(const float* l, int E, int k, int32_t* ids, float* w) {
+  uint32_t taken = 0;
+  float lmax = 0.f, denom = 0.f;
+  for (int j = 0; j < k; ++j) {
+    int bi = 0x7fffffff;
+    float bv = -__builtin_inff();
+    for (int e = 0; e < E; ++e) {
+      if (taken & (1u << e)) continue;
+      float v = sanitize(l[e]);
+      if (better(v, e, bv, bi)) { bv = v; bi = e; }
+    }
+    taken |= 1u << bi;
+    ids[j] = bi;
+    if (j == 0) lmax = bv;
+    // weights: softmax over the selected logits (the full-softmax denominator cancels)
+    float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+    w[j] = z;
+    denom += z;
+  }
+  if (!(denom > 0.f)) {                      // every selected logit was -inf/NaN: equal weights
+    for (int j = 0; j < k; ++j) w[j] = 1.0f / float(k);
+  } else {
+    float r = 1.0f / denom;
+    for (int j = 0; j < k; ++j) w[j] *= r;
+  }
+}
+
+// One wave selects the top-k of one token (any E <= 256).
+__device__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, int lane) {
+  float v[4];
+  bool taken[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    int e = lane + 64 * m;
+    v[m] = e < E ? sanitize(l[e]) : -__builtin_inff();
+    taken[m] = e >= E;
+  }
+  float lmax = 0.f, denom = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      int e = lane + 64 * m;
+      if (!taken[m] && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oi = __shfl_xor(bi, off);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (lane + 64 * m == bi) taken[m] = true;
+    if (j == 0) lmax = bv;
+    // weights: softmax over the selected logits (the full-softmax denominator cancels)
+    float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+    denom += z;
+    if (lane == 0) { ids[j] = bi; w[j] = z; }
+  }
+  if (lane == 0) {
+    if (denom > 0.f) {
+      float r = 1.0f / denom;
+      for (int j = 0; j < k; ++j) w[j] *= r;
+    } else {
+      for (int j = 0; j < k; ++j) w[j] = 1.0f / float(k);
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch ---
+
+// Expert-sorted order, built by one work-group.  Deterministic: the rank of an
+// assignment inside its expert's segment is the number of smaller flat ids
+// routed to the same expert (stable counting sort); no atomics decide order.
+__device__ void dispatch_wg(const RouterArgs& a, int* lds) {
+  const RouteBufs& rb = a.rb;
+  const int E = a.E, n = a.T * a.k, M = a.tile_m;
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wave = tid >> 6, NW = NT >> 6;
+  int* hist = lds;                 // [NW][E]: per-wave counts, then per-wave rank bases
+  int* cnt = hist + NW * E;        // [E]
+  int* off = cnt + E;              // [E+1]
+  const int32_t* ids = rb.topk_ids;
+
+  for (int i = tid; i < NW * E; i += NT) hist[i] = 0;
+  __syncthreads();
+  const int chunk = (n + NW - 1) / NW;
+  const int f0 = min(n, wave * chunk), f1 = min(n, f0 + chunk);
+  for (int f = f0 + lane; f < f1; f += 64) atomicAdd(&hist[wave * E + ids[f]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int s = 0;
+    for (int w = 0; w < NW; ++w) {
+      int c = hist[w * E + e];
+      hist[w * E + e] = s;
+      s += c;
+    }
+    cnt[e] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, cp = 0, na = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = o;
+      rb.offsets[e] = o;
+      rb.cprefix[e] = cp;
+      rb.counts[e] = cnt[e];
+      if (cnt[e] > 0) rb.active[1 + na++] = e;
+      o += (cnt[e] + M - 1) / M * M;
+      cp += cnt[e];
+    }
+    off[E] = o;
+    rb.offsets[E] = o;
+    rb.cprefix[E] = cp;
+    rb.active[0] = na;
+  }
+  __syncthreads();
+  for (int c0 = f0; c0 < f1; c0 += 64) {
+    const int f = c0 + lane;
+    const bool valid = f < f1;
+    const int e = valid ? ids[f] : 0;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    int base = 0;
+    if (valid) base = hist[wave * E + e];
+    if (valid) {
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));
+      const int pos = off[e] + base + rank;
+      rb.sorted_ids[pos] = f;
+      rb.inv[f] = pos;
+    }
+    if (valid && (m >> lane) == 1ull) hist[wave * E + e] = base + __popcll(m);
+  }
+  __syncthreads();
+  for (int e = wave; e < E; e += NW)
+    for (int p = off[e] + cnt[e] + lane; p < off[e + 1]; p += 64) rb.sorted_ids[p] = n;
+  for (int p = off[E] + tid; p < a.capacity; p += NT) rb.sorted_ids[p] = n;
+  const int n_tiles = a.capacity / M;
+  for (int i = tid; i < n_tiles; i += NT) {
+    const int r = i * M;
+    int e = -1;
+    if (r < off[E]) {
+      int lo = 0, hi = E;          // largest e with off[e] <= r
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+      }
+      e = lo;
+    }
+    rb.tile_expert[i] = e;
+  }
+}
+
+// --------------------------------------------------------------- kernel --
+
+template <int RT, int XT>
+__global__ void __launch_bounds__(1024) router_kernel(RouterArgs a) {
+  extern __shared__ int lds[];
+  __shared__ int last_flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
+  const int rtile = blockIdx.x % a.n_row_tiles, ctile = blockIdx.x / a.n_row_tiles;
+
+  // optional side job: clear the prefill accumulator
+  if (a.zero_f32) {
+    const long n4 = a.zero_n / 4;
+    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    for (long i = long(blockIdx.x) * blockDim.x + tid; i < n4; i += long(gridDim.x) * blockDim.x)
+      reinterpret_cast<f32x4_t*>(a.zero_f32)[i] = z;
+  }
+
+  f32x4_t acc = router_dot<RT, XT>(a, rtile, ctile, wave, NW, lane);
+  float* red = reinterpret_cast<float*>(lds);
+  *reinterpret_cast<f32x4_t*>(red + (wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t s = *reinterpret_cast<f32x4_t*>(red + lane * 4);
+    for (int w = 1; w < NW; ++w) s += *reinterpret_cast<f32x4_t*>(red + (w * 64 + lane) * 4);
+    const int tok = ctile * 16 + (lane & 15);
+    if (tok < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = rtile * 16 + (lane >> 4) * 4 + i;
+        if (e < a.E) a.rb.logits[size_t(tok) * a.E + e] = s[i] + (a.bias ? a.bias[e] : 0.f);
+      }
+    }
+  }
+
+  if (!arrive_last(a.rb.counter, gridDim.x, &last_flag)) return;
+
+  // ---- last work-group: top-k for every token, then dispatch
+  const int T = a.T, E = a.E, k = a.k;
+  if (E <= 32) {
+    for (int t = tid; t < T; t += blockDim.x)
+      topk_thread(a.rb.logits + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k);
+  } else {
+    for (int t = wave; t < T; t += NW)
+      topk_wave(a.rb.logits + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k,
+                lane);
+  }
+  __threadfence_block();
+  __syncthreads();
+  dispatch_wg(a, lds);
+  if (tid == 0) reset_counter(a.rb.counter);
+}
+
+// --------------------------------------------------------------- launch --
+
+size_t router_lds_bytes(int NW, int E) {
+  size_t red = size_t(NW) * 64 * 4 * sizeof(float);
+  size_t disp = (size_t(NW) * E + 2 * E + 1) * sizeof(int);
+  return red > disp ? red : disp;
+}
+
+hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st) {
+  dim3 grid(a.n_row_tiles * a.n_col_tiles), block(NW * 64);
+  size_t lds = router_lds_bytes(NW, a.E);
+  if (rdt == DT_F32 && xdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_F32, DT_F32>), grid, block, lds, st, a);
+  else if (rdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_F32, DT_BF16>), grid, block, lds, st, a);
+  else if (xdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_BF16, DT_F32>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((router_kernel<DT_BF16, DT_BF16>), grid, block, lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

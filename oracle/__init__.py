@@ -36,6 +36,7 @@ from .moe import (  # noqa: F401
     silu, swiglu_ffn, moe_forward, moe_forward_tokens, dispatch, dense_gate_matrix,
 )
 from .formats import (  # noqa: F401
-    bf16_to_f64, f16_to_f64, q4_0_decode, weights_to_f64, decode_inputs, decode_workload_inputs,
+    bf16_to_f64, f16_to_f64, q4_0_decode, q4_0_decode_matrix, weights_to_f64, decode_inputs,
+    decode_workload_inputs,
 )
 from .moe import padded_rows  # noqa: F401

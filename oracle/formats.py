@@ -81,3 +81,15 @@ def decode_inputs(inp: dict, T, H, E, I, S, Is, x_dtype, w_dtype, r_dtype) -> di
 def decode_workload_inputs(inp: dict, wl) -> dict:
     """``decode_inputs`` with the sizes and dtypes read from a workload description."""
     return decode_inputs(inp, wl.T, wl.H, wl.E, wl.I, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype)
+
+
+def q4_0_decode_matrix(buf: np.ndarray, n_mat: int, N: int, K: int, e: int) -> np.ndarray:
+    """Matrix e of a Q4_0 SoA stack [n_mat, N, K] -> float64 [N, K] (same reading as q4_0_decode)."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8).reshape(-1)
+    per_nib = N * K // 2
+    nib = buf[e * per_nib:(e + 1) * per_nib].reshape(N, K // 32, 16)
+    q = np.concatenate([(nib & 0x0F).astype(np.int64), (nib >> 4).astype(np.int64)], axis=-1)
+    off = (n_mat * per_nib + 255) // 256 * 256
+    per_sc = N * (K // 32)
+    d = buf[off + 2 * e * per_sc: off + 2 * (e + 1) * per_sc].view(np.float16).astype(np.float64)
+    return (d.reshape(N, K // 32, 1) * (q - 8)).reshape(N, K)

@@ -1,0 +1,145 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
+evaluate the oracle on the same stored inputs, and compare."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+
+def lib():
+    """The binding, with the library built if nothing is built yet."""
+    import mixture_experts_layer_12_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    return m
+
+
+def shape_of(m, wl, path=0):
+    return m.make_shape(wl.T, wl.H, wl.E, wl.I, wl.k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype, path)
+
+
+def run_forward(m, wl, t, path=0, ws=None, out=None):
+    import torch
+    shape = shape_of(m, wl, path)
+    if ws is None:
+        ws = m.alloc_workspace(shape, t["x"].device)
+    if out is None:
+        out = torch.empty_like(t["x"])
+    m.moe_forward(shape, t["x"], t["router_w"], t["router_b"], t["w_gate"], t["w_up"], t["w_down"],
+                  t.get("ws_gate"), t.get("ws_up"), t.get("ws_down"), out, ws)
+    return out
+
+
+def run_route(m, wl, t, ws=None):
+    import torch
+    shape = shape_of(m, wl)
+    dev = t["x"].device
+    tile_m, cap, n_tiles = m.moe_dispatch_dims(shape)
+    n = wl.T * wl.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(topk_ids=torch.full((max(n, 1),), -7, **i32),
+               topk_w=torch.full((max(n, 1),), -7.0, dtype=torch.float32, device=dev),
+               counts=torch.full((wl.E,), -7, **i32), offsets=torch.full((wl.E + 1,), -7, **i32),
+               sorted_ids=torch.full((cap,), -7, **i32), tile_expert=torch.full((n_tiles,), -7, **i32),
+               inv=torch.full((max(n, 1),), -7, **i32), active=torch.full((wl.E + 1,), -7, **i32))
+    if ws is None:
+        ws = m.alloc_workspace(shape, dev)
+    m.moe_route(shape, t["x"], t["router_w"], t["router_b"], out, ws)
+    torch.cuda.synchronize()
+    r = {k: v.cpu().numpy() for k, v in out.items()}
+    r["topk_ids"] = r["topk_ids"][:n].reshape(wl.T, wl.k)
+    r["topk_w"] = r["topk_w"][:n].reshape(wl.T, wl.k)
+    r["inv"] = r["inv"][:n]
+    r["tile_m"] = tile_m
+    return r
+
+
+def to_f64(a) -> np.ndarray:
+    """torch tensor (float32 / bfloat16) -> float64 numpy."""
+    import torch
+    a = a.detach()
+    if a.dtype == torch.bfloat16:
+        return oracle.bf16_to_f64(a.cpu().view(torch.int16).numpy().view(np.uint16))
+    return a.cpu().numpy().astype(np.float64)
+
+
+def relerr(got: np.ndarray, ref: np.ndarray) -> float:
+    """Normwise max relative error: max|got - ref| / max|ref|."""
+    den = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
+
+
+def tolerance(wl) -> float:
+    return 1e-5 if (wl.w_dtype == "f32" and wl.x_dtype == "f32" and wl.r_dtype == "f32") else 1e-2
+
+
+def oracle_layer(wl, inp_np, ids=None):
+    """Full fp64 oracle of a layer call on stored numpy inputs; with ``ids`` the
+    oracle's own renormalised weights are used for the given expert choice."""
+    dec = oracle.decode_workload_inputs(inp_np, wl)
+    l, p, ids_o, w_o = oracle.route(dec["x"], dec["Wr"], dec["b"], wl.k)
+    if ids is None:
+        ids = ids_o
+    w = oracle.renormalize(p, ids)
+    out = oracle.moe_forward_tokens(dec["x"], ids, w, dec["Wg"], dec["Wu"], dec["Wd"], dec["shared"])
+    return dict(out=out, logits=l, p=p, ids=ids_o, w=w_o, ids_used=ids, w_used=w)
+
+
+def check_ids(ids_gpu, logits, k, tau=1e-4):
+    """GPU ids must equal the oracle's except on near-tie tokens, where they must
+    still be a valid top-k (within tau of the k-th largest logit)."""
+    ids_o = oracle.select_topk(logits, k)
+    ties = oracle.near_ties(logits, k, tau)
+    diff = (ids_gpu != ids_o).any(axis=1)
+    bad = diff & ~ties
+    assert not bad.any(), f"ids differ on non-tie tokens {np.nonzero(bad)[0][:10]}"
+    for t in np.nonzero(diff)[0]:
+        kth = np.sort(logits[t])[::-1][k - 1]
+        assert len(set(ids_gpu[t].tolist())) == k
+        assert (logits[t][ids_gpu[t]] >= kth - tau).all()
+    return int(diff.sum()), int(ties.sum())
+
+
+def expert_f64(t, key, wl, e, n_mat, N, K):
+    """Matrix e of a stacked weight tensor (torch, on any device) as float64 [N, K]."""
+    import torch
+    a = t[key]
+    if wl.w_dtype == "q4_0":
+        return oracle.q4_0_decode_matrix(a.cpu().numpy(), n_mat, N, K, e)
+    return to_f64(a[e])
+
+
+def oracle_tokens(wl, t, tokens, ids_gpu=None):
+    """Oracle output of selected tokens only (large workloads), reading weights
+    expert by expert from the torch inputs.  Returns (out [n, H], logits, ids_used)."""
+    x = to_f64(t["x"][tokens])
+    Wr = to_f64(t["router_w"])
+    b = None if t["router_b"] is None else to_f64(t["router_b"])
+    l, p, ids_o, _ = oracle.route(x, Wr, b, wl.k)
+    ids = ids_o if ids_gpu is None else ids_gpu
+    w = oracle.renormalize(p, ids)
+    out = np.zeros((len(tokens), wl.H))
+    for e in np.unique(ids):
+        rows, js = np.nonzero(ids == e)
+        Wg = expert_f64(t, "w_gate", wl, e, wl.E, wl.I, wl.H)
+        Wu = expert_f64(t, "w_up", wl, e, wl.E, wl.I, wl.H)
+        Wd = expert_f64(t, "w_down", wl, e, wl.E, wl.H, wl.I)
+        y = oracle.swiglu_ffn(x[rows], Wg, Wu, Wd)
+        np.add.at(out, rows, w[rows, js][:, None] * y)
+    for s in range(wl.S):
+        Wg = expert_f64(t, "ws_gate", wl, s, wl.S, wl.Is, wl.H)
+        Wu = expert_f64(t, "ws_up", wl, s, wl.S, wl.Is, wl.H)
+        Wd = expert_f64(t, "ws_down", wl, s, wl.S, wl.H, wl.Is)
+        out += oracle.swiglu_ffn(x, Wg, Wu, Wd)
+    return out, l, ids

@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched): the
+library loads, exports every function include/moe.h declares, and rejects bad
+arguments with the documented codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests import helpers as H
+
+
+@pytest.fixture(scope="module")
+def m():
+    return H.lib()
+
+
+def _declared(root):
+    text = open(os.path.join(root, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(m, root):
+    names = _declared(root)
+    assert set(names) == set(m.EXPORTED)
+    lib = m.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding(m, root):
+    text = open(os.path.join(root, "include", "moe.h")).read()
+    assert f"#define MOE_WS_ZERO_BYTES {m.MOE_WS_ZERO_BYTES}" in text
+    for name, val in [("MOE_ERR_WORKSPACE", -5), ("MOE_ERR_HIP", -6), ("MOE_PATH_PREFILL", 2), ("MOE_Q4_0", 2)]:
+        assert re.search(rf"{name}\s*=\s*{val}", text), name
+
+
+def test_strerror(m):
+    assert m.moe_strerror(0) == "ok"
+    assert "workspace" in m.moe_strerror(m.MOE_ERR_WORKSPACE)
+    assert m.moe_strerror(12345) == "unknown error code"
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(H=100), "MOE_ERR_SHAPE"),          # H % 32 != 0
+    (dict(I=0), "MOE_ERR_SHAPE"),
+    (dict(E=0), "MOE_ERR_SHAPE"),
+    (dict(E=257, top_k=2), "MOE_ERR_SHAPE"),
+    (dict(top_k=9), "MOE_ERR_SHAPE"),        # k > E
+    (dict(top_k=0), "MOE_ERR_SHAPE"),
+    (dict(T=-1), "MOE_ERR_SHAPE"),
+    (dict(n_shared=1, I_shared=33), "MOE_ERR_SHAPE"),
+    (dict(x_dtype=2), "MOE_ERR_DTYPE"),      # Q4_0 activations
+    (dict(router_dtype=7), "MOE_ERR_DTYPE"),
+    (dict(w_dtype=5), "MOE_ERR_DTYPE"),
+    (dict(w_dtype=2, path=2), "MOE_ERR_DTYPE"),  # prefill needs bf16 experts
+    (dict(path=3), "MOE_ERR_SHAPE"),
+])
+def test_shape_validation(m, kw, code):
+    base = dict(T=8, H=256, E=8, I=128, top_k=2, n_shared=0, I_shared=0, x_dtype=1, w_dtype=1,
+                router_dtype=1, path=0)
+    base.update(kw)
+    s = m.moe_shape_t(*[base[n] for n, _ in m.moe_shape_t._fields_])
+    n = ctypes.c_size_t(0)
+    assert m.load_library().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == getattr(m, code)
+
+
+def test_workspace_size_and_dims(m):
+    s = m.make_shape(4096, 4096, 8, 14336, 2)
+    tile_m, cap, n_tiles = m.moe_dispatch_dims(s)
+    assert tile_m == 128 and cap == (4096 * 2 + 8 * 127 + 127) // 128 * 128 and n_tiles * tile_m == cap
+    big = m.moe_workspace_size(s)
+    # prefill needs the bf16 activations and the fp32 accumulator
+    assert big >= cap * 14336 * 2 + 4096 * 4096 * 4
+    small = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2))
+    assert m.MOE_WS_ZERO_BYTES < small < big
+
+
+def test_argument_errors_before_launch(m):
+    """Error paths return before any HIP call (safe without a GPU)."""
+    lib = m.load_library()
+    s = m.make_shape(8, 256, 8, 128, 2)
+    fake = 1 << 20                      # never dereferenced: validation fails first
+    nb = m.moe_workspace_size(s)
+    ro = m.moe_route_out_t(fake, fake, None, None, None, None, None, None)
+    # missing weights
+    rc = lib.moe_forward(ctypes.byref(s), fake, fake, None, None, fake, fake, None, None, None, fake, fake, nb, None)
+    assert rc == m.MOE_ERR_NULL
+    # shared weights given with n_shared == 0
+    rc = lib.moe_forward(ctypes.byref(s), fake, fake, None, fake, fake, fake, fake, fake, fake, fake, fake, nb, None)
+    assert rc == m.MOE_ERR_NULL
+    # misaligned pointer
+    rc = lib.moe_forward(ctypes.byref(s), fake + 4, fake, None, fake, fake, fake, None, None, None, fake, fake, nb, None)
+    assert rc == m.MOE_ERR_ALIGN
+    # workspace too small
+    rc = lib.moe_forward(ctypes.byref(s), fake, fake, None, fake, fake, fake, None, None, None, fake, fake, nb - 1, None)
+    assert rc == m.MOE_ERR_WORKSPACE
+    rc = lib.moe_route(ctypes.byref(s), fake, fake, None, ctypes.byref(ro), fake, 16, None)
+    assert rc == m.MOE_ERR_WORKSPACE
+    ro2 = m.moe_route_out_t(None, fake, None, None, None, None, None, None)
+    assert lib.moe_route(ctypes.byref(s), fake, fake, None, ctypes.byref(ro2), fake, nb, None) == m.MOE_ERR_NULL
+    # T == 0 is a no-op that touches nothing
+    s0 = m.make_shape(0, 256, 8, 128, 2)
+    assert lib.moe_forward(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None, None,
+                           0, None) == m.MOE_OK

@@ -282,3 +282,16 @@ def test_near_tie_flagging():
     assert oracle.near_ties(l, 1).tolist() == [True, False, False]
     assert oracle.near_ties(l, 2).tolist() == [True, True, False]
     assert oracle.near_ties(l, 3).tolist() == [True, True, False]
+
+
+def test_q4_0_single_matrix_decode_matches_stack_decode():
+    rng = np.random.default_rng(3)
+    E, N, K = 3, 5, 96
+    q = rng.integers(0, 16, size=(E, N, K), dtype=np.uint8)
+    d = rng.random((E, N, K // 32)).astype(np.float16)
+    buf = synth.q4_0_pack(q, d)
+    full = oracle.q4_0_decode(buf, E, N, K)
+    for e in range(E):
+        assert np.array_equal(oracle.q4_0_decode_matrix(buf, E, N, K, e), full[e])
+    # and both equal d * (q - 8) computed from the unpacked draws
+    assert np.array_equal(full, d.astype(np.float64).repeat(32, axis=-1) * (q.astype(np.float64) - 8))
