@@ -161,6 +161,21 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
                 const void* ws_gate, const void* ws_up, const void* ws_down,
                 void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* moe_forward that also records caller-created HIP events (hipEvent_t,
+ * passed as void*) on `stream` at the stage boundaries of each pass:
+ * events[0] before the first launch, events[i] after launch i.  Launches of
+ * one pass: decode path 1 router+dispatch, 2 gate/up, 3 down+combine;
+ * prefill path 1 router+dispatch, 2 gate/up GEMM, 3 down GEMM + combine,
+ * 4 cast.  A decode call with T > 64 makes several passes; the events then
+ * hold the last pass.  Entries beyond n_events, or NULL entries, are skipped.
+ * Returns MOE_ERR_NULL when events is NULL or n_events < 1; otherwise as
+ * moe_forward.  Meant for stage timing (hipEventElapsedTime). */
+int moe_forward_profiled(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                         const void* w_gate, const void* w_up, const void* w_down,
+                         const void* ws_gate, const void* ws_up, const void* ws_down,
+                         void* out, void* workspace, size_t ws_bytes, void* stream,
+                         void* const* events /* host array of hipEvent_t */, int n_events);
+
 /* Static description of a return code. */
 const char* moe_strerror(int code);
 

@@ -25,7 +25,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 MOE_WS_ZERO_BYTES = 32768
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0}
-EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_strerror")
+EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
+            "moe_strerror")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -65,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route.restype = ctypes.c_int
     lib.moe_forward.argtypes = [P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_profiled.argtypes = [P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                         P(vp), ctypes.c_int]
+    lib.moe_forward_profiled.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -140,6 +144,20 @@ def moe_forward(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up, w_down,
                                     _ptr(ws_down), _ptr(out), _ptr(workspace), nb, _stream(stream))
     if check and rc:
         raise MoeError(rc, "moe_forward")
+    return rc
+
+
+def moe_forward_profiled(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up,
+                         ws_down, out, workspace, events, ws_bytes=None, stream=None, check=True) -> int:
+    """``events``: sequence of raw hipEvent_t handles (ints) recorded at stage boundaries."""
+    nb = _nbytes(workspace) if ws_bytes is None else ws_bytes
+    arr = (ctypes.c_void_p * len(events))(*events)
+    rc = load_library().moe_forward_profiled(ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b),
+                                             _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up),
+                                             _ptr(ws_down), _ptr(out), _ptr(workspace), nb, _stream(stream),
+                                             arr, len(events))
+    if check and rc:
+        raise MoeError(rc, "moe_forward_profiled")
     return rc
 
 

@@ -12,8 +12,9 @@
 
 namespace moe {
 hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st);
-hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st);
-hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
+                         StageMarker* mark);
+hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
 }  // namespace moe
 
 namespace {
@@ -222,10 +223,26 @@ int moe_route(const moe_shape_t* s, const void* x, const void* router_w, const f
                                        static_cast<hipStream_t>(stream)));
 }
 
-int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
-                const void* w_gate, const void* w_up, const void* w_down,
-                const void* ws_gate, const void* ws_up, const void* ws_down,
-                void* out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Records events[i] after launch i of a pass (events[0] before the first launch).
+struct StageEvents : moe::StageMarker {
+  void* const* ev;
+  int n;
+  int next = 0;
+  StageEvents(void* const* e, int k) : ev(e), n(k) {}
+  void mark(hipStream_t st) override {
+    if (ev && next < n && ev[next]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[next]), st);
+    ++next;
+  }
+};
+
+int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                 const void* w_gate, const void* w_up, const void* w_down,
+                 const void* ws_gate, const void* ws_up, const void* ws_down,
+                 void* out, void* workspace, size_t ws_bytes, void* stream, void* const* events, int n_events) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (s->T == 0) return MOE_OK;
@@ -246,12 +263,15 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
   const moe::RouteBufs rb = route_bufs(ws, L);
 
   if (L.path == MOE_PATH_PREFILL) {
+    StageEvents sev{events, n_events};
+    sev.mark(st);
     moe::RouterArgs ra = router_args(s, s->T, x, router_w, router_b, rb);
     ra.zero_f32 = reinterpret_cast<float*>(ws + L.acc);
     ra.zero_n = long(s->T) * s->H;
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
       return MOE_ERR_HIP;
+    sev.mark(st);
     moe::PrefillArgs p{};
     p.x = x;
     p.wg = static_cast<const uint16_t*>(w_gate); p.wu = static_cast<const uint16_t*>(w_up);
@@ -267,7 +287,7 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
     p.h_stride = L.h_stride;
     p.acc = reinterpret_cast<float*>(ws + L.acc);
     p.out = out;
-    return hip_status(moe::launch_prefill(p, s->x_dtype, st));
+    return hip_status(moe::launch_prefill(p, s->x_dtype, st, events ? &sev : nullptr));
   }
 
   // decode: passes of at most kDecodeMaxT tokens (each token's output depends on that token only)
@@ -275,10 +295,13 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
     const int Tc = std::min(kDecodeMaxT, s->T - t0);
     const uint8_t* xc = static_cast<const uint8_t*>(x) + size_t(t0) * s->H * xb;
     uint8_t* oc = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
+    StageEvents sev{events, n_events};
+    sev.mark(st);
     moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb);
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
       return MOE_ERR_HIP;
+    sev.mark(st);
     moe::DecodeArgs d{};
     d.x = xc;
     d.wg = static_cast<const uint8_t*>(w_gate); d.wu = static_cast<const uint8_t*>(w_up);
@@ -299,9 +322,32 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
     d.out = oc;
     const int n_gu_rt = (L.h_stride + 15) / 16;
     d.n_row_tiles = n_gu_rt;
-    if (moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr) != hipSuccess)
+      return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                const void* w_gate, const void* w_up, const void* w_down,
+                const void* ws_gate, const void* ws_up, const void* ws_down,
+                void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(s, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, workspace,
+                      ws_bytes, stream, nullptr, 0);
+}
+
+int moe_forward_profiled(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                         const void* w_gate, const void* w_up, const void* w_down,
+                         const void* ws_gate, const void* ws_up, const void* ws_down,
+                         void* out, void* workspace, size_t ws_bytes, void* stream,
+                         void* const* events, int n_events) {
+  if (!events || n_events < 1) return MOE_ERR_NULL;
+  return forward_impl(s, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, workspace,
+                      ws_bytes, stream, events, n_events);
 }
 
 }  // extern "C"

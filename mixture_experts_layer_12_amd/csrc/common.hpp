@@ -155,6 +155,12 @@ __device__ __forceinline__ void reset_counter(int* counter) {
   __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Host-side hook called after each kernel launch (stage timing).
+struct StageMarker {
+  virtual void mark(hipStream_t st) = 0;
+  virtual ~StageMarker() = default;
+};
+
 // ------------------------------------------------------ kernel arguments --
 
 // Routing state inside the workspace (or caller buffers for moe_route).

@@ -496,30 +496,33 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
 // -------------------------------------------------------------- launch --
 
 template <int WT, int XT, int NCT>
-static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st) {
+static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), g1, b, 0, st, a);
+  if (mark) mark->mark(st);
   dim3 g2(a.H / 16, a.nsplit);
   const size_t lds = size_t(4) * 16 * a.T * sizeof(float);
   hipLaunchKernelGGL((decode_down_kernel<WT, XT, NCT>), g2, b, lds, st, a);
+  if (mark) mark->mark(st);
 }
 
 template <int WT, int XT>
-static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st) {
-  if (a.T <= 16) launch_decode_t<WT, XT, 1>(a, n_gu_row_tiles, st);
-  else launch_decode_t<WT, XT, 4>(a, n_gu_row_tiles, st);
+static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
+  if (a.T <= 16) launch_decode_t<WT, XT, 1>(a, n_gu_row_tiles, st, mark);
+  else launch_decode_t<WT, XT, 4>(a, n_gu_row_tiles, st, mark);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
+                         StageMarker* mark) {
   if (wdt == DT_F32) {
-    if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, n_gu_row_tiles, st);
-    else launch_decode_x<DT_F32, DT_BF16>(a, n_gu_row_tiles, st);
+    if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_F32, DT_BF16>(a, n_gu_row_tiles, st, mark);
   } else if (wdt == DT_BF16) {
-    if (xdt == DT_F32) launch_decode_x<DT_BF16, DT_F32>(a, n_gu_row_tiles, st);
-    else launch_decode_x<DT_BF16, DT_BF16>(a, n_gu_row_tiles, st);
+    if (xdt == DT_F32) launch_decode_x<DT_BF16, DT_F32>(a, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_BF16, DT_BF16>(a, n_gu_row_tiles, st, mark);
   } else {
-    if (xdt == DT_F32) launch_decode_x<DT_Q4, DT_F32>(a, n_gu_row_tiles, st);
-    else launch_decode_x<DT_Q4, DT_BF16>(a, n_gu_row_tiles, st);
+    if (xdt == DT_F32) launch_decode_x<DT_Q4, DT_F32>(a, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_Q4, DT_BF16>(a, n_gu_row_tiles, st, mark);
   }
   return hipGetLastError();
 }

@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(256) cast_kernel(const float* __restrict__ acc
 size_t prefill_gateup_lds() { return size_t(2) * (2 * PF_BN + PF_BM) * PF_LD * sizeof(uint16_t); }
 size_t prefill_down_lds() { return size_t(2) * (2 * PF_BM) * PF_LD * sizeof(uint16_t); }
 
-hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark) {
   // dynamic LDS above 64 KiB must be allowed per kernel (thread-safe one-time set-up)
   static const hipError_t attr_rc = [] {
     hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_gateup_kernel),
@@ -352,14 +352,17 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st) {
   g.n_col_tiles = (nmax + PF_BN - 1) / PF_BN;
   hipLaunchKernelGGL(prefill_gateup_kernel, dim3(g.n_row_tiles * g.n_col_tiles), dim3(256),
                      prefill_gateup_lds(), st, g);
+  if (mark) mark->mark(st);
   PrefillArgs d = a;
   d.n_col_tiles = (a.H + PF_BN - 1) / PF_BN;
   hipLaunchKernelGGL(prefill_down_kernel, dim3(d.n_row_tiles * d.n_col_tiles), dim3(256),
                      prefill_down_lds(), st, d);
+  if (mark) mark->mark(st);
   const long n = long(a.T) * a.H;
   const int blocks = int((n / 4 + 255) / 256);
   if (out_dt == DT_F32) hipLaunchKernelGGL(cast_kernel<DT_F32>, dim3(blocks), dim3(256), 0, st, a.acc, a.out, n);
   else hipLaunchKernelGGL(cast_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, st, a.acc, a.out, n);
+  if (mark) mark->mark(st);
   return hipGetLastError();
 }
 
