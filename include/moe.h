@@ -34,13 +34,9 @@
  *     host.  Results are valid once the caller has synchronised the stream.
  *   - Arguments are validated before anything is enqueued: on any error code
  *     other than MOE_ERR_HIP nothing has been launched.
- *   - Calls that share one workspace must not overlap in time (use one
- *     workspace per stream).
- *
- * Workspace contract: the first MOE_WS_ZERO_BYTES bytes of a workspace must
- * be zero before the workspace is used for the first time (allocate it
- * zero-filled).  They hold completion counters; every successful call leaves
- * them at zero again.  After a MOE_ERR_HIP return, zero them again.
+ *   - The workspace is scratch for one call: no initial contents are
+ *     required and nothing in it survives a call.  Calls that share one
+ *     workspace must not overlap in time (use one workspace per stream).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -72,8 +68,6 @@ enum {
   MOE_ERR_WORKSPACE = -5,  /* workspace smaller than moe_workspace_size() */
   MOE_ERR_HIP = -6         /* a HIP launch failed (hipGetLastError) */
 };
-
-#define MOE_WS_ZERO_BYTES 32768
 
 /*
  * Layer shape and dtypes.
@@ -175,6 +169,10 @@ int moe_forward_profiled(const moe_shape_t* s, const void* x, const void* router
                          const void* ws_gate, const void* ws_up, const void* ws_down,
                          void* out, void* workspace, size_t ws_bytes, void* stream,
                          void* const* events /* host array of hipEvent_t */, int n_events);
+
+/* The hipError_t value behind the most recent MOE_ERR_HIP returned to the
+ * calling thread (0 if there was none).  Host call. */
+int moe_last_hip_error(void);
 
 /* Static description of a return code. */
 const char* moe_strerror(int code);

@@ -22,11 +22,10 @@ MOE_F32, MOE_BF16, MOE_Q4_0 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
-MOE_WS_ZERO_BYTES = 32768
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
-            "moe_strerror")
+            "moe_last_hip_error", "moe_strerror")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -42,7 +41,10 @@ class moe_route_out_t(ctypes.Structure):
 class MoeError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {moe_strerror(code)} ({code})")
+        msg = f"{where}: {moe_strerror(code)} ({code})"
+        if code == MOE_ERR_HIP:
+            msg += f"; {hip_error_name(moe_last_hip_error())}"
+        super().__init__(msg)
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -69,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_profiled.argtypes = [P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                          P(vp), ctypes.c_int]
     lib.moe_forward_profiled.restype = ctypes.c_int
+    lib.moe_last_hip_error.argtypes = []
+    lib.moe_last_hip_error.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -105,6 +109,21 @@ def _nbytes(t) -> int:
 
 def moe_strerror(code: int) -> str:
     return load_library().moe_strerror(int(code)).decode()
+
+
+def moe_last_hip_error() -> int:
+    return int(load_library().moe_last_hip_error())
+
+
+def hip_error_name(err: int) -> str:
+    """hipGetErrorName of a hipError_t value (from the HIP runtime)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipGetErrorName.restype = ctypes.c_char_p
+        hip.hipGetErrorName.argtypes = [ctypes.c_int]
+        return f"hipError {err} ({hip.hipGetErrorName(err).decode()})"
+    except OSError:
+        return f"hipError {err}"
 
 
 def moe_workspace_size(shape: moe_shape_t) -> int:
@@ -162,6 +181,6 @@ def moe_forward_profiled(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up
 
 
 def alloc_workspace(shape: moe_shape_t, device="cuda"):
-    """A zero-filled workspace of moe_workspace_size(shape) bytes (torch uint8 tensor)."""
+    """A workspace of moe_workspace_size(shape) bytes (torch uint8 tensor; contents irrelevant)."""
     import torch
-    return torch.zeros(max(moe_workspace_size(shape), MOE_WS_ZERO_BYTES), dtype=torch.uint8, device=device)
+    return torch.empty(max(moe_workspace_size(shape), 256), dtype=torch.uint8, device=device)

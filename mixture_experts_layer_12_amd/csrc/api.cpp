@@ -22,8 +22,9 @@ namespace {
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (prefill row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
 constexpr size_t kAlign = 256;
-constexpr size_t kCounterRouter = 0;          // byte offset in the zero region
-constexpr size_t kCounterDown = 256;          // H/16 <= 4096 ints
+#ifndef MOE_DOWN_WAVES
+#define MOE_DOWN_WAVES 8192                   // target waves of the decode down launch
+#endif
 
 size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 long roundup(long n, long m) { return (n + m - 1) / m * m; }
@@ -82,7 +83,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
   const int Tr = std::max(L.Tr, 1);
   L.cap = int(roundup(long(Tr) * k + long(E) * (kTileM - 1), kTileM));
   L.n_tiles = L.cap / kTileM;
-  size_t off = MOE_WS_ZERO_BYTES;
+  size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
   L.logits = take(size_t(Tr) * E * 4);
   L.topk_ids = take(size_t(Tr) * k * 4);
@@ -103,8 +104,8 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     const int n_rt = H / 16;
     const long slots = std::min<long>(E, long(Tr) * k);
     const long steps_max = slots * decode_steps(s->w_dtype, I) + long(S) * (S ? decode_steps(s->w_dtype, Is) : 0);
-    int nsplit = int((2048 + 4L * n_rt - 1) / (4L * n_rt));
-    nsplit = std::max(1, std::min(nsplit, 32));
+    int nsplit = int((MOE_DOWN_WAVES + 4L * n_rt - 1) / (4L * n_rt));
+    nsplit = std::max(1, std::min(nsplit, 64));
     nsplit = int(std::max<long>(1, std::min<long>(nsplit, steps_max / 16)));
     L.nsplit = nsplit;
     L.partials = nsplit > 1 ? take(size_t(nsplit) * H * Tr * 4) : 0;
@@ -122,7 +123,13 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = int(e);
+  return MOE_ERR_HIP;
+}
 
 int router_waves(int nblocks) { return nblocks < 64 ? 16 : (nblocks < 256 ? 8 : 4); }
 
@@ -138,7 +145,6 @@ moe::RouteBufs route_bufs(uint8_t* ws, const Layout& L) {
   rb.sorted_ids = reinterpret_cast<int32_t*>(ws + L.sorted_ids);
   rb.tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_expert);
   rb.inv = reinterpret_cast<int32_t*>(ws + L.inv);
-  rb.counter = reinterpret_cast<int*>(ws + kCounterRouter);
   return rb;
 }
 
@@ -172,6 +178,8 @@ const char* moe_strerror(int code) {
     default: return "unknown error code";
   }
 }
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
 
 int moe_workspace_size(const moe_shape_t* s, size_t* bytes) {
   if (!s || !bytes) return MOE_ERR_NULL;
@@ -269,8 +277,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     ra.zero_f32 = reinterpret_cast<float*>(ws + L.acc);
     ra.zero_n = long(s->T) * s->H;
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
-      return MOE_ERR_HIP;
+    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
     moe::PrefillArgs p{};
     p.x = x;
@@ -299,8 +306,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     sev.mark(st);
     moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb);
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    if (moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st) != hipSuccess)
-      return MOE_ERR_HIP;
+    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
     moe::DecodeArgs d{};
     d.x = xc;
@@ -318,12 +324,11 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
     d.h_stride = L.h_stride;
     d.partials = reinterpret_cast<float*>(ws + L.partials);
-    d.counters = reinterpret_cast<int*>(ws + kCounterDown);
     d.out = oc;
     const int n_gu_rt = (L.h_stride + 15) / 16;
     d.n_row_tiles = n_gu_rt;
-    if (moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr) != hipSuccess)
-      return MOE_ERR_HIP;
+    if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))
+      return e;
   }
   return MOE_OK;
 }

@@ -135,26 +135,6 @@ __device__ __forceinline__ u32x2_t ldg8(const void* p) {
   return *reinterpret_cast<const u32x2_t*>(p);
 }
 
-// Device-scope completion counter: returns true in exactly one work-group,
-// the last of `n` to arrive.  Release: every thread's global writes before
-// the call are visible to the last group after it returns true.
-__device__ __forceinline__ bool arrive_last(int* counter, int n, int* lds_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *lds_flag = (old == n - 1);
-  }
-  __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-__device__ __forceinline__ void reset_counter(int* counter) {
-  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Host-side hook called after each kernel launch (stage timing).
 struct StageMarker {
   virtual void mark(hipStream_t st) = 0;
@@ -175,7 +155,6 @@ struct RouteBufs {
   int32_t* sorted_ids;  // [capacity]
   int32_t* tile_expert; // [n_tiles]
   int32_t* inv;         // [T*k]
-  int* counter;         // completion counter (zero region)
 };
 
 struct RouterArgs {
@@ -203,8 +182,7 @@ struct DecodeArgs {
   void* h;              // activations between the two launches
   long h_plane;         // elements per plane (bf16 hi/lo planes)
   int h_stride;         // elements per h row
-  float* partials;      // down: [nsplit][H/16][16][T]
-  int* counters;        // down: per row tile
+  float* partials;      // down: [nsplit][T][H] when nsplit > 1
   void* out;            // [T, H]
 };
 

@@ -24,10 +24,12 @@
 //   down:     grid (row tile of 16 hidden outputs, split).  The waves of all
 //             splits of one row tile share the (slot, k) space of that row
 //             tile evenly; each wave folds its partial outputs into a private
-//             LDS accumulator indexed by token, the work-group sums its waves
-//             in a fixed order, and the last work-group of the row tile sums
-//             the splits in a fixed order and writes `out` once.  The combine
-//             is therefore deterministic and needs no atomics on data.
+//             LDS accumulator indexed by token and the work-group sums its
+//             waves in a fixed order.  With one split the work-group writes
+//             `out`; otherwise it writes its split's partial and a small
+//             combine launch sums the splits in a fixed order.  The combine is
+//             deterministic, needs no atomics, and needs no device-wide fence
+//             (the kernel boundary orders the partials and their sum).
 //
 // Matrix cores do the dot products: weights are the A operand (16 rows per
 // wave tile), tokens the B operand (16 per column tile).  bf16 weights use the
@@ -200,9 +202,19 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT
 }
 
 // Unroll depth: keep several 16-byte weight loads in flight per lane.
+#ifndef MOE_GU_UNROLL_BF16
+#define MOE_GU_UNROLL_BF16 8
+#endif
+#ifndef MOE_DN_UNROLL_BF16
+#define MOE_DN_UNROLL_BF16 16
+#endif
 template <int WT, int NCT>
 struct Unroll {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? 8 : 2) : (NCT == 1 ? 4 : 1);
+  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 4 : 1);
+};
+template <int WT, int NCT>
+struct UnrollDown {
+  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 4) : (NCT == 1 ? 8 : 2);
 };
 
 // ------------------------------------------------------------- gate/up --
@@ -372,7 +384,6 @@ __device__ __forceinline__ f32x4_t mma_h(const AReady<WT>& a, const HFrag<WT>& b
 template <int WT, int OT, int NCT>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   extern __shared__ float acc_lds[];     // [4 waves][16 rows][T]
-  __shared__ int last_flag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int rt = blockIdx.x, split = blockIdx.y;
   const int T = a.T, g = lane >> 4, H = a.H;
@@ -387,7 +398,7 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   long pos = total * gw / G;
   const long r1 = total * (gw + 1) / G;
   const int row = rt * 16 + (lane & 15);
-  constexpr int U = Unroll<WT, NCT>::v;
+  constexpr int U = UnrollDown<WT, NCT>::v;
 
   while (pos < r1) {
     int e, n_e, hrow0, seg = 0, K, sstep, sl_steps;
@@ -464,33 +475,38 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // waves -> work-group partial, in wave order (region of wave 0 reused)
-  const int n_rt = H / 16;
+  // waves -> work-group sum, in wave order (region of wave 0 reused)
   for (int idx = tid; idx < 16 * T; idx += 256) {
     float v = acc_lds[idx];
 #pragma unroll
     for (int w = 1; w < 4; ++w) v += acc_lds[w * 16 * T + idx];
-    if (a.nsplit == 1) acc_lds[idx] = v;
-    else a.partials[(size_t(split) * n_rt + rt) * 16 * T + idx] = v;
-  }
-  if (a.nsplit > 1) {
-    // splits -> row tile, in split order, by the last work-group to arrive
-    if (!arrive_last(&a.counters[rt], a.nsplit, &last_flag)) return;
-    for (int idx = tid; idx < 16 * T; idx += 256) {
-      float v = 0.f;
-      for (int sp = 0; sp < a.nsplit; ++sp) v += a.partials[(size_t(sp) * n_rt + rt) * 16 * T + idx];
-      acc_lds[idx] = v;
-    }
-    if (tid == 0) reset_counter(&a.counters[rt]);
+    acc_lds[idx] = v;
   }
   __syncthreads();
   for (int j = tid; j < 16 * T; j += 256) {
     const int t = j >> 4, r = j & 15;
     const float v = acc_lds[r * T + t];
     const size_t o = size_t(t) * H + rt * 16 + r;
-    if constexpr (OT == DT_F32) reinterpret_cast<float*>(a.out)[o] = v;
-    else reinterpret_cast<uint16_t*>(a.out)[o] = uint16_t(f32_to_bf16(v));
+    if (a.nsplit > 1) {
+      a.partials[size_t(split) * T * H + o] = v;      // summed by decode_combine_kernel
+    } else if constexpr (OT == DT_F32) {
+      reinterpret_cast<float*>(a.out)[o] = v;
+    } else {
+      reinterpret_cast<uint16_t*>(a.out)[o] = uint16_t(f32_to_bf16(v));
+    }
   }
+}
+
+// Sum of the split partials [nsplit][T*H] in split order -> out (4 outputs per thread).
+template <int OT>
+__global__ void __launch_bounds__(256) decode_combine_kernel(const float* __restrict__ partials, void* out,
+                                                             int nsplit, long n) {
+  const long i4 = long(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i4 * 4 >= n) return;
+  f32x4_t v = reinterpret_cast<const f32x4_t*>(partials)[i4];
+  for (int sp = 1; sp < nsplit; ++sp) v += reinterpret_cast<const f32x4_t*>(partials + size_t(sp) * n)[i4];
+  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(out)[i4] = v;
+  else reinterpret_cast<u32x2_t*>(out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
 }
 
 // -------------------------------------------------------------- launch --
@@ -503,6 +519,11 @@ static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
   dim3 g2(a.H / 16, a.nsplit);
   const size_t lds = size_t(4) * 16 * a.T * sizeof(float);
   hipLaunchKernelGGL((decode_down_kernel<WT, XT, NCT>), g2, b, lds, st, a);
+  if (a.nsplit > 1) {
+    const long n = long(a.T) * a.H;
+    hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n / 4 + 255) / 256)), b, 0, st, a.partials, a.out,
+                       a.nsplit, n);
+  }
   if (mark) mark->mark(st);
 }
 

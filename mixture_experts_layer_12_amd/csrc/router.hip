@@ -37,47 +37,72 @@ __device__ __forceinline__ f32x4_t router_dot(const RouterArgs& a, int rtile, in
     const int nsteps = H / 16;
     const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
     const float* wrow = reinterpret_cast<const float*>(a.wr) + size_t(row) * H;
-    for (int s = s0; s < s1; ++s) {
-      const int k0 = s * 16 + g * 4;
-      u32x4_t av = arow ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (btok) {
-        if constexpr (XT == DT_F32) {
-          u32x4_t t = ldg16(reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0);
+    for (int sb = s0; sb < s1; sb += 8) {
+      u32x4_t av[8];
+      float bv[8][4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) bv[m] = __uint_as_float(t[m]);
-        } else {
-          u32x2_t t = ldg8(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0);
-          bv[0] = bf16_lo(t[0]); bv[1] = bf16_hi(t[0]); bv[2] = bf16_lo(t[1]); bv[3] = bf16_hi(t[1]);
+      for (int u = 0; u < 8; ++u) {
+        const int s = sb + u;
+        const int k0 = s * 16 + g * 4;
+        const bool in = s < s1;
+        av[u] = (arow && in) ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) bv[u][m] = 0.f;
+        if (btok && in) {
+          if constexpr (XT == DT_F32) {
+            u32x4_t t = ldg16(reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) bv[u][m] = __uint_as_float(t[m]);
+          } else {
+            u32x2_t t = ldg8(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0);
+            bv[u][0] = bf16_lo(t[0]); bv[u][1] = bf16_hi(t[0]); bv[u][2] = bf16_lo(t[1]); bv[u][3] = bf16_hi(t[1]);
+          }
         }
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mfma_f32(__uint_as_float(av[m]), bv[m], acc);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mfma_f32(__uint_as_float(av[u][m]), bv[u][m], acc);
     }
   } else {
     // 16x16x32 bf16 MFMA; one 16-byte load = 8 k values; step covers 32 k.
     const int nsteps = H / 32;
     const int s0 = wave * nsteps / NW, s1 = (wave + 1) * nsteps / NW;
     const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.wr) + size_t(row) * H;
-    for (int s = s0; s < s1; ++s) {
-      const int k0 = s * 32 + g * 8;
-      u32x4_t av = arow ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
-      if constexpr (XT == DT_BF16) {
-        u32x4_t bv = btok ? ldg16(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0)
-                          : u32x4_t{0, 0, 0, 0};
-        acc = mfma_bf16(av, bv, acc);
-      } else {
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (btok) {
-          const float* xp = reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0;
-          u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
+    for (int sb = s0; sb < s1; sb += 8) {
+      u32x4_t av[8];
+      float v[8][8];
+      u32x4_t bx[8];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) { v[m] = __uint_as_float(t0[m]); v[m + 4] = __uint_as_float(t1[m]); }
+      for (int u = 0; u < 8; ++u) {
+        const int s = sb + u;
+        const int k0 = s * 32 + g * 8;
+        const bool in = s < s1;
+        av[u] = (arow && in) ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+        if constexpr (XT == DT_BF16) {
+          bx[u] = (btok && in) ? ldg16(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0)
+                               : u32x4_t{0, 0, 0, 0};
+        } else {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) v[u][m] = 0.f;
+          if (btok && in) {
+            const float* xp = reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0;
+            u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) { v[u][m] = __uint_as_float(t0[m]); v[u][m + 4] = __uint_as_float(t1[m]); }
+          }
         }
-        u32x4_t hi, lo;
-        split_bf16x8(v, hi, lo);
-        acc = mfma_bf16(av, hi, acc);
-        acc = mfma_bf16(av, lo, acc);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if constexpr (XT == DT_BF16) {
+          acc = mfma_bf16(av[u], bx[u], acc);
+        } else {
+          u32x4_t hi, lo;
+          split_bf16x8(v[u], hi, lo);
+          acc = mfma_bf16(av[u], hi, acc);
+          acc = mfma_bf16(av[u], lo, acc);
+        }
       }
     }
   }
@@ -96,15 +121,18 @@ __device__ __forceinline__ float sanitize(float v) { return v != v ? -__builtin_
 
 // One thread selects the top-k of one token (E <= 32).
 __device__ void topk_thread(const float* l, int E, int k, int32_t* ids, float* w) {
+  float lv[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) lv[e] = e < E ? sanitize(l[e]) : -__builtin_inff();
   uint32_t taken = 0;
   float lmax = 0.f, denom = 0.f;
   for (int j = 0; j < k; ++j) {
     int bi = 0x7fffffff;
     float bv = -__builtin_inff();
-    for (int e = 0; e < E; ++e) {
-      if (taken & (1u << e)) continue;
-      float v = sanitize(l[e]);
-      if (better(v, e, bv, bi)) { bv = v; bi = e; }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if (e >= E || (taken & (1u << e))) continue;
+      if (better(lv[e], e, bv, bi)) { bv = lv[e]; bi = e; }
     }
     taken |= 1u << bi;
     ids[j] = bi;
@@ -196,21 +224,45 @@ __device__ void dispatch_wg(const RouterArgs& a, int* lds) {
     cnt[e] = s;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, cp = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = o;
-      rb.offsets[e] = o;
-      rb.cprefix[e] = cp;
-      rb.counts[e] = cnt[e];
-      if (cnt[e] > 0) rb.active[1 + na++] = e;
-      o += (cnt[e] + M - 1) / M * M;
-      cp += cnt[e];
+  if (wave == 0) {
+    // exclusive scans over experts (padded offsets, unpadded prefix) and the
+    // compact active list; experts 4*lane .. 4*lane+3 belong to this lane
+    int c[4], pad[4], act = 0, sp = 0, sc = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane * 4 + m;
+      c[m] = e < E ? cnt[e] : 0;
+      pad[m] = (c[m] + M - 1) / M * M;
+      sp += pad[m];
+      sc += c[m];
+      act += c[m] > 0;
     }
-    off[E] = o;
-    rb.offsets[E] = o;
-    rb.cprefix[E] = cp;
-    rb.active[0] = na;
+    int ip = sp, ic = sc, ia = act;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(ip, d), uc = __shfl_up(ic, d), ua = __shfl_up(ia, d);
+      if (lane >= d) { ip += up; ic += uc; ia += ua; }
+    }
+    int bp = ip - sp, bc = ic - sc, ba = ia - act;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane * 4 + m;
+      if (e < E) {
+        off[e] = bp;
+        rb.offsets[e] = bp;
+        rb.cprefix[e] = bc;
+        rb.counts[e] = c[m];
+        if (c[m] > 0) rb.active[1 + ba++] = e;
+      }
+      bp += pad[m];
+      bc += c[m];
+    }
+    if (lane == 63) {
+      off[E] = ip;
+      rb.offsets[E] = ip;
+      rb.cprefix[E] = ic;
+      rb.active[0] = ia;
+    }
   }
   __syncthreads();
   for (int c0 = f0; c0 < f1; c0 += 64) {
@@ -256,23 +308,20 @@ __device__ void dispatch_wg(const RouterArgs& a, int* lds) {
 
 // --------------------------------------------------------------- kernel --
 
+// One 16-expert x 16-token logits tile: the waves split H, partial sums meet
+// in LDS, wave 0 adds the bias and stores to `dst` ([T, E], row stride E).
 template <int RT, int XT>
-__global__ void __launch_bounds__(1024) router_kernel(RouterArgs a) {
-  extern __shared__ int lds[];
-  __shared__ int last_flag;
+__device__ __forceinline__ void logits_tile(const RouterArgs& a, float* red, float* dst) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
   const int rtile = blockIdx.x % a.n_row_tiles, ctile = blockIdx.x / a.n_row_tiles;
-
-  // optional side job: clear the prefill accumulator
+  // side job of the prefill path: clear the fp32 combine accumulator
   if (a.zero_f32) {
     const long n4 = a.zero_n / 4;
-    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
     for (long i = long(blockIdx.x) * blockDim.x + tid; i < n4; i += long(gridDim.x) * blockDim.x)
       reinterpret_cast<f32x4_t*>(a.zero_f32)[i] = z;
   }
-
   f32x4_t acc = router_dot<RT, XT>(a, rtile, ctile, wave, NW, lane);
-  float* red = reinterpret_cast<float*>(lds);
   *reinterpret_cast<f32x4_t*>(red + (wave * 64 + lane) * 4) = acc;
   __syncthreads();
   if (wave == 0) {
@@ -283,27 +332,49 @@ __global__ void __launch_bounds__(1024) router_kernel(RouterArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = rtile * 16 + (lane >> 4) * 4 + i;
-        if (e < a.E) a.rb.logits[size_t(tok) * a.E + e] = s[i] + (a.bias ? a.bias[e] : 0.f);
+        if (e < a.E) dst[size_t(tok) * a.E + e] = s[i] + (a.bias ? a.bias[e] : 0.f);
       }
     }
   }
+}
 
-  if (!arrive_last(a.rb.counter, gridDim.x, &last_flag)) return;
-
-  // ---- last work-group: top-k for every token, then dispatch
+// Top-k of every token from logits `l` ([T, E]), then the dispatch.  One work-group.
+__device__ __forceinline__ void select_and_dispatch(const RouterArgs& a, const float* l, int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
   const int T = a.T, E = a.E, k = a.k;
   if (E <= 32) {
     for (int t = tid; t < T; t += blockDim.x)
-      topk_thread(a.rb.logits + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k);
+      topk_thread(l + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k);
   } else {
     for (int t = wave; t < T; t += NW)
-      topk_wave(a.rb.logits + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k,
-                lane);
+      topk_wave(l + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k, lane);
   }
   __threadfence_block();
   __syncthreads();
   dispatch_wg(a, lds);
-  if (tid == 0) reset_counter(a.rb.counter);
+}
+
+// Single work-group (at most 16 experts x 16 tokens): logits stay in LDS.
+template <int RT, int XT>
+__global__ void __launch_bounds__(1024) router_fused_kernel(RouterArgs a) {
+  extern __shared__ int lds[];
+  __shared__ float lg[256];
+  logits_tile<RT, XT>(a, reinterpret_cast<float*>(lds), lg);
+  __syncthreads();
+  select_and_dispatch(a, lg, lds);
+}
+
+// Larger grids: the logits go to the workspace; the selection and dispatch run
+// in a second launch (the kernel boundary orders them, no device-wide fences).
+template <int RT, int XT>
+__global__ void __launch_bounds__(1024) router_logits_kernel(RouterArgs a) {
+  extern __shared__ int lds[];
+  logits_tile<RT, XT>(a, reinterpret_cast<float*>(lds), a.rb.logits);
+}
+
+__global__ void __launch_bounds__(1024) router_select_kernel(RouterArgs a) {
+  extern __shared__ int lds[];
+  select_and_dispatch(a, a.rb.logits, lds);
 }
 
 // --------------------------------------------------------------- launch --
@@ -314,13 +385,23 @@ size_t router_lds_bytes(int NW, int E) {
   return red > disp ? red : disp;
 }
 
+template <int RT, int XT>
+static void launch_router_t(const RouterArgs& a, int NW, hipStream_t st) {
+  const int nblocks = a.n_row_tiles * a.n_col_tiles;
+  if (nblocks == 1) {
+    hipLaunchKernelGGL((router_fused_kernel<RT, XT>), dim3(1), dim3(NW * 64), router_lds_bytes(NW, a.E), st, a);
+  } else {
+    hipLaunchKernelGGL((router_logits_kernel<RT, XT>), dim3(nblocks), dim3(NW * 64),
+                       size_t(NW) * 64 * 4 * sizeof(float), st, a);
+    hipLaunchKernelGGL(router_select_kernel, dim3(1), dim3(1024), router_lds_bytes(16, a.E), st, a);
+  }
+}
+
 hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st) {
-  dim3 grid(a.n_row_tiles * a.n_col_tiles), block(NW * 64);
-  size_t lds = router_lds_bytes(NW, a.E);
-  if (rdt == DT_F32 && xdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_F32, DT_F32>), grid, block, lds, st, a);
-  else if (rdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_F32, DT_BF16>), grid, block, lds, st, a);
-  else if (xdt == DT_F32) hipLaunchKernelGGL((router_kernel<DT_BF16, DT_F32>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((router_kernel<DT_BF16, DT_BF16>), grid, block, lds, st, a);
+  if (rdt == DT_F32 && xdt == DT_F32) launch_router_t<DT_F32, DT_F32>(a, NW, st);
+  else if (rdt == DT_F32) launch_router_t<DT_F32, DT_BF16>(a, NW, st);
+  else if (xdt == DT_F32) launch_router_t<DT_BF16, DT_F32>(a, NW, st);
+  else launch_router_t<DT_BF16, DT_BF16>(a, NW, st);
   return hipGetLastError();
 }
 

@@ -31,7 +31,6 @@ def test_exports_every_declared_function(m, root):
 
 def test_header_constants_match_binding(m, root):
     text = open(os.path.join(root, "include", "moe.h")).read()
-    assert f"#define MOE_WS_ZERO_BYTES {m.MOE_WS_ZERO_BYTES}" in text
     for name, val in [("MOE_ERR_WORKSPACE", -5), ("MOE_ERR_HIP", -6), ("MOE_PATH_PREFILL", 2), ("MOE_Q4_0", 2)]:
         assert re.search(rf"{name}\s*=\s*{val}", text), name
 
@@ -74,7 +73,7 @@ def test_workspace_size_and_dims(m):
     # prefill needs the bf16 activations and the fp32 accumulator
     assert big >= cap * 14336 * 2 + 4096 * 4096 * 4
     small = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2))
-    assert m.MOE_WS_ZERO_BYTES < small < big
+    assert 0 < small < big
 
 
 def test_argument_errors_before_launch(m):

@@ -143,22 +143,25 @@ def test_decode_is_deterministic(m):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_workspace_reuse_across_shapes(m):
-    """One zero-initialised workspace serves calls of different shapes in a row
-    (the completion counters return to zero after every call)."""
+def test_workspace_needs_no_initialisation(m):
+    """A workspace filled with garbage serves calls of different shapes and
+    paths in a row: nothing in it has to be prepared or survives a call."""
     import torch
-    big = SMALL["deepseek_small_t40"]
-    shape_big = H.shape_of(m, big)
-    ws = m.alloc_workspace(shape_big)
-    for name in ("deepseek_small_t8", "deepseek_small_t40", "deepseek_small_t8"):
+    big = SMALL["prefill_small_zipf"]
+    ws = m.alloc_workspace(H.shape_of(m, big))
+    ws.fill_(0xA5)
+    for name in ("deepseek_small_t8", "prefill_small_zipf", "deepseek_small_t40", "qwen_small_q4_t5",
+                 "deepseek_small_t8"):
         wl = SMALL[name]
+        need = m.moe_workspace_size(H.shape_of(m, wl))
+        assert need <= ws.numel() or name == "qwen_small_q4_t5"
+        w = ws if need <= ws.numel() else m.alloc_workspace(H.shape_of(m, wl)).fill_(0x5A)
         inp = _inputs(wl, 6)
         t = synth.to_torch(inp)
-        out = H.run_forward(m, wl, t, ws=ws)
+        out = H.run_forward(m, wl, t, ws=w)
         torch.cuda.synchronize()
-        assert torch.all(ws[: m.MOE_WS_ZERO_BYTES] == 0)
         err = H.relerr(H.to_f64(out), H.oracle_layer(wl, inp)["out"])
-        assert err <= 1e-2, (name, err)
+        assert err <= H.tolerance(wl), (name, err)
 
 
 # -------------------------------------------------------------- full size ----
