@@ -208,6 +208,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for ~10 GiB)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -246,20 +247,48 @@ def main():
         else:
             m.moe_forward_profiled(*a, events, stream=sh)
 
+    def timed(fn, n, first):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(first + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # eager warm-up (also performs the library's one-time set-up before any capture)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, 1)):
         step(i)
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    eager_elapsed = timed(step, args.steps, args.warmup)
+    eager_value = wl.T * args.steps / eager_elapsed
+    graph_value = None
 
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if not args.graph:
+        elapsed = eager_elapsed
+        timing = "eager launches"
+    else:
+        # one captured graph per weight copy, replayed in rotation: every replay
+        # runs the whole layer (router, dispatch, experts, combine) again
+        cap = torch.cuda.Stream()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                a = (shape, inp["x"][c], inp["router_w"][c], inp["router_b"][c], inp["w_gate"][c], inp["w_up"][c],
+                     inp["w_down"][c], inp["ws_gate"][c], inp["ws_up"][c], inp["ws_down"][c], out, ws)
+                m.moe_forward(*a, stream=cap.cuda_stream)
+            graphs.append(g)
+        replay = lambda i: graphs[i % copies].replay()
+        for i in range(args.warmup):
+            replay(i)
+        elapsed = timed(replay, args.steps, args.warmup)
+        graph_value = wl.T * args.steps / elapsed
+        timing = "hipGraph replay, one graph per weight copy"
+    log(f"[bench] warmup {args.warmup}; timed {args.steps} steps ({timing})")
     ms_per_step = elapsed * 1e3 / args.steps
     value = wl.T * args.steps / elapsed
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s")
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s (eager {eager_value:.1f} tokens/s)")
 
     # stage timing with HIP events recorded on the launch stream
     prefill = wl.x_dtype == "bf16" and wl.w_dtype == "bf16" and wl.T > 64
@@ -326,7 +355,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "top_k": wl.k, "I": wl.I,
                    "n_shared": wl.S, "I_shared": wl.Is, "weights": wl.w_dtype, "activations": wl.x_dtype,
                    "router": wl.r_dtype, "path": "prefill" if prefill else "decode", "weight_copies": copies,
-                   "parallelism": "single-gpu"},
+                   "timing": timing, "parallelism": "single-gpu"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -23,7 +23,7 @@ constexpr int kTileM = 128;          // padding multiple of the expert-sorted or
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
 constexpr size_t kAlign = 256;
 #ifndef MOE_DOWN_WAVES
-#define MOE_DOWN_WAVES 8192                   // target waves of the decode down launch
+#define MOE_DOWN_WAVES 4096                   // target waves of the decode down launch
 #endif
 
 size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
@@ -104,7 +104,8 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     const int n_rt = H / 16;
     const long slots = std::min<long>(E, long(Tr) * k);
     const long steps_max = slots * decode_steps(s->w_dtype, I) + long(S) * (S ? decode_steps(s->w_dtype, Is) : 0);
-    int nsplit = int((MOE_DOWN_WAVES + 4L * n_rt - 1) / (4L * n_rt));
+    const long waves = Tr > 16 ? 2L * MOE_DOWN_WAVES : MOE_DOWN_WAVES;   // heavier steps with 4 column tiles
+    int nsplit = int((waves + 4L * n_rt - 1) / (4L * n_rt));
     nsplit = std::max(1, std::min(nsplit, 64));
     nsplit = int(std::max<long>(1, std::min<long>(nsplit, steps_max / 16)));
     L.nsplit = nsplit;
@@ -149,12 +150,12 @@ moe::RouteBufs route_bufs(uint8_t* ws, const Layout& L) {
 }
 
 moe::RouterArgs router_args(const moe_shape_t* s, int T, const void* x, const void* wr, const float* b,
-                            const moe::RouteBufs& rb) {
+                            const moe::RouteBufs& rb, int tile_m = kTileM) {
   moe::RouterArgs a{};
   a.x = x; a.wr = wr; a.bias = b;
   a.T = T; a.H = s->H; a.E = s->E; a.k = s->top_k;
-  a.tile_m = kTileM;
-  a.capacity = int(roundup(long(T) * s->top_k + long(s->E) * (kTileM - 1), kTileM));
+  a.tile_m = tile_m;
+  a.capacity = int(roundup(long(T) * s->top_k + long(s->E) * (tile_m - 1), tile_m));
   a.n_row_tiles = (s->E + 15) / 16;
   a.n_col_tiles = (T + 15) / 16;
   a.zero_f32 = nullptr; a.zero_n = 0;
@@ -304,7 +305,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     uint8_t* oc = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
     StageEvents sev{events, n_events};
     sev.mark(st);
-    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb);
+    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb, 1);   // decode uses no padding
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);

@@ -206,7 +206,7 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT
 #define MOE_GU_UNROLL_BF16 8
 #endif
 #ifndef MOE_DN_UNROLL_BF16
-#define MOE_DN_UNROLL_BF16 16
+#define MOE_DN_UNROLL_BF16 8
 #endif
 template <int WT, int NCT>
 struct Unroll {

@@ -20,6 +20,8 @@
 
 namespace moe {
 
+constexpr int kRouterIdsLds = 16384;   // flat ids kept in LDS for the dispatch (64 KiB)
+
 // ------------------------------------------------------------- logits ----
 
 template <int RT, int XT>
@@ -119,46 +121,75 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 
 __device__ __forceinline__ float sanitize(float v) { return v != v ? -__builtin_inff() : v; }
 
-// One thread selects the top-k of one token (E <= 32).
-__device__ void topk_thread(const float* l, int E, int k, int32_t* ids, float* w) {
-  float lv[32];
+// One thread selects the top-k of one token (E <= EMAX <= 32, k <= 8).  Logits,
+// selections and weights stay in registers (loops fully unrolled and
+// predicated); ids and weights are written once.  `ids_lds` (or null)
+// receives a copy of the ids for the dispatch.
+template <int EMAX>
+__device__ void topk_thread(const float* l, int E, int k, int32_t* ids, float* w, int32_t* ids_lds) {
+  constexpr int KMAX = 8;
+  float lv[EMAX], zv[KMAX];
+  int iv[KMAX];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) lv[e] = e < E ? sanitize(l[e]) : -__builtin_inff();
+  for (int e = 0; e < EMAX; ++e) lv[e] = e < E ? sanitize(l[e]) : -__builtin_inff();
   uint32_t taken = 0;
   float lmax = 0.f, denom = 0.f;
-  for (int j = 0; j < k; ++j) {
-    int bi = 0x7fffffff;
-    float bv = -__builtin_inff();
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      if (e >= E || (taken & (1u << e))) continue;
-      if (better(lv[e], e, bv, bi)) { bv = lv[e]; bi = e; }
+  for (int j = 0; j < KMAX; ++j) {
+    zv[j] = 0.f;
+    iv[j] = 0;
+    if (j < k) {
+      int bi = 0x7fffffff;
+      float bv = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E && !(taken & (1u << e)) && better(lv[e], e, bv, bi)) { bv = lv[e]; bi = e; }
+      }
+      taken |= 1u << bi;
+      if (j == 0) lmax = bv;
+      // weights: softmax over the selected logits (the full-softmax denominator cancels)
+      const float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+      zv[j] = z;
+      iv[j] = bi;
+      denom += z;
     }
-    taken |= 1u << bi;
-    ids[j] = bi;
-    if (j == 0) lmax = bv;
-    // weights: softmax over the selected logits (the full-softmax denominator cancels)
-    float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
-    w[j] = z;
-    denom += z;
   }
-  if (!(denom > 0.f)) {                      // every selected logit was -inf/NaN: equal weights
-    for (int j = 0; j < k; ++j) w[j] = 1.0f / float(k);
-  } else {
-    float r = 1.0f / denom;
-    for (int j = 0; j < k; ++j) w[j] *= r;
+  const float r = denom > 0.f ? 1.0f / denom : 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      ids[j] = iv[j];
+      if (ids_lds) ids_lds[j] = iv[j];
+      w[j] = denom > 0.f ? zv[j] * r : 1.0f / float(k);   // all selected logits -inf/NaN: equal weights
+    }
   }
 }
 
-// One wave selects the top-k of one token (any E <= 256).
-__device__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, int lane) {
-  float v[4];
+// (value, index) maximum over the 16 lanes of a DPP row: rotations by 8, 4, 2
+// and 1 lanes leave every lane of the row holding the row's best candidate.
+template <int ROT>
+__device__ __forceinline__ void dpp_row_best(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), 0x120 + ROT, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, 0x120 + ROT, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+
+// One wave selects the top-k of one token (any E <= 256, k <= E).  Each
+// round takes the best remaining candidate of every lane (4 per lane), the
+// best of every 16-lane row with DPP rotations, and the best of the 4 rows
+// with lane reads.  Selection j is kept by lane j % 64 (slot j / 64) and
+// written once at the end.
+__device__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, int32_t* ids_lds, int lane) {
+  float v[4], zk[4];
   bool taken[4];
+  int ik[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    int e = lane + 64 * m;
+    const int e = lane + 64 * m;
     v[m] = e < E ? sanitize(l[e]) : -__builtin_inff();
     taken[m] = e >= E;
+    zk[m] = 0.f;
+    ik[m] = 0;
   }
   float lmax = 0.f, denom = 0.f;
   for (int j = 0; j < k; ++j) {
@@ -166,30 +197,42 @@ __device__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, 
     int bi = 0x7fffffff;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      int e = lane + 64 * m;
+      const int e = lane + 64 * m;
       if (!taken[m] && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
     }
+    dpp_row_best<8>(bv, bi);
+    dpp_row_best<4>(bv, bi);
+    dpp_row_best<2>(bv, bi);
+    dpp_row_best<1>(bv, bi);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oi = __shfl_xor(bi, off);
+    for (int r = 16; r < 64; r += 16) {
+      const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
+      const int oi = __builtin_amdgcn_readlane(bi, r);
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
+    // every lane of row 0 now holds the wave's best; broadcast it
+    bv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
+    bi = __builtin_amdgcn_readfirstlane(bi);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       if (lane + 64 * m == bi) taken[m] = true;
     if (j == 0) lmax = bv;
-    // weights: softmax over the selected logits (the full-softmax denominator cancels)
-    float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+    const float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
     denom += z;
-    if (lane == 0) { ids[j] = bi; w[j] = z; }
+    if (lane == (j & 63)) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if ((j >> 6) == m) { zk[m] = z; ik[m] = bi; }
+    }
   }
-  if (lane == 0) {
-    if (denom > 0.f) {
-      float r = 1.0f / denom;
-      for (int j = 0; j < k; ++j) w[j] *= r;
-    } else {
-      for (int j = 0; j < k; ++j) w[j] = 1.0f / float(k);
+  const float r = denom > 0.f ? 1.0f / denom : 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = lane + 64 * m;
+    if (j < k) {
+      ids[j] = ik[m];
+      if (ids_lds) ids_lds[j] = ik[m];
+      w[j] = denom > 0.f ? zk[m] * r : 1.0f / float(k);
     }
   }
 }
@@ -199,14 +242,13 @@ __device__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, 
 // Expert-sorted order, built by one work-group.  Deterministic: the rank of an
 // assignment inside its expert's segment is the number of smaller flat ids
 // routed to the same expert (stable counting sort); no atomics decide order.
-__device__ void dispatch_wg(const RouterArgs& a, int* lds) {
+__device__ void dispatch_wg(const RouterArgs& a, int* lds, const int32_t* ids) {
   const RouteBufs& rb = a.rb;
   const int E = a.E, n = a.T * a.k, M = a.tile_m;
   const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wave = tid >> 6, NW = NT >> 6;
   int* hist = lds;                 // [NW][E]: per-wave counts, then per-wave rank bases
   int* cnt = hist + NW * E;        // [E]
   int* off = cnt + E;              // [E+1]
-  const int32_t* ids = rb.topk_ids;
 
   for (int i = tid; i < NW * E; i += NT) hist[i] = 0;
   __syncthreads();
@@ -338,20 +380,31 @@ __device__ __forceinline__ void logits_tile(const RouterArgs& a, float* red, flo
   }
 }
 
-// Top-k of every token from logits `l` ([T, E]), then the dispatch.  One work-group.
+// Top-k of every token from logits `l` ([T, E]), then the dispatch.  One
+// work-group.  The ids are also kept in LDS (after the dispatch scratch) when
+// T*k fits, so the dispatch does not read them back from memory.
 __device__ __forceinline__ void select_and_dispatch(const RouterArgs& a, const float* l, int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
-  const int T = a.T, E = a.E, k = a.k;
-  if (E <= 32) {
-    for (int t = tid; t < T; t += blockDim.x)
-      topk_thread(l + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k);
+  const int T = a.T, E = a.E, k = a.k, n = T * k;
+  int* ids_lds = (n <= kRouterIdsLds) ? lds + NW * E + 2 * E + 1 : nullptr;
+  if (E <= 32 && k <= 8) {
+    for (int t = tid; t < T; t += blockDim.x) {
+      const float* lt = l + size_t(t) * E;
+      int32_t* it = a.rb.topk_ids + size_t(t) * k;
+      float* wt = a.rb.topk_w + size_t(t) * k;
+      int32_t* il = ids_lds ? ids_lds + t * k : nullptr;
+      if (E <= 8) topk_thread<8>(lt, E, k, it, wt, il);
+      else if (E <= 16) topk_thread<16>(lt, E, k, it, wt, il);
+      else topk_thread<32>(lt, E, k, it, wt, il);
+    }
   } else {
     for (int t = wave; t < T; t += NW)
-      topk_wave(l + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k, lane);
+      topk_wave(l + size_t(t) * E, E, k, a.rb.topk_ids + size_t(t) * k, a.rb.topk_w + size_t(t) * k,
+                ids_lds ? ids_lds + t * k : nullptr, lane);
   }
   __threadfence_block();
   __syncthreads();
-  dispatch_wg(a, lds);
+  dispatch_wg(a, lds, ids_lds ? ids_lds : a.rb.topk_ids);
 }
 
 // Single work-group (at most 16 experts x 16 tokens): logits stay in LDS.
@@ -379,9 +432,9 @@ __global__ void __launch_bounds__(1024) router_select_kernel(RouterArgs a) {
 
 // --------------------------------------------------------------- launch --
 
-size_t router_lds_bytes(int NW, int E) {
+size_t router_lds_bytes(int NW, int E, int n) {
   size_t red = size_t(NW) * 64 * 4 * sizeof(float);
-  size_t disp = (size_t(NW) * E + 2 * E + 1) * sizeof(int);
+  size_t disp = (size_t(NW) * E + 2 * E + 1 + (n <= kRouterIdsLds ? n : 0)) * sizeof(int);
   return red > disp ? red : disp;
 }
 
@@ -389,11 +442,12 @@ template <int RT, int XT>
 static void launch_router_t(const RouterArgs& a, int NW, hipStream_t st) {
   const int nblocks = a.n_row_tiles * a.n_col_tiles;
   if (nblocks == 1) {
-    hipLaunchKernelGGL((router_fused_kernel<RT, XT>), dim3(1), dim3(NW * 64), router_lds_bytes(NW, a.E), st, a);
+    hipLaunchKernelGGL((router_fused_kernel<RT, XT>), dim3(1), dim3(NW * 64), router_lds_bytes(NW, a.E, a.T * a.k),
+                       st, a);
   } else {
     hipLaunchKernelGGL((router_logits_kernel<RT, XT>), dim3(nblocks), dim3(NW * 64),
                        size_t(NW) * 64 * 4 * sizeof(float), st, a);
-    hipLaunchKernelGGL(router_select_kernel, dim3(1), dim3(1024), router_lds_bytes(16, a.E), st, a);
+    hipLaunchKernelGGL(router_select_kernel, dim3(1), dim3(1024), router_lds_bytes(16, a.E, a.T * a.k), st, a);
   }
 }
 
