@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -217,6 +219,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(2 ** 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB x5")
+        return
     import mixture_experts_layer_12_amd as m
     if not os.path.exists(m.LIB_PATH):
         import __graft_entry__

@@ -14,21 +14,39 @@
 //                 and adds into an fp32 [T, H] accumulator (the combine);
 //   cast          fp32 accumulator -> output dtype.
 //
-// Tiles: 128 sorted rows x 128 output columns per work-group, 4 waves in a
-// 2 x 2 arrangement, k staged 64 at a time through double-buffered LDS with
-// the next stage's global loads in flight during the current stage's MFMAs.
-// Rows are padded to 72 bf16 (144 bytes) in LDS so that the 16 rows read by
-// one 16-lane group land on distinct banks.  Work-group ids are remapped so
-// that the groups resident on one XCD (one L2) work on neighbouring tiles.
+// Tiles: 128 sorted rows x 128 output columns per work-group (for gate/up:
+// 128 gate and 128 up columns), 8 waves in a 2 x 4 arrangement (two waves
+// per SIMD hide each other's LDS and barrier stalls), k staged 64 at a time.
+// Operands move global -> LDS with the gfx950 direct-to-LDS loads (one wave
+// instruction = 8 rows x 128 bytes, no register staging) into a ring of LDS
+// stages filled ahead of the MFMAs that consume them: 3 stages (144 KiB, one
+// work-group per CU) for gate/up, 2 stages (64 KiB, two work-groups per CU)
+// for down.
+// Because those loads write each row contiguously, rows cannot be padded;
+// instead the 16-byte chunks of row r are XOR-permuted by (r >> 1) & 7 so
+// that the 16 rows one MFMA operand read touches fall on distinct LDS banks.
+// A partial last k stage (K % 64 == 32) is staged through registers with
+// zero fill.  Work-group ids are remapped so that the groups resident on one
+// XCD (one L2) work on neighbouring tiles.
 #include "common.hpp"
 
 namespace moe {
 
+#ifndef MOE_PF_GROUP
+#define MOE_PF_GROUP 8
+#endif
 constexpr int PF_BM = 128;     // sorted rows per tile (== dispatch padding tile)
 constexpr int PF_BN = 128;     // output columns per tile
-constexpr int PF_BK = 64;      // k per LDS stage
-constexpr int PF_LD = PF_BK + 8;   // LDS row stride in bf16 elements
-constexpr int PF_GROUP = 8;    // row tiles per scheduling group
+constexpr int PF_BK = 64;      // k per LDS stage: a staged row is 128 bytes = 8 chunks
+constexpr int PF_STAGES = 3;   // gate/up ring depth (144 KiB of LDS)
+#ifndef MOE_PF_DN_STAGES
+#define MOE_PF_DN_STAGES 2
+#endif
+constexpr int DN_STAGES = MOE_PF_DN_STAGES;   // down ring depth
+constexpr int PF_GROUP = MOE_PF_GROUP;   // row tiles per scheduling group
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 // XCD-aware tile order: hardware places work-group b on XCD b % 8.  Give each
 // XCD a contiguous range of logical tiles, then walk them in groups of
@@ -36,12 +54,9 @@ constexpr int PF_GROUP = 8;    // row tiles per scheduling group
 // in that XCD's L2.
 __device__ __forceinline__ void tile_of(int bid, int n_rt, int n_ct, int& rt, int& ct) {
   const int total = n_rt * n_ct;
-  const int per = total / 8, extra = total % 8;
+  const int per = total / 8;
   const int xcd = bid % 8, local = bid / 8;
-  int L;
-  if (local < per) L = xcd * per + local;
-  else L = 8 * per + xcd;                 // leftovers (only when extra > 0)
-  (void)extra;
+  const int L = local < per ? xcd * per + local : 8 * per + xcd;   // leftovers when total % 8 != 0
   const int group = L / (PF_GROUP * n_ct);
   const int first = group * PF_GROUP;
   const int gsz = min(PF_GROUP, n_rt - first);
@@ -50,137 +65,174 @@ __device__ __forceinline__ void tile_of(int bid, int n_rt, int n_ct, int& rt, in
   ct = in / gsz;
 }
 
-// --------------------------------------------------------------- gate/up --
-// MFMA A operand = weight rows (gate rows 0..127 and up rows 128..255 of the
-// stage), B operand = gathered token rows, so the accumulator of a lane holds
-// 4 consecutive intermediate columns of one token row.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-__global__ void __launch_bounds__(256) prefill_gateup_kernel(PrefillArgs a) {
+// Element offset of logical 16-byte chunk c of staged row r.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * PF_BK + ((c ^ swz(r)) << 3); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Work-group barrier for the k-stage ring: this wave's LDS reads are complete
+// (lgkmcnt 0) and the caller has already waited for its own stage loads.  A
+// plain __syncthreads() would also wait for every load still in flight
+// (vmcnt 0), which would serialise the ring.  The asm statement clobbers
+// memory, so the compiler moves no memory access across it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | (0x0 << 8) | ((0x3F >> 4) << 14));   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// One wave instruction: 8 staged rows x 128 bytes.  Lane l fills row
+// (first row of the group) + l/8, physical chunk l%8, with the logical chunk
+// (l%8) ^ swz(row) of its source row.  `src` is this lane's source row at the
+// stage's first k; `dst` is the group's first staged row (wave-uniform).
+__device__ __forceinline__ void dma_group(const uint16_t* src, int row, int lane, uint16_t* dst) {
+  const int c = (lane & 7) ^ swz(row);
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(src + c * 8), (lds_void_t*)dst, 16, 0, 0);
+}
+
+// Register path for a partial k stage: the same lane -> (row, chunk) mapping,
+// zero fill where k >= K.
+__device__ __forceinline__ void reg_group(const uint16_t* src, int row, int lane, uint16_t* dst, int k0, int K) {
+  const int p = lane & 7, c = p ^ swz(row);
+  u32x4_t v = {0, 0, 0, 0};
+  if (k0 + c * 8 < K) v = ldg16(src + c * 8);
+  *reinterpret_cast<u32x4_t*>(dst + (lane >> 3) * PF_BK + p * 8) = v;
+}
+
+// --------------------------------------------------------------- gate/up --
+// Staged rows per k stage: [0,128) gate rows, [128,256) up rows, [256,384)
+// gathered x rows.  MFMA A operand = weight rows, B operand = token rows, so
+// a lane's accumulator holds 4 consecutive intermediate columns of one token.
+
+#ifndef MOE_PF_GU_WAVES
+#define MOE_PF_GU_WAVES 8
+#endif
+constexpr int GU_WAVES = MOE_PF_GU_WAVES;            // 4: 2x2 wave grid, 8: 2x4
+constexpr int GU_ROWS = 2 * PF_BN + PF_BM;           // 384
+constexpr int GU_GROUPS_PER_WAVE = GU_ROWS / 8 / GU_WAVES;
+constexpr int GU_WN = GU_WAVES / 2;                  // waves across the columns
+constexpr int GU_NF = PF_BN / GU_WN / 16;            // 16-column fragments per wave (gate and up each)
+
+__global__ void __launch_bounds__(64 * GU_WAVES) prefill_gateup_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  constexpr int ROWS = 2 * PF_BN + PF_BM;      // gate, up, x rows per stage
-  constexpr int STAGE = ROWS * PF_LD;
+  constexpr int STAGE = GU_ROWS * PF_BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int rt, ct;
   tile_of(blockIdx.x, a.n_row_tiles, a.n_col_tiles, rt, ct);
 
   const int n_routed_tiles = a.capacity / PF_BM;
   const int H = a.H;
-  int N;
+  int N, e_or_s;
   const uint16_t *Wg, *Wu;
-  int hrow0 = rt * PF_BM;
-  int tokrow[4];                      // token of this thread's 4 staged x rows (-1 = padding)
-  const int kc = tid & 7, r0 = tid >> 3;
-  if (rt < n_routed_tiles) {
-    const int e = a.tile_expert[rt];
-    if (e < 0) return;
+  const bool routed = rt < n_routed_tiles;
+  int local = 0;
+  if (routed) {
+    e_or_s = a.tile_expert[rt];
+    if (e_or_s < 0) return;
     N = a.I;
-    Wg = a.wg + size_t(e) * a.I * H;
-    Wu = a.wu + size_t(e) * a.I * H;
-    const int n = a.T * a.k;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int f = a.sorted_ids[rt * PF_BM + r0 + 32 * j];
-      tokrow[j] = f < n ? f / a.k : -1;
-    }
+    Wg = a.wg + size_t(e_or_s) * a.I * H;
+    Wu = a.wu + size_t(e_or_s) * a.I * H;
   } else {
     const int tiles_per_shared = a.t_pad / PF_BM;
-    const int s = (rt - n_routed_tiles) / tiles_per_shared;
-    const int local = (rt - n_routed_tiles) % tiles_per_shared;
+    e_or_s = (rt - n_routed_tiles) / tiles_per_shared;
+    local = (rt - n_routed_tiles) % tiles_per_shared;
     N = a.Is;
-    Wg = a.sg + size_t(s) * a.Is * H;
-    Wu = a.su + size_t(s) * a.Is * H;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = local * PF_BM + r0 + 32 * j;
-      tokrow[j] = t < a.T ? t : -1;
-    }
+    Wg = a.sg + size_t(e_or_s) * a.Is * H;
+    Wu = a.su + size_t(e_or_s) * a.Is * H;
   }
   const int n0 = ct * PF_BN;
   if (n0 >= N) return;
+  const int hrow0 = rt * PF_BM;
 
-  // global -> register staging: 8 weight chunks + 4 x chunks of 16 bytes
-  const uint16_t* xptr[4];
+  // this lane's source row for each of its wave's 12 staged 8-row groups
+  const uint16_t* src[GU_GROUPS_PER_WAVE];
+  int srow[GU_GROUPS_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    xptr[j] = reinterpret_cast<const uint16_t*>(a.x) + size_t(tokrow[j] < 0 ? 0 : tokrow[j]) * H + kc * 8;
-  const uint16_t* wptr[8];
-  bool wok[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = r0 + 32 * (j & 3);
-    const int n = n0 + r;
-    wok[j] = n < N;
-    wptr[j] = (j < 4 ? Wg : Wu) + size_t(wok[j] ? n : n0) * H + kc * 8;
+  for (int j = 0; j < GU_GROUPS_PER_WAVE; ++j) {
+    const int r = (wave * GU_GROUPS_PER_WAVE + j) * 8 + (lane >> 3);
+    srow[j] = r;
+    if (r < 2 * PF_BN) {
+      const int n = n0 + (r & (PF_BN - 1));
+      src[j] = (r < PF_BN ? Wg : Wu) + size_t(n < N ? n : n0) * H;
+    } else {
+      const int m = r - 2 * PF_BN;
+      int tok;
+      if (routed) {
+        const int f = a.sorted_ids[hrow0 + m];
+        tok = f < a.T * a.k ? f / a.k : 0;        // padding rows read a real row; their outputs are never used
+      } else {
+        tok = local * PF_BM + m;
+        tok = tok < a.T ? tok : 0;
+      }
+      src[j] = reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H;
+    }
   }
   const int nk = (H + PF_BK - 1) / PF_BK;
-  u32x4_t stg[12];
-  const u32x4_t z4 = {0, 0, 0, 0};
-  auto gload = [&](int kt) {
-    const int k = kt * PF_BK + kc * 8;
-    const bool kok = k < H;
+  const bool k_tail = (H % PF_BK) != 0;
+  auto stage_in = [&](int kt) {
+    uint16_t* s = smem + (kt % PF_STAGES) * STAGE;
+    const int k0 = kt * PF_BK;
+    if (!(k_tail && kt == nk - 1)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) stg[j] = (wok[j] && kok) ? ldg16(wptr[j] + size_t(kt) * PF_BK) : z4;
+      for (int j = 0; j < GU_GROUPS_PER_WAVE; ++j)
+        dma_group(src[j] + k0, srow[j], lane, s + (wave * GU_GROUPS_PER_WAVE + j) * 8 * PF_BK);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) stg[8 + j] = (tokrow[j] >= 0 && kok) ? ldg16(xptr[j] + size_t(kt) * PF_BK) : z4;
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* s = smem + buf * STAGE;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = (j < 4 ? 0 : PF_BN) + r0 + 32 * (j & 3);
-      *reinterpret_cast<u32x4_t*>(s + row * PF_LD + kc * 8) = stg[j];
+      for (int j = 0; j < GU_GROUPS_PER_WAVE; ++j)
+        reg_group(src[j] + k0, srow[j], lane, s + (wave * GU_GROUPS_PER_WAVE + j) * 8 * PF_BK, k0, H);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4_t*>(s + (2 * PF_BN + r0 + 32 * j) * PF_LD + kc * 8) = stg[8 + j];
   };
 
-  // wave tile: 64 intermediate columns (gate and up) x 64 token rows
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % GU_WN, wm = wave / GU_WN;
   const int g = lane >> 4, l16 = lane & 15;
-  f32x4_t accg[4][4], accu[4][4];
+  f32x4_t accg[GU_NF][4], accu[GU_NF][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < GU_NF; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) accg[i][j] = accu[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  stage_in(0);
+  if (nk > 1) stage_in(1);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* s = smem + buf * STAGE;
+    if (kt + 1 < nk) wait_vmcnt<GU_GROUPS_PER_WAVE>();   // stage kt landed; kt+1 may be in flight
+    else wait_vmcnt<0>();
+    ring_barrier();                                       // every wave's part of stage kt landed,
+    if (kt + 2 < nk) stage_in(kt + 2);                    // and every wave is done with stage kt-1
+    const uint16_t* s = smem + (kt % PF_STAGES) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < PF_BK / 32; ++ks) {
-      const int ko = ks * 32 + g * 8;
-      u32x4_t ga[4], ua[4], xb[4];
+      const int c = ks * 4 + g;
+      u32x4_t ga[GU_NF], ua[GU_NF], xb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ga[i] = *reinterpret_cast<const u32x4_t*>(s + (wn * 64 + i * 16 + l16) * PF_LD + ko);
-        ua[i] = *reinterpret_cast<const u32x4_t*>(s + (PF_BN + wn * 64 + i * 16 + l16) * PF_LD + ko);
+      for (int i = 0; i < GU_NF; ++i) {
+        const int rg = wn * (GU_NF * 16) + i * 16 + l16;
+        ga[i] = *reinterpret_cast<const u32x4_t*>(s + lds_off(rg, c));
+        ua[i] = *reinterpret_cast<const u32x4_t*>(s + lds_off(PF_BN + rg, c));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xb[j] = *reinterpret_cast<const u32x4_t*>(s + (2 * PF_BN + wm * 64 + j * 16 + l16) * PF_LD + ko);
+        xb[j] = *reinterpret_cast<const u32x4_t*>(s + lds_off(2 * PF_BN + wm * 64 + j * 16 + l16, c));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < GU_NF; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           accg[i][j] = mfma_bf16(ga[i], xb[j], accg[i][j]);
           accu[i][j] = mfma_bf16(ua[i], xb[j], accu[i][j]);
         }
     }
-    if (kt + 1 < nk) {
-      sstore(buf ^ 1);
-      __syncthreads();
-    }
   }
 
   // epilogue: h[row][n] = bf16(silu(g) * u)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + wn * 64 + i * 16 + g * 4;
+  for (int i = 0; i < GU_NF; ++i) {
+    const int n = n0 + wn * (GU_NF * 16) + i * 16 + g * 4;
     if (n >= N) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -195,17 +247,26 @@ __global__ void __launch_bounds__(256) prefill_gateup_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ down --
-// MFMA A operand = activation rows (sorted order), B operand = down-projection
-// rows (hidden outputs); a lane's accumulator holds 4 sorted rows of one
+// Staged rows per k stage: [0,128) activation rows (sorted order), [128,256)
+// down-projection rows (hidden outputs).  MFMA A operand = activation rows,
+// B operand = down rows; a lane's accumulator holds 4 sorted rows of one
 // hidden column, which it scales by the routing weight and adds into the fp32
 // accumulator with hardware float atomics.
 
-__global__ void __launch_bounds__(256) prefill_down_kernel(PrefillArgs a) {
+#ifndef MOE_PF_DN_WAVES
+#define MOE_PF_DN_WAVES 8
+#endif
+constexpr int DN_WAVES = MOE_PF_DN_WAVES;            // 4: 2x2 wave grid, 8: 2x4
+constexpr int DN_ROWS = PF_BM + PF_BN;               // 256
+constexpr int DN_GROUPS_PER_WAVE = DN_ROWS / 8 / DN_WAVES;
+constexpr int DN_WN = DN_WAVES / 2;
+constexpr int DN_NF = PF_BN / DN_WN / 16;            // 16-column fragments per wave
+
+__global__ void __launch_bounds__(64 * DN_WAVES) prefill_down_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   __shared__ int tok_s[PF_BM];
   __shared__ float w_s[PF_BM];
-  constexpr int ROWS = 2 * PF_BM;
-  constexpr int STAGE = ROWS * PF_LD;
+  constexpr int STAGE = DN_ROWS * PF_BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int rt, ct;
   tile_of(blockIdx.x, a.n_row_tiles, a.n_col_tiles, rt, ct);
@@ -238,76 +299,77 @@ __global__ void __launch_bounds__(256) prefill_down_kernel(PrefillArgs a) {
   }
   const int n0 = ct * PF_BN;
   const int hrow0 = rt * PF_BM;
-  const int kc = tid & 7, r0 = tid >> 3;
-  const uint16_t* hptr[4];
-  const uint16_t* wptr[4];
+
+  const uint16_t* src[DN_GROUPS_PER_WAVE];
+  int srow[DN_GROUPS_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    hptr[j] = a.h + size_t(hrow0 + r0 + 32 * j) * a.h_stride + kc * 8;
-    wptr[j] = Wd + size_t(n0 + r0 + 32 * j) * K + kc * 8;   // H % 128 may leave a partial tile
+  for (int j = 0; j < DN_GROUPS_PER_WAVE; ++j) {
+    const int r = (wave * DN_GROUPS_PER_WAVE + j) * 8 + (lane >> 3);
+    srow[j] = r;
+    if (r < PF_BM) {
+      src[j] = a.h + size_t(hrow0 + r) * a.h_stride;
+    } else {
+      const int n = n0 + r - PF_BM;
+      src[j] = Wd + size_t(n < H ? n : n0) * K;     // H % 128 may leave a partial tile
+    }
   }
-  bool wok[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) wok[j] = n0 + r0 + 32 * j < H;
   const int nk = (K + PF_BK - 1) / PF_BK;
-  u32x4_t stg[8];
-  const u32x4_t z4 = {0, 0, 0, 0};
-  auto gload = [&](int kt) {
-    const int k = kt * PF_BK + kc * 8;
-    const bool kok = k < K;
+  const bool k_tail = (K % PF_BK) != 0;
+  auto stage_in = [&](int kt) {
+    uint16_t* s = smem + (kt % DN_STAGES) * STAGE;
+    const int k0 = kt * PF_BK;
+    if (!(k_tail && kt == nk - 1)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) stg[j] = kok ? ldg16(hptr[j] + size_t(kt) * PF_BK) : z4;
+      for (int j = 0; j < DN_GROUPS_PER_WAVE; ++j)
+        dma_group(src[j] + k0, srow[j], lane, s + (wave * DN_GROUPS_PER_WAVE + j) * 8 * PF_BK);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) stg[4 + j] = (kok && wok[j]) ? ldg16(wptr[j] + size_t(kt) * PF_BK) : z4;
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* s = smem + buf * STAGE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4_t*>(s + (r0 + 32 * j) * PF_LD + kc * 8) = stg[j];
-      *reinterpret_cast<u32x4_t*>(s + (PF_BM + r0 + 32 * j) * PF_LD + kc * 8) = stg[4 + j];
+      for (int j = 0; j < DN_GROUPS_PER_WAVE; ++j)
+        reg_group(src[j] + k0, srow[j], lane, s + (wave * DN_GROUPS_PER_WAVE + j) * 8 * PF_BK, k0, K);
     }
   };
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / DN_WN, wn = wave % DN_WN;
   const int g = lane >> 4, l16 = lane & 15;
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][DN_NF];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < DN_NF; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // ring of DN_STAGES slots, loads issued DN_STAGES - 1 stages ahead
+  constexpr int AHEAD = DN_STAGES - 1;
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p)
+    if (p < nk) stage_in(p);
+  static_assert(AHEAD >= 1 && AHEAD <= 3, "ring depth 2..4");
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* s = smem + buf * STAGE;
+    const int newer = min(kt + AHEAD - 1, nk - 1) - kt;   // stages issued after stage kt, still allowed in flight
+    if (newer >= 2) wait_vmcnt<2 * DN_GROUPS_PER_WAVE>();
+    else if (newer == 1) wait_vmcnt<DN_GROUPS_PER_WAVE>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    if (kt + AHEAD < nk) stage_in(kt + AHEAD);
+    const uint16_t* s = smem + (kt % DN_STAGES) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < PF_BK / 32; ++ks) {
-      const int ko = ks * 32 + g * 8;
-      u32x4_t ha[4], wb[4];
+      const int c = ks * 4 + g;
+      u32x4_t ha[4], wb[DN_NF];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ha[i] = *reinterpret_cast<const u32x4_t*>(s + lds_off(wm * 64 + i * 16 + l16, c));
+#pragma unroll
+      for (int j = 0; j < DN_NF; ++j)
+        wb[j] = *reinterpret_cast<const u32x4_t*>(s + lds_off(PF_BM + wn * (DN_NF * 16) + j * 16 + l16, c));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        ha[i] = *reinterpret_cast<const u32x4_t*>(s + (wm * 64 + i * 16 + l16) * PF_LD + ko);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wb[j] = *reinterpret_cast<const u32x4_t*>(s + (PF_BM + wn * 64 + j * 16 + l16) * PF_LD + ko);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(ha[i], wb[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      sstore(buf ^ 1);
-      __syncthreads();
+        for (int j = 0; j < DN_NF; ++j) acc[i][j] = mfma_bf16(ha[i], wb[j], acc[i][j]);
     }
   }
 
   // epilogue: acc[t][n] += w * y
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + j * 16 + l16;
+  for (int j = 0; j < DN_NF; ++j) {
+    const int n = n0 + wn * (DN_NF * 16) + j * 16 + l16;
     if (n >= H) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -334,8 +396,8 @@ __global__ void __launch_bounds__(256) cast_kernel(const float* __restrict__ acc
 
 // ---------------------------------------------------------------- launch --
 
-size_t prefill_gateup_lds() { return size_t(2) * (2 * PF_BN + PF_BM) * PF_LD * sizeof(uint16_t); }
-size_t prefill_down_lds() { return size_t(2) * (2 * PF_BM) * PF_LD * sizeof(uint16_t); }
+size_t prefill_gateup_lds() { return size_t(PF_STAGES) * GU_ROWS * PF_BK * sizeof(uint16_t); }
+size_t prefill_down_lds() { return size_t(DN_STAGES) * DN_ROWS * PF_BK * sizeof(uint16_t); }
 
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark) {
   // dynamic LDS above 64 KiB must be allowed per kernel (thread-safe one-time set-up)
@@ -350,12 +412,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   PrefillArgs g = a;
   const int nmax = a.I > a.Is ? a.I : a.Is;
   g.n_col_tiles = (nmax + PF_BN - 1) / PF_BN;
-  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(g.n_row_tiles * g.n_col_tiles), dim3(256),
+  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(g.n_row_tiles * g.n_col_tiles), dim3(64 * GU_WAVES),
                      prefill_gateup_lds(), st, g);
   if (mark) mark->mark(st);
   PrefillArgs d = a;
   d.n_col_tiles = (a.H + PF_BN - 1) / PF_BN;
-  hipLaunchKernelGGL(prefill_down_kernel, dim3(d.n_row_tiles * d.n_col_tiles), dim3(256),
+  hipLaunchKernelGGL(prefill_down_kernel, dim3(d.n_row_tiles * d.n_col_tiles), dim3(64 * DN_WAVES),
                      prefill_down_lds(), st, d);
   if (mark) mark->mark(st);
   const long n = long(a.T) * a.H;

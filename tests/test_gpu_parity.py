@@ -248,5 +248,8 @@ def test_graph_replay_matches_eager(m, name, path):
         if path != 2:    # decode: deterministic, bit-exact
             assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
                                eager.view(torch.int16) if eager.dtype == torch.bfloat16 else eager), r
-        else:            # prefill combine adds k + S terms with float atomics: order may vary
-            assert H.relerr(H.to_f64(out), H.to_f64(eager)) < 1e-5, r
+        else:            # prefill combine adds k + S terms with float atomics: the fp32 sum
+            # may differ in its last bits, which can move the bf16 rounding by one ulp
+            o, e = H.to_f64(out), H.to_f64(eager)
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
+            assert (np.abs(o - e) <= ulp).all(), r
