@@ -22,9 +22,6 @@ namespace {
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (prefill row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
 constexpr size_t kAlign = 256;
-#ifndef MOE_DOWN_WAVES
-#define MOE_DOWN_WAVES 4096                   // target waves of the decode down launch
-#endif
 
 size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 long roundup(long n, long m) { return (n + m - 1) / m * m; }
@@ -37,7 +34,6 @@ struct Layout {
   size_t h, partials, acc;
   long h_plane;
   int h_stride;
-  int nsplit;
   int t_pad;
   size_t total;
 };
@@ -68,11 +64,6 @@ int choose_path(const moe_shape_t* s) {
   return MOE_PATH_DECODE;
 }
 
-int decode_steps(int w_dtype, int K) {
-  if (w_dtype == MOE_Q4_0) return (K / 32 + 3) / 4;
-  return w_dtype == MOE_F32 ? K / 16 : K / 32;
-}
-
 // route_only: buffers for moe_route over all T tokens.
 Layout make_layout(const moe_shape_t* s, bool route_only) {
   Layout L{};
@@ -101,15 +92,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     L.h_plane = rows * L.h_stride;
     const size_t elem = s->w_dtype == MOE_Q4_0 ? 2 : 4;   // fp16 | fp32 | bf16 hi + lo planes
     L.h = take(size_t(L.h_plane) * elem);
-    const int n_rt = H / 16;
-    const long slots = std::min<long>(E, long(Tr) * k);
-    const long steps_max = slots * decode_steps(s->w_dtype, I) + long(S) * (S ? decode_steps(s->w_dtype, Is) : 0);
-    const long waves = Tr > 16 ? 2L * MOE_DOWN_WAVES : MOE_DOWN_WAVES;   // heavier steps with 4 column tiles
-    int nsplit = int((waves + 4L * n_rt - 1) / (4L * n_rt));
-    nsplit = std::max(1, std::min(nsplit, 64));
-    nsplit = int(std::max<long>(1, std::min<long>(nsplit, steps_max / 16)));
-    L.nsplit = nsplit;
-    L.partials = nsplit > 1 ? take(size_t(nsplit) * H * Tr * 4) : 0;
+    L.partials = take(size_t(rows) * H * 4);
   }
   if (!route_only && L.path == MOE_PATH_PREFILL) {
     L.t_pad = int(roundup(T, kTileM));
@@ -305,7 +288,10 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     uint8_t* oc = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
     StageEvents sev{events, n_events};
     sev.mark(st);
-    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rb, 1);   // decode uses no padding
+    // decode uses no padding, so the tile table would hold one entry per row: it is not written
+    moe::RouteBufs rbd = rb;
+    rbd.tile_expert = nullptr;
+    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rbd, 1);
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
@@ -318,9 +304,8 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.T = Tc; d.H = s->H; d.E = s->E; d.I = s->I; d.k = s->top_k; d.S = s->n_shared;
     d.Is = has_shared ? s->I_shared : 0;
     d.n_routed_slots = std::min(s->E, Tc * s->top_k);
-    d.nsplit = L.nsplit;
     d.active = rb.active; d.counts = rb.counts; d.offsets = rb.offsets; d.cprefix = rb.cprefix;
-    d.sorted_ids = rb.sorted_ids; d.topk_w = rb.topk_w;
+    d.sorted_ids = rb.sorted_ids; d.topk_w = rb.topk_w; d.inv = rb.inv;
     d.h = ws + L.h;
     d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
     d.h_stride = L.h_stride;

@@ -153,7 +153,7 @@ struct RouteBufs {
   int32_t* cprefix;     // [E+1] unpadded prefix of counts
   int32_t* active;      // [E+1]
   int32_t* sorted_ids;  // [capacity]
-  int32_t* tile_expert; // [n_tiles]
+  int32_t* tile_expert; // [n_tiles]; nullptr: not written
   int32_t* inv;         // [T*k]
 };
 
@@ -176,13 +176,12 @@ struct DecodeArgs {
   int T, H, E, I, k, S, Is;
   int n_routed_slots;   // min(E, T*k)
   int n_row_tiles;      // gate/up: ceil(max(I, Is) / 16); down: H / 16
-  int nsplit;           // down: work-groups per output row tile
   const int32_t* active; const int32_t* counts; const int32_t* offsets; const int32_t* cprefix;
-  const int32_t* sorted_ids; const float* topk_w;
+  const int32_t* sorted_ids; const float* topk_w; const int32_t* inv;
   void* h;              // activations between the two launches
   long h_plane;         // elements per plane (bf16 hi/lo planes)
   int h_stride;         // elements per h row
-  float* partials;      // down: [nsplit][T][H] when nsplit > 1
+  float* partials;      // down: [T*k + S*T][H] weighted expert output rows
   void* out;            // [T, H]
 };
 

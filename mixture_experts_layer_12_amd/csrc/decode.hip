@@ -14,22 +14,21 @@
 // experts are extra slots of the same grid, and Q4_0 blocks are expanded in
 // registers only.
 //
-// Two launches:
+// Three launches:
 //   gate/up:  grid (row tile of 16 intermediate rows, expert slot).  Slots are
 //             the active routed experts (compact list built by the router)
 //             followed by the shared experts.  The 4 waves of a work-group
 //             split the hidden dimension; partial sums meet in LDS.  The
 //             epilogue applies silu(g) * u and the routing weight and writes
 //             the activation rows in the format the down launch consumes.
-//   down:     grid (row tile of 16 hidden outputs, split).  The waves of all
-//             splits of one row tile share the (slot, k) space of that row
-//             tile evenly; each wave folds its partial outputs into a private
-//             LDS accumulator indexed by token and the work-group sums its
-//             waves in a fixed order.  With one split the work-group writes
-//             `out`; otherwise it writes its split's partial and a small
-//             combine launch sums the splits in a fixed order.  The combine is
-//             deterministic, needs no atomics, and needs no device-wide fence
-//             (the kernel boundary orders the partials and their sum).
+//   down:     grid (row tile of 16 hidden outputs, expert slot), the same
+//             shape as gate/up: the 4 waves split the slot's intermediate
+//             dimension and meet in LDS; the work-group writes the slot's
+//             routing-weighted output rows (one row per assignment) once.
+//   combine:  out[t] = the k assignment rows of token t (located through the
+//             dispatch's inverse permutation) plus its shared-expert rows,
+//             summed in a fixed order.  Deterministic, no atomics, and no
+//             device-wide fence (the kernel boundary orders the handoff).
 //
 // Matrix cores do the dot products: weights are the A operand (16 rows per
 // wave tile), tokens the B operand (16 per column tile).  bf16 weights use the
@@ -99,56 +98,89 @@ template <> struct XFrag<DT_BF16, DT_BF16> { u32x4_t v; };
 template <> struct XFrag<DT_BF16, DT_F32> { u32x4_t hi, lo; };
 template <int XT> struct XFrag<DT_Q4, XT> { u32x4_t v[4]; };
 
+// Raw activation words of one step, loaded with the step's weights and only
+// turned into MFMA operands (cook_x) when the step is computed, so that no
+// wait for them is placed where the loads are issued.
+template <int WT, int XT> struct XRaw;
+template <> struct XRaw<DT_F32, DT_F32> { u32x4_t t; };
+template <> struct XRaw<DT_F32, DT_BF16> { u32x2_t t; };
+template <> struct XRaw<DT_BF16, DT_BF16> { u32x4_t t; };
+template <> struct XRaw<DT_BF16, DT_F32> { u32x4_t t0, t1; };
+template <> struct XRaw<DT_Q4, DT_F32> { u32x4_t t[8]; };
+template <> struct XRaw<DT_Q4, DT_BF16> { u32x4_t t[4]; };
+
 template <int WT, int XT>
-__device__ __forceinline__ XFrag<WT, XT> load_x(const uint8_t* xrow, bool ok, int s, int g, int K) {
-  XFrag<WT, XT> b;
+__device__ __forceinline__ XRaw<WT, XT> load_x_raw(const uint8_t* xrow, int s, int g, int K) {
+  XRaw<WT, XT> r;
   if constexpr (WT == DT_F32) {
     const int k0 = s * 16 + g * 4;
-    if constexpr (XT == DT_F32) {
-      u32x4_t t = ldg16(xrow + size_t(k0) * 4);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) b.v[m] = ok ? __uint_as_float(t[m]) : 0.f;
-    } else {
-      u32x2_t t = ldg8(xrow + size_t(k0) * 2);
-      b.v[0] = ok ? bf16_lo(t[0]) : 0.f; b.v[1] = ok ? bf16_hi(t[0]) : 0.f;
-      b.v[2] = ok ? bf16_lo(t[1]) : 0.f; b.v[3] = ok ? bf16_hi(t[1]) : 0.f;
-    }
+    if constexpr (XT == DT_F32) r.t = ldg16(xrow + size_t(k0) * 4);
+    else r.t = ldg8(xrow + size_t(k0) * 2);
   } else if constexpr (WT == DT_BF16) {
     const int k0 = s * 32 + g * 8;
     if constexpr (XT == DT_BF16) {
-      u32x4_t t = ldg16(xrow + size_t(k0) * 2);
-      const u32x4_t z = {0, 0, 0, 0};
-      b.v = ok ? t : z;
+      r.t = ldg16(xrow + size_t(k0) * 2);
     } else {
       const float* xp = reinterpret_cast<const float*>(xrow) + k0;
-      u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
-      float v[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v[m] = ok ? __uint_as_float(t0[m]) : 0.f;
-        v[m + 4] = ok ? __uint_as_float(t1[m]) : 0.f;
-      }
-      split_bf16x8(v, b.hi, b.lo);
+      r.t0 = ldg16(xp);
+      r.t1 = ldg16(xp + 4);
     }
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
-    ok = ok && blk < nblk;
     blk = blk < nblk ? blk : nblk - 1;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int k0 = blk * 32 + f * 8;
       if constexpr (XT == DT_F32) {
         const float* xp = reinterpret_cast<const float*>(xrow) + k0;
-        u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
+        r.t[2 * f] = ldg16(xp);
+        r.t[2 * f + 1] = ldg16(xp + 4);
+      } else {
+        r.t[f] = ldg16(xrow + size_t(k0) * 2);
+      }
+    }
+  }
+  return r;
+}
+
+template <int WT, int XT>
+__device__ __forceinline__ XFrag<WT, XT> cook_x(const XRaw<WT, XT>& r, bool ok, int s, int g, int K) {
+  XFrag<WT, XT> b;
+  if constexpr (WT == DT_F32) {
+    if constexpr (XT == DT_F32) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) b.v[m] = ok ? __uint_as_float(r.t[m]) : 0.f;
+    } else {
+      b.v[0] = ok ? bf16_lo(r.t[0]) : 0.f; b.v[1] = ok ? bf16_hi(r.t[0]) : 0.f;
+      b.v[2] = ok ? bf16_lo(r.t[1]) : 0.f; b.v[3] = ok ? bf16_hi(r.t[1]) : 0.f;
+    }
+  } else if constexpr (WT == DT_BF16) {
+    if constexpr (XT == DT_BF16) {
+      const u32x4_t z = {0, 0, 0, 0};
+      b.v = ok ? r.t : z;
+    } else {
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        v[m] = ok ? __uint_as_float(r.t0[m]) : 0.f;
+        v[m + 4] = ok ? __uint_as_float(r.t1[m]) : 0.f;
+      }
+      split_bf16x8(v, b.hi, b.lo);
+    }
+  } else {
+    ok = ok && (4 * s + g) < K / 32;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if constexpr (XT == DT_F32) {
+        const u32x4_t t0 = r.t[2 * f], t1 = r.t[2 * f + 1];
         b.v[f][0] = pack_f16(__uint_as_float(t0[0]), __uint_as_float(t0[1]));
         b.v[f][1] = pack_f16(__uint_as_float(t0[2]), __uint_as_float(t0[3]));
         b.v[f][2] = pack_f16(__uint_as_float(t1[0]), __uint_as_float(t1[1]));
         b.v[f][3] = pack_f16(__uint_as_float(t1[2]), __uint_as_float(t1[3]));
       } else {
-        u32x4_t t = ldg16(xrow + size_t(k0) * 2);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) b.v[f][m] = bf16x2_to_f16x2(t[m]);
+        for (int m = 0; m < 4; ++m) b.v[f][m] = bf16x2_to_f16x2(r.t[f][m]);
       }
       if (!ok) b.v[f] = u32x4_t{0, 0, 0, 0};
     }
@@ -203,19 +235,68 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT
 
 // Unroll depth: keep several 16-byte weight loads in flight per lane.
 #ifndef MOE_GU_UNROLL_BF16
-#define MOE_GU_UNROLL_BF16 8
+#define MOE_GU_UNROLL_BF16 4
 #endif
 #ifndef MOE_DN_UNROLL_BF16
-#define MOE_DN_UNROLL_BF16 8
+#define MOE_DN_UNROLL_BF16 4
 #endif
 template <int WT, int NCT>
 struct Unroll {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 4 : 1);
+  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 2 : 1);
 };
 template <int WT, int NCT>
 struct UnrollDown {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 4) : (NCT == 1 ? 8 : 2);
+  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 1) : (NCT == 1 ? 2 : 1);
 };
+
+// Steps [s0, s1) in groups of U with the weight loads of group i+1 issued
+// before the MFMAs of group i, so the wave keeps weight bytes in flight
+// across group boundaries (a plain unrolled loop drains them at every group).
+// `load(s)` returns the A fragments of step s, `body(s, frag)` consumes them.
+#ifndef MOE_DECODE_MASKED_B
+#define MOE_DECODE_MASKED_B 0
+#endif
+#ifndef MOE_DECODE_PIPELINE
+#define MOE_DECODE_PIPELINE 1
+#endif
+template <int U, class Load, class Body>
+__device__ __forceinline__ void stream_steps(int s0, int s1, Load load, Body body) {
+  using F = decltype(load(0));
+  int s = s0;
+  if (!MOE_DECODE_PIPELINE) {
+    for (; s + U <= s1; s += U) {
+      F cur[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = load(s + u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) body(s + u, cur[u]);
+    }
+    for (; s < s1; ++s) body(s, load(s));
+    return;
+  }
+  if (s + U <= s1) {
+    F cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load(s + u);
+    for (; s + 2 * U <= s1; s += U) {
+      F nxt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u] = load(s + U + u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) body(s + u, cur[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) body(s + u, cur[u]);
+    s += U;
+  }
+  for (; s < s1; ++s) body(s, load(s));
+}
+
+template <int WT, int XT, int NCT>
+struct GUStep { AFrag<WT> g, u; XRaw<WT, XT> x[NCT]; };
+
 
 // ------------------------------------------------------------- gate/up --
 
@@ -267,29 +348,29 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   for (int ct = 0; ct < NCT; ++ct) accg[ct] = accu[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   constexpr int U = Unroll<WT, NCT>::v;
-  auto body = [&](int s, const AFrag<WT>& fa_g, const AFrag<WT>& fa_u) {
-    const AReady<WT> ag = prep_a<WT>(fa_g), au = prep_a<WT>(fa_u);
+  auto load = [&](int s) {
+    GUStep<WT, XT, NCT> st;
+    st.g = load_a<WT>(rg, s, g, K);
+    st.u = load_a<WT>(ru, s, g, K);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      if (NCT == 1 || ct < nct) {
+        if (!MOE_DECODE_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<WT, XT>(xrow[ct], s, g, K);
+      }
+    return st;
+  };
+  auto body = [&](int s, const GUStep<WT, XT, NCT>& st) {
+    const AReady<WT> ag = prep_a<WT>(st.g), au = prep_a<WT>(st.u);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (NCT == 1 || ct < nct) {
-        XFrag<WT, XT> b = load_x<WT, XT>(xrow[ct], xok[ct], s, g, K);
+        const XFrag<WT, XT> b = cook_x<WT, XT>(st.x[ct], xok[ct], s, g, K);
         accg[ct] = mma_ready<WT, XT>(ag, b, accg[ct]);
         accu[ct] = mma_ready<WT, XT>(au, b, accu[ct]);
       }
     }
   };
-  int s = s0;
-  for (; s + U <= s1; s += U) {
-    AFrag<WT> fg[U], fu[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      fg[u] = load_a<WT>(rg, s + u, g, K);
-      fu[u] = load_a<WT>(ru, s + u, g, K);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) body(s + u, fg[u], fu[u]);
-  }
-  for (; s < s1; ++s) body(s, load_a<WT>(rg, s, g, K), load_a<WT>(ru, s, g, K));
+  stream_steps<U>(s0, s1, load, body);
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -339,29 +420,40 @@ template <> struct HFrag<DT_BF16> { u32x4_t hi, lo; };
 template <> struct HFrag<DT_Q4> { u32x4_t v[4]; };
 
 template <int WT>
-__device__ __forceinline__ HFrag<WT> load_h(const DecodeArgs& a, size_t row_off, bool ok, int s, int g, int K) {
+__device__ __forceinline__ HFrag<WT> load_h_raw(const DecodeArgs& a, size_t row_off, int s, int g, int K) {
   HFrag<WT> b;
-  const u32x4_t z = {0, 0, 0, 0};
   if constexpr (WT == DT_F32) {
-    u32x4_t t = ldg16(reinterpret_cast<const float*>(a.h) + row_off + s * 16 + g * 4);
+    const u32x4_t t = ldg16(reinterpret_cast<const float*>(a.h) + row_off + s * 16 + g * 4);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) b.v[m] = ok ? __uint_as_float(t[m]) : 0.f;
+    for (int m = 0; m < 4; ++m) b.v[m] = __uint_as_float(t[m]);
   } else if constexpr (WT == DT_BF16) {
     const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + s * 32 + g * 8;
-    u32x4_t t0 = ldg16(hp), t1 = ldg16(hp + a.h_plane);
-    b.hi = ok ? t0 : z;
-    b.lo = ok ? t1 : z;
+    b.hi = ldg16(hp);
+    b.lo = ldg16(hp + a.h_plane);
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
-    ok = ok && blk < nblk;
     blk = blk < nblk ? blk : nblk - 1;
     const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + blk * 32;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      u32x4_t t = ldg16(hp + f * 8);
-      b.v[f] = ok ? t : z;
-    }
+    for (int f = 0; f < 4; ++f) b.v[f] = ldg16(hp + f * 8);
+  }
+  return b;
+}
+
+template <int WT>
+__device__ __forceinline__ HFrag<WT> cook_h(HFrag<WT> b, bool ok, int s, int g, int K) {
+  const u32x4_t z = {0, 0, 0, 0};
+  if constexpr (WT == DT_F32) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) b.v[m] = ok ? b.v[m] : 0.f;
+  } else if constexpr (WT == DT_BF16) {
+    b.hi = ok ? b.hi : z;
+    b.lo = ok ? b.lo : z;
+  } else {
+    ok = ok && (4 * s + g) < K / 32;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) b.v[f] = ok ? b.v[f] : z;
   }
   return b;
 }
@@ -381,132 +473,104 @@ __device__ __forceinline__ f32x4_t mma_h(const AReady<WT>& a, const HFrag<WT>& b
   return c;
 }
 
-template <int WT, int OT, int NCT>
+template <int WT, int NCT>
+struct DNStep { AFrag<WT> a; HFrag<WT> h[NCT]; };
+
+// One work-group: 16 hidden outputs (rows of the down projection) of one
+// expert slot, for every token of that slot.  Its 4 waves split the slot's
+// intermediate dimension; partial sums meet in LDS.  The result rows are the
+// routing-weighted expert outputs; they go to `partials` at the same row the
+// activations use (one row per routed assignment, then the shared tokens).
+template <int WT, int NCT>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
-  extern __shared__ float acc_lds[];     // [4 waves][16 rows][T]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
-  const int rt = blockIdx.x, split = blockIdx.y;
-  const int T = a.T, g = lane >> 4, H = a.H;
-  float* myacc = acc_lds + wave * 16 * T;
-  for (int i = lane; i < 16 * T; i += 64) myacc[i] = 0.f;
+  __shared__ f32x4_t red[4][NCT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rt = blockIdx.x, slot = blockIdx.y;
+  const bool routed = slot < a.n_routed_slots;
+  int e, n_e, hrow0, K;
+  long n_mat;
+  const uint8_t* base;
+  if (routed) {
+    if (slot >= a.active[0]) return;
+    e = a.active[1 + slot];
+    n_e = a.counts[e];
+    hrow0 = a.cprefix[e];
+    K = a.I; base = a.wd; n_mat = a.E;
+  } else {
+    e = slot - a.n_routed_slots;
+    n_e = a.T;
+    hrow0 = a.T * a.k + e * a.T;
+    K = a.Is; base = a.sd; n_mat = a.S;
+  }
+  const int H = a.H, g = lane >> 4;
+  RowPtr<WT> rw;
+  rw.init(base, n_mat, H, K, e, rt * 16 + (lane & 15));
+  size_t hoff[NCT];
+  bool hok[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = ct * 16 + (lane & 15);
+    hok[ct] = c < n_e;
+    hoff[ct] = size_t(hrow0 + (hok[ct] ? c : 0)) * a.h_stride;
+  }
+  const int nct = (n_e + 15) >> 4;
+  const int nsteps = n_steps<WT>(K);
+  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  f32x4_t acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int n_act = a.active[0];
-  const int SR = n_steps<WT>(a.I), SS = n_steps<WT>(a.Is);
-  const long routed_steps = long(n_act) * SR;
-  const long total = routed_steps + long(a.S) * SS;
-  const long G = long(a.nsplit) * 4, gw = long(split) * 4 + wave;
-  long pos = total * gw / G;
-  const long r1 = total * (gw + 1) / G;
-  const int row = rt * 16 + (lane & 15);
   constexpr int U = UnrollDown<WT, NCT>::v;
-
-  while (pos < r1) {
-    int e, n_e, hrow0, seg = 0, K, sstep, sl_steps;
-    long n_mat;
-    const uint8_t* base;
-    bool routed;
-    if (pos < routed_steps) {
-      const int slot = int(pos / SR);
-      sstep = int(pos % SR);
-      sl_steps = SR;
-      e = a.active[1 + slot];
-      n_e = a.counts[e];
-      seg = a.offsets[e];
-      hrow0 = a.cprefix[e];
-      K = a.I; base = a.wd; n_mat = a.E; routed = true;
-    } else {
-      const long q = pos - routed_steps;
-      e = int(q / SS);
-      sstep = int(q % SS);
-      sl_steps = SS;
-      n_e = T;
-      hrow0 = T * a.k + e * T;
-      K = a.Is; base = a.sd; n_mat = a.S; routed = false;
-    }
-    const int cnt = int(min(long(sl_steps - sstep), r1 - pos));
-    RowPtr<WT> rw;
-    rw.init(base, n_mat, H, K, e, row);
-    size_t hoff[NCT];
-    bool hok[NCT];
-    int tok[NCT];
+  auto load = [&](int s) {
+    DNStep<WT, NCT> st;
+    st.a = load_a<WT>(rw, s, g, K);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      if (NCT == 1 || ct < nct) {
+        if (!MOE_DECODE_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<WT>(a, hoff[ct], s, g, K);
+      }
+    return st;
+  };
+  auto body = [&](int s, const DNStep<WT, NCT>& st) {
+    const AReady<WT> ar = prep_a<WT>(st.a);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int c = ct * 16 + (lane & 15);
-      hok[ct] = c < n_e;
-      const int cc = hok[ct] ? c : 0;
-      hoff[ct] = size_t(hrow0 + cc) * a.h_stride;
-      tok[ct] = routed ? a.sorted_ids[seg + cc] / a.k : cc;
+      if (NCT == 1 || ct < nct) acc[ct] = mma_h<WT>(ar, cook_h<WT>(st.h[ct], hok[ct], s, g, K), acc[ct]);
     }
-    const int nct = (n_e + 15) >> 4;
-    f32x4_t acc[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  stream_steps<U>(s0, s1, load, body);
 
-    auto body = [&](int s, const AFrag<WT>& fa) {
-      const AReady<WT> ar = prep_a<WT>(fa);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        if (NCT == 1 || ct < nct) {
-          HFrag<WT> b = load_h<WT>(a, hoff[ct], hok[ct], s, g, K);
-          acc[ct] = mma_h<WT>(ar, b, acc[ct]);
-        }
-      }
-    };
-    int s = sstep;
-    const int s_end = sstep + cnt;
-    for (; s + U <= s_end; s += U) {
-      AFrag<WT> fa[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) fa[u] = load_a<WT>(rw, s + u, g, K);
-#pragma unroll
-      for (int u = 0; u < U; ++u) body(s + u, fa[u]);
-    }
-    for (; s < s_end; ++s) body(s, load_a<WT>(rw, s, g, K));
-
-    // fold into this wave's accumulator (distinct (row, token) per lane)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if ((NCT == 1 || ct < nct) && hok[ct]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) myacc[((lane >> 4) * 4 + i) * T + tok[ct]] += acc[ct][i];
-      }
-    }
-    pos += cnt;
-  }
+  for (int ct = 0; ct < NCT; ++ct) red[wave][ct][lane] = acc[ct];
   __syncthreads();
-
-  // waves -> work-group sum, in wave order (region of wave 0 reused)
-  for (int idx = tid; idx < 16 * T; idx += 256) {
-    float v = acc_lds[idx];
+  if (wave != 0) return;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += acc_lds[w * 16 * T + idx];
-    acc_lds[idx] = v;
-  }
-  __syncthreads();
-  for (int j = tid; j < 16 * T; j += 256) {
-    const int t = j >> 4, r = j & 15;
-    const float v = acc_lds[r * T + t];
-    const size_t o = size_t(t) * H + rt * 16 + r;
-    if (a.nsplit > 1) {
-      a.partials[size_t(split) * T * H + o] = v;      // summed by decode_combine_kernel
-    } else if constexpr (OT == DT_F32) {
-      reinterpret_cast<float*>(a.out)[o] = v;
-    } else {
-      reinterpret_cast<uint16_t*>(a.out)[o] = uint16_t(f32_to_bf16(v));
-    }
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (!(NCT == 1 || ct < nct)) continue;
+    f32x4_t v = red[0][ct][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[w][ct][lane];
+    const int c = ct * 16 + (lane & 15);
+    if (c >= n_e) continue;
+    // lane holds rows 4*(lane/16) + 0..3 of this tile for token column c
+    *reinterpret_cast<f32x4_t*>(a.partials + size_t(hrow0 + c) * H + rt * 16 + (lane >> 4) * 4) = v;
   }
 }
 
-// Sum of the split partials [nsplit][T*H] in split order -> out (4 outputs per thread).
+// out[t] = sum over j of the partial row of assignment t*k + j (found through
+// inv), then the shared experts' rows, in that fixed order; 4 outputs per thread.
 template <int OT>
-__global__ void __launch_bounds__(256) decode_combine_kernel(const float* __restrict__ partials, void* out,
-                                                             int nsplit, long n) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+  const int H4 = a.H / 4;
   const long i4 = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i4 * 4 >= n) return;
-  f32x4_t v = reinterpret_cast<const f32x4_t*>(partials)[i4];
-  for (int sp = 1; sp < nsplit; ++sp) v += reinterpret_cast<const f32x4_t*>(partials + size_t(sp) * n)[i4];
-  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(out)[i4] = v;
-  else reinterpret_cast<u32x2_t*>(out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  if (i4 >= long(a.T) * H4) return;
+  const int t = int(i4 / H4), h4 = int(i4 % H4);
+  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(a.partials);
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.k; ++j) v += p[size_t(a.inv[t * a.k + j]) * H4 + h4];
+  for (int s = 0; s < a.S; ++s) v += p[size_t(a.T * a.k + s * a.T + t) * H4 + h4];
+  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
+  else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
 }
 
 // -------------------------------------------------------------- launch --
@@ -516,14 +580,10 @@ static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
-  dim3 g2(a.H / 16, a.nsplit);
-  const size_t lds = size_t(4) * 16 * a.T * sizeof(float);
-  hipLaunchKernelGGL((decode_down_kernel<WT, XT, NCT>), g2, b, lds, st, a);
-  if (a.nsplit > 1) {
-    const long n = long(a.T) * a.H;
-    hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n / 4 + 255) / 256)), b, 0, st, a.partials, a.out,
-                       a.nsplit, n);
-  }
+  dim3 g2(a.H / 16, a.n_routed_slots + a.S);
+  hipLaunchKernelGGL((decode_down_kernel<WT, NCT>), g2, b, 0, st, a);
+  const long n4 = long(a.T) * a.H / 4;
+  hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n4 + 255) / 256)), b, 0, st, a);
   if (mark) mark->mark(st);
 }
 

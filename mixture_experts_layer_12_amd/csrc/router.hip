@@ -332,7 +332,7 @@ __device__ void dispatch_wg(const RouterArgs& a, int* lds, const int32_t* ids) {
   for (int e = wave; e < E; e += NW)
     for (int p = off[e] + cnt[e] + lane; p < off[e + 1]; p += 64) rb.sorted_ids[p] = n;
   for (int p = off[E] + tid; p < a.capacity; p += NT) rb.sorted_ids[p] = n;
-  const int n_tiles = a.capacity / M;
+  const int n_tiles = rb.tile_expert ? a.capacity / M : 0;   // the decode path reads no tile table
   for (int i = tid; i < n_tiles; i += NT) {
     const int r = i * M;
     int e = -1;
