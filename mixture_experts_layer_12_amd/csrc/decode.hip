@@ -253,8 +253,13 @@ struct UnrollDown {
 // before the MFMAs of group i, so the wave keeps weight bytes in flight
 // across group boundaries (a plain unrolled loop drains them at every group).
 // `load(s)` returns the A fragments of step s, `body(s, frag)` consumes them.
-#ifndef MOE_DECODE_MASKED_B
-#define MOE_DECODE_MASKED_B 0
+// Masked B: lanes of token columns past the slot's count issue no activation
+// loads (their operand is zeroed anyway).  Pays off in gate/up, not in down.
+#ifndef MOE_GU_MASKED_B
+#define MOE_GU_MASKED_B 1
+#endif
+#ifndef MOE_DN_MASKED_B
+#define MOE_DN_MASKED_B 0
 #endif
 #ifndef MOE_DECODE_PIPELINE
 #define MOE_DECODE_PIPELINE 1
@@ -355,7 +360,7 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       if (NCT == 1 || ct < nct) {
-        if (!MOE_DECODE_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<WT, XT>(xrow[ct], s, g, K);
+        if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<WT, XT>(xrow[ct], s, g, K);
       }
     return st;
   };
@@ -527,7 +532,7 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       if (NCT == 1 || ct < nct) {
-        if (!MOE_DECODE_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<WT>(a, hoff[ct], s, g, K);
+        if (!MOE_DN_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<WT>(a, hoff[ct], s, g, K);
       }
     return st;
   };
