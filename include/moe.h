@@ -53,9 +53,15 @@ enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2 };
 
 /* execution path (moe_shape_t.path) */
 enum {
-  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill */
+  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill;
+                           the single-launch decode where it applies (see below) */
   MOE_PATH_DECODE = 1,  /* weight-streaming mat-vec kernels, any supported dtype, any T */
-  MOE_PATH_PREFILL = 2  /* bf16 MFMA grouped GEMMs; needs x, experts bf16 */
+  MOE_PATH_PREFILL = 2, /* bf16 MFMA grouped GEMMs; needs x, experts bf16 */
+  MOE_PATH_DECODE_FUSED = 3  /* the decode kernels as one cooperative launch per pass of
+                           at most 64 tokens; needs router_dtype == x_dtype and
+                           top_k <= 16.  While `stream` is being captured into a
+                           graph the call runs path 1 instead (a captured launch
+                           would replay the completion tags of the capture). */
 };
 
 /* return codes */
@@ -159,6 +165,7 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
  * passed as void*) on `stream` at the stage boundaries of each pass:
  * events[0] before the first launch, events[i] after launch i.  Launches of
  * one pass: decode path 1 router+dispatch, 2 gate/up, 3 down+combine;
+ * single-launch decode 1 the whole pass;
  * prefill path 1 router+dispatch, 2 gate/up GEMM, 3 down GEMM + combine,
  * 4 cast.  A decode call with T > 64 makes several passes; the events then
  * hold the last pass.  Entries beyond n_events, or NULL entries, are skipped.

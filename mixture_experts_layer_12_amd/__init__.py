@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
 
 # enums of moe.h
 MOE_F32, MOE_BF16, MOE_Q4_0 = 0, 1, 2
-MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_DECODE_FUSED = 0, 1, 2, 3
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 

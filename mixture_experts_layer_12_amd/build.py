@@ -5,11 +5,12 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/api.cpp", "csrc/router.hip", "csrc/decode.hip", "csrc/prefill.hip"]
-HEADERS = ["csrc/common.hpp", "../include/moe.h"]
+SOURCES = ["csrc/api.cpp", "csrc/router.hip", "csrc/decode.hip", "csrc/decode_fused.hip", "csrc/prefill.hip"]
+HEADERS = ["csrc/common.hpp", "csrc/router_items.hpp", "csrc/decode_items.hpp", "../include/moe.h"]
 OUT = os.path.join(HERE, "lib", "libmoe.so")
 
 
@@ -20,27 +21,47 @@ def hipcc() -> str:
     raise FileNotFoundError("hipcc not found")
 
 
-def command(out: str = OUT) -> list:
-    return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-munsafe-fp-atomics",
-            # packed fp32 ops are kept out of the generated code on purpose
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
-            *[os.path.join(HERE, s) for s in SOURCES], "-o", out]
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+         # packed fp32 ops are kept out of the generated code on purpose
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def compile_command(src: str, obj: str) -> list:
+    return [hipcc(), *FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
+            "-c", os.path.join(HERE, src), "-o", obj]
+
+
+def _check(r, what):
+    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({r.returncode}):\n{err}")
+    return err
 
 
 def build(verbose: bool = True) -> str:
+    """Compile every source (in parallel) and link lib/libmoe.so; always rebuilds."""
     os.makedirs(os.path.dirname(OUT), exist_ok=True)
     tmp = OUT + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as d:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            cmd = compile_command(src, obj)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        warnings = []
+        for src, p in procs:
+            out, err = p.communicate()
+            warnings.append(_check(subprocess.CompletedProcess(p.args, p.returncode, out, err), src))
+        link = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        warnings.append(_check(subprocess.run(link, capture_output=True, text=True), "link"))
+    text = "\n".join(w for w in warnings if w.strip())
+    if text.strip() and verbose:
+        print(text, file=sys.stderr)
     os.replace(tmp, OUT)
     return OUT
 

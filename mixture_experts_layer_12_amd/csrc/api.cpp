@@ -1,12 +1,16 @@
 // C ABI of the MoE layer forward: argument validation, workspace layout, path
 // choice and kernel launches.  Host code only; the kernels live in
-// router.hip, decode.hip and prefill.hip.  See include/moe.h for the contract.
+// router.hip, decode.hip, decode_fused.hip and prefill.hip.  See include/moe.h
+// for the contract.
 #include "moe.h"
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstdint>
+#include <random>
 
 #include "common.hpp"
 
@@ -15,23 +19,28 @@ hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStrea
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark);
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
+hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t st);
 }  // namespace moe
 
 namespace {
 
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (prefill row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
+constexpr int kFusedMaxK = 16;       // top_k limit of the single-launch decode
+constexpr int kHRowAlign = 64;       // decode activation rows padded to 64 elements (whole 128-byte lines)
 constexpr size_t kAlign = 256;
 
 size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 long roundup(long n, long m) { return (n + m - 1) / m * m; }
 
 struct Layout {
-  int path;            // MOE_PATH_DECODE | MOE_PATH_PREFILL
+  int path;            // MOE_PATH_DECODE | MOE_PATH_PREFILL | MOE_PATH_DECODE_FUSED
   int Tr;              // tokens per routing pass
   int cap, n_tiles;    // sorted-order capacity and tiles for Tr tokens
   size_t logits, topk_ids, topk_w, counts, offsets, cprefix, active, sorted_ids, tile_expert, inv;
   size_t h, partials, acc;
+  size_t flags, error;  // single-launch decode: completion flags [n_items], error tag
+  long n_items;
   long h_plane;
   int h_stride;
   int t_pad;
@@ -51,17 +60,48 @@ int check_shape(const moe_shape_t* s) {
   if (s->x_dtype != MOE_F32 && s->x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (s->router_dtype != MOE_F32 && s->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_Q4_0) return MOE_ERR_DTYPE;
-  if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_PREFILL) return MOE_ERR_SHAPE;
+  if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_DECODE_FUSED) return MOE_ERR_SHAPE;
+  if (s->path == MOE_PATH_DECODE_FUSED && s->router_dtype != s->x_dtype) return MOE_ERR_DTYPE;
+  if (s->path == MOE_PATH_DECODE_FUSED && s->top_k > kFusedMaxK) return MOE_ERR_SHAPE;
   if (s->path == MOE_PATH_PREFILL && (s->x_dtype != MOE_BF16 || s->w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
   // index arithmetic of the largest buffers stays in 32-bit ranges
   if (roundup(T * k + E * (kTileM - 1), kTileM) + S * roundup(T, kTileM) > 2147483647L / 8) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
+bool fused_ok(const moe_shape_t* s) { return s->router_dtype == s->x_dtype && s->top_k <= kFusedMaxK; }
+
 int choose_path(const moe_shape_t* s) {
   if (s->path != MOE_PATH_AUTO) return s->path;
   if (s->x_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 && s->T > kDecodeMaxT) return MOE_PATH_PREFILL;
-  return MOE_PATH_DECODE;
+  return fused_ok(s) ? MOE_PATH_DECODE_FUSED : MOE_PATH_DECODE;
+}
+
+// Work list of one single-launch decode pass of Tc tokens (see decode_fused.hip).
+moe::FusedArgs fused_plan(const moe_shape_t* s, int Tc) {
+  moe::FusedArgs f{};
+  const int S = s->n_shared, Is = S > 0 ? s->I_shared : 0;
+  const int n_slots = std::min(s->E, Tc * s->top_k);
+  f.gu_rt_routed = s->I / 16;
+  f.gu_rt_shared = Is / 16;
+  f.n_logit = 4 * ((s->E + 15) / 16) * ((Tc + 15) / 16);   // 4 partial planes per tile
+  f.end_shared_gu = f.n_logit + S * f.gu_rt_shared;
+  f.end_select = f.end_shared_gu + 1;
+  f.end_gu = f.end_select + n_slots * f.gu_rt_routed;
+  f.end_down = f.end_gu + (n_slots + S) * (s->H / 16);
+  f.n_items = f.end_down + int((long(Tc) * s->H / 4 + 255) / 256);
+  return f;
+}
+
+// Completion tags of the single-launch decode: a process-wide counter started
+// at a random 64-bit value, so that no tag matches leftover workspace contents.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> ctr{[] {
+    std::random_device rd;
+    const unsigned long long t = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+    return ((uint64_t(rd()) << 32) ^ uint64_t(rd()) ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
+  }()};
+  return ctr.fetch_add(1, std::memory_order_relaxed) + 1;
 }
 
 // route_only: buffers for moe_route over all T tokens.
@@ -76,7 +116,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
   L.n_tiles = L.cap / kTileM;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
-  L.logits = take(size_t(Tr) * E * 4);
+  L.logits = take(size_t(Tr) * E * 4 * (L.path == MOE_PATH_DECODE_FUSED ? 4 : 1));
   L.topk_ids = take(size_t(Tr) * k * 4);
   L.topk_w = take(size_t(Tr) * k * 4);
   L.counts = take(size_t(E) * 4);
@@ -87,12 +127,18 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
   L.tile_expert = take(size_t(L.n_tiles) * 4);
   L.inv = take(size_t(Tr) * k * 4);
   L.h_stride = std::max(I, Is);
-  if (!route_only && L.path == MOE_PATH_DECODE) {
+  if (!route_only && (L.path == MOE_PATH_DECODE || L.path == MOE_PATH_DECODE_FUSED)) {
+    L.h_stride = int(roundup(L.h_stride, kHRowAlign));
     const long rows = long(Tr) * k + long(S) * Tr;
     L.h_plane = rows * L.h_stride;
     const size_t elem = s->w_dtype == MOE_Q4_0 ? 2 : 4;   // fp16 | fp32 | bf16 hi + lo planes
     L.h = take(size_t(L.h_plane) * elem);
     L.partials = take(size_t(rows) * H * 4);
+    if (L.path == MOE_PATH_DECODE_FUSED) {
+      L.n_items = fused_plan(s, Tr).n_items;
+      L.flags = take(size_t(L.n_items) * 8);
+      L.error = take(8);
+    }
   }
   if (!route_only && L.path == MOE_PATH_PREFILL) {
     L.t_pad = int(roundup(T, kTileM));
@@ -141,6 +187,7 @@ moe::RouterArgs router_args(const moe_shape_t* s, int T, const void* x, const vo
   a.capacity = int(roundup(long(T) * s->top_k + long(s->E) * (tile_m - 1), tile_m));
   a.n_row_tiles = (s->E + 15) / 16;
   a.n_col_tiles = (T + 15) / 16;
+  a.logit_parts = 1;
   a.zero_f32 = nullptr; a.zero_n = 0;
   a.rb = rb;
   return a;
@@ -281,20 +328,26 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     return hip_status(moe::launch_prefill(p, s->x_dtype, st, events ? &sev : nullptr));
   }
 
-  // decode: passes of at most kDecodeMaxT tokens (each token's output depends on that token only)
+  // decode: passes of at most kDecodeMaxT tokens (each token's output depends on that token only).
+  // The single-launch form is not captured into graphs: a replay would reuse the capture's tags.
+  bool fused = L.path == MOE_PATH_DECODE_FUSED;
+  if (fused) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      cs = hipStreamCaptureStatusActive;
+    }
+    fused = cs == hipStreamCaptureStatusNone;
+  }
   for (int t0 = 0; t0 < s->T; t0 += kDecodeMaxT) {
     const int Tc = std::min(kDecodeMaxT, s->T - t0);
     const uint8_t* xc = static_cast<const uint8_t*>(x) + size_t(t0) * s->H * xb;
     uint8_t* oc = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
     StageEvents sev{events, n_events};
-    sev.mark(st);
     // decode uses no padding, so the tile table would hold one entry per row: it is not written
     moe::RouteBufs rbd = rb;
     rbd.tile_expert = nullptr;
     moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rbd, 1);
-    const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
-    sev.mark(st);
     moe::DecodeArgs d{};
     d.x = xc;
     d.wg = static_cast<const uint8_t*>(w_gate); d.wu = static_cast<const uint8_t*>(w_up);
@@ -311,8 +364,24 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.h_stride = L.h_stride;
     d.partials = reinterpret_cast<float*>(ws + L.partials);
     d.out = oc;
-    const int n_gu_rt = (L.h_stride + 15) / 16;
+    const int n_gu_rt = (std::max(s->I, d.Is) + 15) / 16;
     d.n_row_tiles = n_gu_rt;
+    sev.mark(st);
+    if (fused) {
+      moe::FusedArgs f = fused_plan(s, Tc);
+      f.r = ra;
+      f.r.logit_parts = 4;
+      f.d = d;
+      f.epoch = next_epoch();
+      f.flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
+      f.error = reinterpret_cast<unsigned long long*>(ws + L.error);
+      if (int e = hip_status(moe::launch_decode_fused(f, s->w_dtype, s->x_dtype, st))) return e;
+      sev.mark(st);
+      continue;
+    }
+    const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
+    sev.mark(st);
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))
       return e;
   }

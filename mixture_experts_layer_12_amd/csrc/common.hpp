@@ -135,6 +135,54 @@ __device__ __forceinline__ u32x2_t ldg8(const void* p) {
   return *reinterpret_cast<const u32x2_t*>(p);
 }
 
+// Handoffs between work-groups of one launch (the single-launch decode).  The
+// L2 of each XCD is not coherent with the others, so data that another
+// work-group reads later in the same launch is written with device-scope
+// stores (written through to memory) and flags and small routing values are
+// read with device-scope loads.  COH false: ordinary accesses, for launches
+// whose consumers run in a later kernel.
+template <bool COH>
+__device__ __forceinline__ void st_i32(int32_t* p, int32_t v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_f32(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_u32x2(void* p, u32x2_t v) {
+  if constexpr (COH) {
+    const uint64_t w = uint64_t(v[0]) | (uint64_t(v[1]) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<u32x2_t*>(p) = v;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ void st_f32x4(float* p, f32x4_t v) {
+  if constexpr (COH) {
+    st_u32x2<true>(p, u32x2_t{__float_as_uint(v[0]), __float_as_uint(v[1])});
+    st_u32x2<true>(p + 2, u32x2_t{__float_as_uint(v[2]), __float_as_uint(v[3])});
+  } else {
+    *reinterpret_cast<f32x4_t*>(p) = v;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ int32_t ld_i32(const int32_t* p) {
+  if constexpr (COH) return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float ld_f32(const float* p) {
+  if constexpr (COH)
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+  else return *p;
+}
+
 // Host-side hook called after each kernel launch (stage timing).
 struct StageMarker {
   virtual void mark(hipStream_t st) = 0;
@@ -164,6 +212,7 @@ struct RouterArgs {
   int T, H, E, k;
   int tile_m, capacity;
   int n_row_tiles, n_col_tiles;
+  int logit_parts;      // 1: rb.logits holds the logits; 4: four group planes [4][T][E] without the bias
   float* zero_f32;      // optional buffer to clear (prefill accumulator), or null
   long zero_n;          // its length in floats (multiple of 4)
   RouteBufs rb;
@@ -183,6 +232,24 @@ struct DecodeArgs {
   int h_stride;         // elements per h row
   float* partials;      // down: [T*k + S*T][H] weighted expert output rows
   void* out;            // [T, H]
+};
+
+// Single-launch decode: one work list of items in a fixed order, taken
+// round-robin by a co-resident grid; an item waits only on items of lower
+// index (completion flags carry the call's epoch).
+struct FusedArgs {
+  RouterArgs r;
+  DecodeArgs d;
+  int n_logit;          // [0, n_logit): router logit tiles
+  int end_shared_gu;    // [n_logit, end_shared_gu): shared-expert gate/up row tiles
+  int end_select;       // end_shared_gu: top-k and dispatch (one item)
+  int end_gu;           // [end_select, end_gu): routed gate/up row tiles, slot-major
+  int end_down;         // [end_gu, end_down): down row tiles, slot-major, routed then shared
+  int n_items;          // [end_down, n_items): combine blocks of 1024 outputs
+  int gu_rt_routed, gu_rt_shared;   // gate/up row tiles per routed / shared slot
+  unsigned long long epoch;
+  unsigned long long* flags;        // [n_items]
+  unsigned long long* error;        // holds the epoch when a wait of this call gave up
 };
 
 struct PrefillArgs {

@@ -1,581 +1,26 @@
-// Decode path: the expert FFNs for small batches (T <= 64 per pass), where the
-// layer is bound by reading each engaged expert's weights once from HBM.
-//
-// Sources: "Why MoE on RTX 5090 falls short: a bandwidth measurement"
-// (news.malakhovai.ru): mat-vec work dominates decode kernel time while
-// routing is a small share (kernel-time split paragraph), and kernels that
-// read little per launch do not reach full DRAM bandwidth (bandwidth versus
-// bytes-per-kernel measurement) -- so each launch here covers every engaged
-// expert at once and streams its rows with 16-byte loads.  "llama.cpp:
-// fusing shared experts into MMVQ" (ai-manual.ru), sections "What MMVQ is and
-// what CUDA has to do with it" (quantised weights are read once without being
-// expanded to full precision in memory) and "How fusing shared experts into
-// MMVQ can speed up inference" (shared experts in the same pass): the shared
-// experts are extra slots of the same grid, and Q4_0 blocks are expanded in
-// registers only.
-//
-// Three launches:
-//   gate/up:  grid (row tile of 16 intermediate rows, expert slot).  Slots are
-//             the active routed experts (compact list built by the router)
-//             followed by the shared experts.  The 4 waves of a work-group
-//             split the hidden dimension; partial sums meet in LDS.  The
-//             epilogue applies silu(g) * u and the routing weight and writes
-//             the activation rows in the format the down launch consumes.
-//   down:     grid (row tile of 16 hidden outputs, expert slot), the same
-//             shape as gate/up: the 4 waves split the slot's intermediate
-//             dimension and meet in LDS; the work-group writes the slot's
-//             routing-weighted output rows (one row per assignment) once.
-//   combine:  out[t] = the k assignment rows of token t (located through the
-//             dispatch's inverse permutation) plus its shared-expert rows,
-//             summed in a fixed order.  Deterministic, no atomics, and no
-//             device-wide fence (the kernel boundary orders the handoff).
-//
-// Matrix cores do the dot products: weights are the A operand (16 rows per
-// wave tile), tokens the B operand (16 per column tile).  bf16 weights use the
-// bf16 MFMA with fp32 activations split into hi + lo bf16 parts; Q4_0 weights
-// are dequantised in registers to fp16 and use the fp16 MFMA against fp16
-// activations; fp32 weights use the fp32 MFMA.
-#include "common.hpp"
+// Decode path: the multi-launch kernels (gate/up, down, combine) built from
+// the work items of decode_items.hpp.
+#include "decode_items.hpp"
 
 namespace moe {
 
-template <int WT> struct KPL;
-template <> struct KPL<DT_F32> { static constexpr int v = 4; };
-template <> struct KPL<DT_BF16> { static constexpr int v = 8; };
-template <> struct KPL<DT_Q4> { static constexpr int v = 32; };
-
-// Number of 4-lane-group steps along a reduction of length K.
-template <int WT>
-__host__ __device__ __forceinline__ int n_steps(int K) {
-  if constexpr (WT == DT_Q4) return (K / 32 + 3) / 4;
-  else return K / (4 * KPL<WT>::v);
-}
-
-// Row r of matrix `e` in a stack [n_mat, N, K].
-template <int WT>
-struct RowPtr {
-  const uint8_t* p;        // first byte of the row (nibbles for Q4_0)
-  const uint16_t* sc;      // Q4_0 scales of the row
-  __device__ __forceinline__ void init(const uint8_t* base, long n_mat, long N, long K, long e, long r) {
-    if constexpr (WT == DT_F32) p = base + (size_t(e) * N + r) * K * 4;
-    else if constexpr (WT == DT_BF16) p = base + (size_t(e) * N + r) * K * 2;
-    else {
-      p = base + (size_t(e) * N + r) * (K / 2);
-      sc = reinterpret_cast<const uint16_t*>(base + q4_scale_offset(n_mat, N, K)) + (size_t(e) * N + r) * (K / 32);
-    }
-  }
-};
-
-// A operand fragments of one step.
-template <int WT> struct AFrag;
-template <> struct AFrag<DT_F32> { u32x4_t v; };
-template <> struct AFrag<DT_BF16> { u32x4_t v; };
-template <> struct AFrag<DT_Q4> { u32x4_t raw; uint16_t d; };
-
-template <int WT>
-__device__ __forceinline__ AFrag<WT> load_a(const RowPtr<WT>& r, int s, int g, int K) {
-  AFrag<WT> f;
-  if constexpr (WT == DT_F32) f.v = ldg16(r.p + size_t(s * 16 + g * 4) * 4);
-  else if constexpr (WT == DT_BF16) f.v = ldg16(r.p + size_t(s * 32 + g * 8) * 2);
-  else {
-    const int nblk = K / 32;
-    int blk = 4 * s + g;
-    const bool ok = blk < nblk;
-    blk = ok ? blk : nblk - 1;
-    f.raw = ldg16(r.p + size_t(blk) * 16);
-    f.d = ok ? r.sc[blk] : uint16_t(0);
-  }
-  return f;
-}
-
-// -------------------------------------------------- B operand: activations --
-// x rows (gate/up) in fp32 or bf16; for each weight type the lane supplies the
-// k positions that its A fragment covers.
-
-template <int WT, int XT> struct XFrag;
-template <int XT> struct XFrag<DT_F32, XT> { float v[4]; };
-template <> struct XFrag<DT_BF16, DT_BF16> { u32x4_t v; };
-template <> struct XFrag<DT_BF16, DT_F32> { u32x4_t hi, lo; };
-template <int XT> struct XFrag<DT_Q4, XT> { u32x4_t v[4]; };
-
-// Raw activation words of one step, loaded with the step's weights and only
-// turned into MFMA operands (cook_x) when the step is computed, so that no
-// wait for them is placed where the loads are issued.
-template <int WT, int XT> struct XRaw;
-template <> struct XRaw<DT_F32, DT_F32> { u32x4_t t; };
-template <> struct XRaw<DT_F32, DT_BF16> { u32x2_t t; };
-template <> struct XRaw<DT_BF16, DT_BF16> { u32x4_t t; };
-template <> struct XRaw<DT_BF16, DT_F32> { u32x4_t t0, t1; };
-template <> struct XRaw<DT_Q4, DT_F32> { u32x4_t t[8]; };
-template <> struct XRaw<DT_Q4, DT_BF16> { u32x4_t t[4]; };
-
-template <int WT, int XT>
-__device__ __forceinline__ XRaw<WT, XT> load_x_raw(const uint8_t* xrow, int s, int g, int K) {
-  XRaw<WT, XT> r;
-  if constexpr (WT == DT_F32) {
-    const int k0 = s * 16 + g * 4;
-    if constexpr (XT == DT_F32) r.t = ldg16(xrow + size_t(k0) * 4);
-    else r.t = ldg8(xrow + size_t(k0) * 2);
-  } else if constexpr (WT == DT_BF16) {
-    const int k0 = s * 32 + g * 8;
-    if constexpr (XT == DT_BF16) {
-      r.t = ldg16(xrow + size_t(k0) * 2);
-    } else {
-      const float* xp = reinterpret_cast<const float*>(xrow) + k0;
-      r.t0 = ldg16(xp);
-      r.t1 = ldg16(xp + 4);
-    }
-  } else {
-    const int nblk = K / 32;
-    int blk = 4 * s + g;
-    blk = blk < nblk ? blk : nblk - 1;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int k0 = blk * 32 + f * 8;
-      if constexpr (XT == DT_F32) {
-        const float* xp = reinterpret_cast<const float*>(xrow) + k0;
-        r.t[2 * f] = ldg16(xp);
-        r.t[2 * f + 1] = ldg16(xp + 4);
-      } else {
-        r.t[f] = ldg16(xrow + size_t(k0) * 2);
-      }
-    }
-  }
-  return r;
-}
-
-template <int WT, int XT>
-__device__ __forceinline__ XFrag<WT, XT> cook_x(const XRaw<WT, XT>& r, bool ok, int s, int g, int K) {
-  XFrag<WT, XT> b;
-  if constexpr (WT == DT_F32) {
-    if constexpr (XT == DT_F32) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) b.v[m] = ok ? __uint_as_float(r.t[m]) : 0.f;
-    } else {
-      b.v[0] = ok ? bf16_lo(r.t[0]) : 0.f; b.v[1] = ok ? bf16_hi(r.t[0]) : 0.f;
-      b.v[2] = ok ? bf16_lo(r.t[1]) : 0.f; b.v[3] = ok ? bf16_hi(r.t[1]) : 0.f;
-    }
-  } else if constexpr (WT == DT_BF16) {
-    if constexpr (XT == DT_BF16) {
-      const u32x4_t z = {0, 0, 0, 0};
-      b.v = ok ? r.t : z;
-    } else {
-      float v[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v[m] = ok ? __uint_as_float(r.t0[m]) : 0.f;
-        v[m + 4] = ok ? __uint_as_float(r.t1[m]) : 0.f;
-      }
-      split_bf16x8(v, b.hi, b.lo);
-    }
-  } else {
-    ok = ok && (4 * s + g) < K / 32;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if constexpr (XT == DT_F32) {
-        const u32x4_t t0 = r.t[2 * f], t1 = r.t[2 * f + 1];
-        b.v[f][0] = pack_f16(__uint_as_float(t0[0]), __uint_as_float(t0[1]));
-        b.v[f][1] = pack_f16(__uint_as_float(t0[2]), __uint_as_float(t0[3]));
-        b.v[f][2] = pack_f16(__uint_as_float(t1[0]), __uint_as_float(t1[1]));
-        b.v[f][3] = pack_f16(__uint_as_float(t1[2]), __uint_as_float(t1[3]));
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) b.v[f][m] = bf16x2_to_f16x2(r.t[f][m]);
-      }
-      if (!ok) b.v[f] = u32x4_t{0, 0, 0, 0};
-    }
-  }
-  return b;
-}
-
-template <int WT, int XT>
-__device__ __forceinline__ f32x4_t mma(const AFrag<WT>& a, const XFrag<WT, XT>& b, f32x4_t c) {
-  if constexpr (WT == DT_F32) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) c = mfma_f32(__uint_as_float(a.v[m]), b.v[m], c);
-  } else if constexpr (WT == DT_BF16) {
-    if constexpr (XT == DT_BF16) c = mfma_bf16(a.v, b.v, c);
-    else {
-      c = mfma_bf16(a.v, b.hi, c);
-      c = mfma_bf16(a.v, b.lo, c);
-    }
-  } else {
-    u32x4_t fr[4];
-    q4_dequant_block(a.raw, a.d, fr);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) c = mfma_f16(fr[f], b.v[f], c);
-  }
-  return c;
-}
-
-// Q4_0 A fragments are dequantised once and used for every column tile.
-template <int WT>
-struct AReady { AFrag<WT> a; };
-template <>
-struct AReady<DT_Q4> { u32x4_t fr[4]; };
-
-template <int WT>
-__device__ __forceinline__ AReady<WT> prep_a(const AFrag<WT>& a) {
-  AReady<WT> r;
-  if constexpr (WT == DT_Q4) q4_dequant_block(a.raw, a.d, r.fr);
-  else r.a = a;
-  return r;
-}
-
-template <int WT, int XT>
-__device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT, XT>& b, f32x4_t c) {
-  if constexpr (WT == DT_Q4) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
-    return c;
-  } else {
-    return mma<WT, XT>(a.a, b, c);
-  }
-}
-
-// Unroll depth: keep several 16-byte weight loads in flight per lane.
-#ifndef MOE_GU_UNROLL_BF16
-#define MOE_GU_UNROLL_BF16 4
-#endif
-#ifndef MOE_DN_UNROLL_BF16
-#define MOE_DN_UNROLL_BF16 4
-#endif
-template <int WT, int NCT>
-struct Unroll {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 2 : 1);
-};
-template <int WT, int NCT>
-struct UnrollDown {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 1) : (NCT == 1 ? 2 : 1);
-};
-
-// Steps [s0, s1) in groups of U with the weight loads of group i+1 issued
-// before the MFMAs of group i, so the wave keeps weight bytes in flight
-// across group boundaries (a plain unrolled loop drains them at every group).
-// `load(s)` returns the A fragments of step s, `body(s, frag)` consumes them.
-// Masked B: lanes of token columns past the slot's count issue no activation
-// loads (their operand is zeroed anyway).  Pays off in gate/up, not in down.
-#ifndef MOE_GU_MASKED_B
-#define MOE_GU_MASKED_B 1
-#endif
-#ifndef MOE_DN_MASKED_B
-#define MOE_DN_MASKED_B 0
-#endif
-#ifndef MOE_DECODE_PIPELINE
-#define MOE_DECODE_PIPELINE 1
-#endif
-template <int U, class Load, class Body>
-__device__ __forceinline__ void stream_steps(int s0, int s1, Load load, Body body) {
-  using F = decltype(load(0));
-  int s = s0;
-  if (!MOE_DECODE_PIPELINE) {
-    for (; s + U <= s1; s += U) {
-      F cur[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = load(s + u);
-#pragma unroll
-      for (int u = 0; u < U; ++u) body(s + u, cur[u]);
-    }
-    for (; s < s1; ++s) body(s, load(s));
-    return;
-  }
-  if (s + U <= s1) {
-    F cur[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = load(s + u);
-    for (; s + 2 * U <= s1; s += U) {
-      F nxt[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) nxt[u] = load(s + U + u);
-#pragma unroll
-      for (int u = 0; u < U; ++u) body(s + u, cur[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) body(s + u, cur[u]);
-    s += U;
-  }
-  for (; s < s1; ++s) body(s, load(s));
-}
-
-template <int WT, int XT, int NCT>
-struct GUStep { AFrag<WT> g, u; XRaw<WT, XT> x[NCT]; };
-
-
-// ------------------------------------------------------------- gate/up --
+// ------------------------------------------------------------- kernels --
 
 template <int WT, int XT, int NCT>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = blockIdx.x, slot = blockIdx.y;
-  const bool routed = slot < a.n_routed_slots;
-  int e, n_e, hrow0, N, seg = 0;
-  long n_mat;
-  const uint8_t *bg, *bu;
-  if (routed) {
-    if (slot >= a.active[0]) return;
-    e = a.active[1 + slot];
-    n_e = a.counts[e];
-    seg = a.offsets[e];
-    hrow0 = a.cprefix[e];
-    N = a.I; bg = a.wg; bu = a.wu; n_mat = a.E;
-  } else {
-    e = slot - a.n_routed_slots;
-    n_e = a.T;
-    hrow0 = a.T * a.k + e * a.T;
-    N = a.Is; bg = a.sg; bu = a.su; n_mat = a.S;
-  }
-  if (rt * 16 >= N) return;
-  const int K = a.H, g = lane >> 4;
-  RowPtr<WT> rg, ru;
-  rg.init(bg, n_mat, N, K, e, rt * 16 + (lane & 15));
-  ru.init(bu, n_mat, N, K, e, rt * 16 + (lane & 15));
-
-  constexpr int xb = XT == DT_F32 ? 4 : 2;
-  const uint8_t* xrow[NCT];
-  bool xok[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
-    xok[ct] = c < n_e;
-    int tok = 0;
-    if (xok[ct]) tok = routed ? a.sorted_ids[seg + c] / a.k : c;
-    xrow[ct] = reinterpret_cast<const uint8_t*>(a.x) + size_t(tok) * K * xb;
-  }
-  const int nct = (n_e + 15) >> 4;
-
-  const int nsteps = n_steps<WT>(K);
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
-  f32x4_t accg[NCT], accu[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) accg[ct] = accu[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int U = Unroll<WT, NCT>::v;
-  auto load = [&](int s) {
-    GUStep<WT, XT, NCT> st;
-    st.g = load_a<WT>(rg, s, g, K);
-    st.u = load_a<WT>(ru, s, g, K);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      if (NCT == 1 || ct < nct) {
-        if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<WT, XT>(xrow[ct], s, g, K);
-      }
-    return st;
-  };
-  auto body = [&](int s, const GUStep<WT, XT, NCT>& st) {
-    const AReady<WT> ag = prep_a<WT>(st.g), au = prep_a<WT>(st.u);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if (NCT == 1 || ct < nct) {
-        const XFrag<WT, XT> b = cook_x<WT, XT>(st.x[ct], xok[ct], s, g, K);
-        accg[ct] = mma_ready<WT, XT>(ag, b, accg[ct]);
-        accu[ct] = mma_ready<WT, XT>(au, b, accu[ct]);
-      }
-    }
-  };
-  stream_steps<U>(s0, s1, load, body);
-
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    red[wave][ct][lane] = accg[ct];
-    red[wave][NCT + ct][lane] = accu[ct];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if (!(NCT == 1 || ct < nct)) continue;
-    f32x4_t gs = red[0][ct][lane], us = red[0][NCT + ct][lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      gs += red[w][ct][lane];
-      us += red[w][NCT + ct][lane];
-    }
-    const int c = ct * 16 + (lane & 15);
-    if (c >= n_e) continue;
-    const float wr = routed ? a.topk_w[a.sorted_ids[seg + c]] : 1.0f;
-    float hv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = silu_f(gs[i]) * us[i] * wr;
-    const size_t off = size_t(hrow0 + c) * a.h_stride + rt * 16 + (lane >> 4) * 4;
-    if constexpr (WT == DT_F32) {
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.h) + off) = f32x4_t{hv[0], hv[1], hv[2], hv[3]};
-    } else if constexpr (WT == DT_BF16) {
-      uint32_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]), h2 = f32_to_bf16(hv[2]), h3 = f32_to_bf16(hv[3]);
-      float r0 = hv[0] - __uint_as_float(h0 << 16), r1 = hv[1] - __uint_as_float(h1 << 16);
-      float r2 = hv[2] - __uint_as_float(h2 << 16), r3 = hv[3] - __uint_as_float(h3 << 16);
-      uint16_t* hp = reinterpret_cast<uint16_t*>(a.h);
-      *reinterpret_cast<u32x2_t*>(hp + off) = u32x2_t{h0 | (h1 << 16), h2 | (h3 << 16)};
-      *reinterpret_cast<u32x2_t*>(hp + a.h_plane + off) = u32x2_t{pack_bf16(r0, r1), pack_bf16(r2, r3)};
-    } else {
-      uint16_t* hp = reinterpret_cast<uint16_t*>(a.h);
-      *reinterpret_cast<u32x2_t*>(hp + off) = u32x2_t{pack_f16(hv[0], hv[1]), pack_f16(hv[2], hv[3])};
-    }
-  }
+  gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
 }
 
-// ---------------------------------------------------------------- down --
-
-// B operand of the down projection: activation rows written by gate/up.
-template <int WT> struct HFrag;
-template <> struct HFrag<DT_F32> { float v[4]; };
-template <> struct HFrag<DT_BF16> { u32x4_t hi, lo; };
-template <> struct HFrag<DT_Q4> { u32x4_t v[4]; };
-
-template <int WT>
-__device__ __forceinline__ HFrag<WT> load_h_raw(const DecodeArgs& a, size_t row_off, int s, int g, int K) {
-  HFrag<WT> b;
-  if constexpr (WT == DT_F32) {
-    const u32x4_t t = ldg16(reinterpret_cast<const float*>(a.h) + row_off + s * 16 + g * 4);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) b.v[m] = __uint_as_float(t[m]);
-  } else if constexpr (WT == DT_BF16) {
-    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + s * 32 + g * 8;
-    b.hi = ldg16(hp);
-    b.lo = ldg16(hp + a.h_plane);
-  } else {
-    const int nblk = K / 32;
-    int blk = 4 * s + g;
-    blk = blk < nblk ? blk : nblk - 1;
-    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + blk * 32;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) b.v[f] = ldg16(hp + f * 8);
-  }
-  return b;
-}
-
-template <int WT>
-__device__ __forceinline__ HFrag<WT> cook_h(HFrag<WT> b, bool ok, int s, int g, int K) {
-  const u32x4_t z = {0, 0, 0, 0};
-  if constexpr (WT == DT_F32) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) b.v[m] = ok ? b.v[m] : 0.f;
-  } else if constexpr (WT == DT_BF16) {
-    b.hi = ok ? b.hi : z;
-    b.lo = ok ? b.lo : z;
-  } else {
-    ok = ok && (4 * s + g) < K / 32;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) b.v[f] = ok ? b.v[f] : z;
-  }
-  return b;
-}
-
-template <int WT>
-__device__ __forceinline__ f32x4_t mma_h(const AReady<WT>& a, const HFrag<WT>& b, f32x4_t c) {
-  if constexpr (WT == DT_F32) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) c = mfma_f32(__uint_as_float(a.a.v[m]), b.v[m], c);
-  } else if constexpr (WT == DT_BF16) {
-    c = mfma_bf16(a.a.v, b.hi, c);
-    c = mfma_bf16(a.a.v, b.lo, c);
-  } else {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
-  }
-  return c;
-}
-
-template <int WT, int NCT>
-struct DNStep { AFrag<WT> a; HFrag<WT> h[NCT]; };
-
-// One work-group: 16 hidden outputs (rows of the down projection) of one
-// expert slot, for every token of that slot.  Its 4 waves split the slot's
-// intermediate dimension; partial sums meet in LDS.  The result rows are the
-// routing-weighted expert outputs; they go to `partials` at the same row the
-// activations use (one row per routed assignment, then the shared tokens).
 template <int WT, int NCT>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][NCT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = blockIdx.x, slot = blockIdx.y;
-  const bool routed = slot < a.n_routed_slots;
-  int e, n_e, hrow0, K;
-  long n_mat;
-  const uint8_t* base;
-  if (routed) {
-    if (slot >= a.active[0]) return;
-    e = a.active[1 + slot];
-    n_e = a.counts[e];
-    hrow0 = a.cprefix[e];
-    K = a.I; base = a.wd; n_mat = a.E;
-  } else {
-    e = slot - a.n_routed_slots;
-    n_e = a.T;
-    hrow0 = a.T * a.k + e * a.T;
-    K = a.Is; base = a.sd; n_mat = a.S;
-  }
-  const int H = a.H, g = lane >> 4;
-  RowPtr<WT> rw;
-  rw.init(base, n_mat, H, K, e, rt * 16 + (lane & 15));
-  size_t hoff[NCT];
-  bool hok[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
-    hok[ct] = c < n_e;
-    hoff[ct] = size_t(hrow0 + (hok[ct] ? c : 0)) * a.h_stride;
-  }
-  const int nct = (n_e + 15) >> 4;
-  const int nsteps = n_steps<WT>(K);
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
-  f32x4_t acc[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int U = UnrollDown<WT, NCT>::v;
-  auto load = [&](int s) {
-    DNStep<WT, NCT> st;
-    st.a = load_a<WT>(rw, s, g, K);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      if (NCT == 1 || ct < nct) {
-        if (!MOE_DN_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<WT>(a, hoff[ct], s, g, K);
-      }
-    return st;
-  };
-  auto body = [&](int s, const DNStep<WT, NCT>& st) {
-    const AReady<WT> ar = prep_a<WT>(st.a);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if (NCT == 1 || ct < nct) acc[ct] = mma_h<WT>(ar, cook_h<WT>(st.h[ct], hok[ct], s, g, K), acc[ct]);
-    }
-  };
-  stream_steps<U>(s0, s1, load, body);
-
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) red[wave][ct][lane] = acc[ct];
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if (!(NCT == 1 || ct < nct)) continue;
-    f32x4_t v = red[0][ct][lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[w][ct][lane];
-    const int c = ct * 16 + (lane & 15);
-    if (c >= n_e) continue;
-    // lane holds rows 4*(lane/16) + 0..3 of this tile for token column c
-    *reinterpret_cast<f32x4_t*>(a.partials + size_t(hrow0 + c) * H + rt * 16 + (lane >> 4) * 4) = v;
-  }
+  down_item<WT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
 }
 
-// out[t] = sum over j of the partial row of assignment t*k + j (found through
-// inv), then the shared experts' rows, in that fixed order; 4 outputs per thread.
 template <int OT>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
-  const int H4 = a.H / 4;
-  const long i4 = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i4 >= long(a.T) * H4) return;
-  const int t = int(i4 / H4), h4 = int(i4 % H4);
-  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(a.partials);
-  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) v += p[size_t(a.inv[t * a.k + j]) * H4 + h4];
-  for (int s = 0; s < a.S; ++s) v += p[size_t(a.T * a.k + s * a.T + t) * H4 + h4];
-  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
-  else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  combine_item<OT, false>(a, long(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 
 // -------------------------------------------------------------- launch --

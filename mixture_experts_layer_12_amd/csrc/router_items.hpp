@@ -1,0 +1,570 @@
+// Router: logits GEMV/GEMM on MFMA, then (in the last work-group to finish)
+// softmax, top-k with renormalisation and the dispatch into expert-sorted
+// order.
+//
+// Sources: "Fused MoE kernel on Triton: 5 launches vs 24" (ai-manual.ru),
+// section "Fused kernel: one operation instead of twenty-four": routing
+// (top-k weights) and dispatch each take one launch in the fused design; here
+// both sit in one launch.  "Why MoE on RTX 5090 falls short: a bandwidth
+// measurement" (news.malakhovai.ru), paragraph on the kernel-time split:
+// top-k plus row gathering are a small share of decode time, so this kernel
+// favours few launches and full-chip parallelism for the logits read over
+// cleverness in the top-k.
+//
+// Logits: rows = experts (A operand, router weights), columns = tokens
+// (B operand, x).  One work-group owns a 16-expert x 16-token tile; its waves
+// split H and reduce through LDS.  Accumulation is fp32: bf16 x bf16 products
+// are exact in fp32; fp32 activations against bf16 weights are split into a
+// bf16 hi + lo pair (two MFMAs); fp32 x fp32 uses the fp32 MFMA.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kRouterIdsLds = 8192;    // flat ids kept in LDS for the dispatch (32 KiB)
+constexpr int kRouterStage = 8192;     // logits staged in LDS per chunk of tokens (32 KiB)
+
+// ------------------------------------------------------------- logits ----
+
+// The reduction over H is cut into kLogitChunks chunks of steps, each with its
+// own accumulator, and the chunk sums are added in one fixed order (groups of
+// four chunks left to right, then the groups left to right, then the bias),
+// whatever the number of waves or work-groups that computed them: the
+// multi-launch and the single-launch paths produce the same bits.
+constexpr int kLogitChunks = 16;
+
+template <int RT>
+__host__ __device__ __forceinline__ int logit_steps(int H) { return RT == DT_F32 ? H / 16 : H / 32; }
+
+// Accumulators of chunks c0 .. c0+CPW-1 of the 16-expert x 16-token tile;
+// each batch issues 8 loads of A (and of B) per lane across the CPW chunks.
+template <int RT, int XT, int CPW>
+__device__ __forceinline__ void router_dot(const RouterArgs a, int rtile, int ctile, int c0, int lane, f32x4_t* acc) {
+  // fp32 activations against bf16 router rows hold 8 floats per step: half the batch
+  constexpr int U = (RT == DT_BF16 && XT == DT_F32) ? (CPW >= 4 ? 1 : 4 / CPW) : 8 / CPW;
+  const int H = a.H, nsteps = logit_steps<RT>(H);
+  const int row = rtile * 16 + (lane & 15);
+  const int tok = ctile * 16 + (lane & 15);
+  const int g = lane >> 4;
+  const bool arow = row < a.E;
+  const bool btok = tok < a.T;
+  int s0[CPW], s1[CPW], len = 0;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    s0[j] = (c0 + j) * nsteps / kLogitChunks;
+    s1[j] = (c0 + j + 1) * nsteps / kLogitChunks;
+    len = max(len, s1[j] - s0[j]);
+    acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sb = 0; sb < len; sb += U) {
+    if constexpr (RT == DT_F32) {
+      // 16x16x4 fp32 MFMA; one 16-byte load = 4 k values; a step covers 16 k.
+      const float* wrow = reinterpret_cast<const float*>(a.wr) + size_t(row) * H;
+      u32x4_t av[CPW][U];
+      float bv[CPW][U][4];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int s = s0[j] + sb + u;
+          const int k0 = s * 16 + g * 4;
+          const bool in = s < s1[j];
+          av[j][u] = (arow && in) ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) bv[j][u][m] = 0.f;
+          if (btok && in) {
+            if constexpr (XT == DT_F32) {
+              const u32x4_t t = ldg16(reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0);
+#pragma unroll
+              for (int m = 0; m < 4; ++m) bv[j][u][m] = __uint_as_float(t[m]);
+            } else {
+              const u32x2_t t = ldg8(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0);
+              bv[j][u][0] = bf16_lo(t[0]); bv[j][u][1] = bf16_hi(t[0]);
+              bv[j][u][2] = bf16_lo(t[1]); bv[j][u][3] = bf16_hi(t[1]);
+            }
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[j] = mfma_f32(__uint_as_float(av[j][u][m]), bv[j][u][m], acc[j]);
+    } else {
+      // 16x16x32 bf16 MFMA; one 16-byte load = 8 k values; a step covers 32 k.
+      const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.wr) + size_t(row) * H;
+      u32x4_t av[CPW][U], bx[CPW][U];
+      float v[CPW][U][8];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int s = s0[j] + sb + u;
+          const int k0 = s * 32 + g * 8;
+          const bool in = s < s1[j];
+          av[j][u] = (arow && in) ? ldg16(wrow + k0) : u32x4_t{0, 0, 0, 0};
+          if constexpr (XT == DT_BF16) {
+            bx[j][u] = (btok && in) ? ldg16(reinterpret_cast<const uint16_t*>(a.x) + size_t(tok) * H + k0)
+                                    : u32x4_t{0, 0, 0, 0};
+          } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) v[j][u][m] = 0.f;
+            if (btok && in) {
+              const float* xp = reinterpret_cast<const float*>(a.x) + size_t(tok) * H + k0;
+              const u32x4_t t0 = ldg16(xp), t1 = ldg16(xp + 4);
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                v[j][u][m] = __uint_as_float(t0[m]);
+                v[j][u][m + 4] = __uint_as_float(t1[m]);
+              }
+            }
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (XT == DT_BF16) {
+            acc[j] = mfma_bf16(av[j][u], bx[j][u], acc[j]);
+          } else {
+            u32x4_t hi, lo;
+            split_bf16x8(v[j][u], hi, lo);
+            acc[j] = mfma_bf16(av[j][u], hi, acc[j]);
+            acc[j] = mfma_bf16(av[j][u], lo, acc[j]);
+          }
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------- top-k -----
+
+// Candidate order: larger logit first; equal logits -> lower expert index.
+// NaN logits are treated as -inf so every selected index is a real expert.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ float sanitize(float v) { return v != v ? -__builtin_inff() : v; }
+
+// One thread selects the top-k of one token (E <= EMAX <= 32, k <= 8).  Logits,
+// selections and weights stay in registers (loops fully unrolled and
+// predicated); ids and weights are written once.  `ids_lds` (or null)
+// receives a copy of the ids for the dispatch.
+template <int EMAX, bool COH>
+__device__ __forceinline__ void topk_thread(const float* l, int E, int k, int32_t* ids, float* w, int32_t* ids_lds) {
+  constexpr int KMAX = 8;
+  float lv[EMAX], zv[KMAX];
+  int iv[KMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) lv[e] = e < E ? sanitize(l[e]) : -__builtin_inff();
+  uint32_t taken = 0;
+  float lmax = 0.f, denom = 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    zv[j] = 0.f;
+    iv[j] = 0;
+    if (j < k) {
+      int bi = 0x7fffffff;
+      float bv = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E && !(taken & (1u << e)) && better(lv[e], e, bv, bi)) { bv = lv[e]; bi = e; }
+      }
+      taken |= 1u << bi;
+      if (j == 0) lmax = bv;
+      // weights: softmax over the selected logits (the full-softmax denominator cancels)
+      const float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+      zv[j] = z;
+      iv[j] = bi;
+      denom += z;
+    }
+  }
+  const float r = denom > 0.f ? 1.0f / denom : 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      st_i32<COH>(ids + j, iv[j]);
+      if (ids_lds) ids_lds[j] = iv[j];
+      st_f32<COH>(w + j, denom > 0.f ? zv[j] * r : 1.0f / float(k));   // all selected logits -inf/NaN: equal weights
+    }
+  }
+}
+
+// (value, index) maximum over the 16 lanes of a DPP row: rotations by 8, 4, 2
+// and 1 lanes leave every lane of the row holding the row's best candidate.
+template <int ROT>
+__device__ __forceinline__ void dpp_row_best(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), 0x120 + ROT, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, 0x120 + ROT, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+
+// One wave selects the top-k of one token (any E <= 256, k <= E).  Each
+// round takes the best remaining candidate of every lane (4 per lane), the
+// best of every 16-lane row with DPP rotations, and the best of the 4 rows
+// with lane reads.  Selection j is kept by lane j % 64 (slot j / 64) and
+// written once at the end.
+template <bool COH>
+__device__ __forceinline__ void topk_wave(const float* l, int E, int k, int32_t* ids, float* w, int32_t* ids_lds, int lane) {
+  float v[4], zk[4];
+  bool taken[4];
+  int ik[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + 64 * m;
+    v[m] = e < E ? sanitize(l[e]) : -__builtin_inff();
+    taken[m] = e >= E;
+    zk[m] = 0.f;
+    ik[m] = 0;
+  }
+  float lmax = 0.f, denom = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane + 64 * m;
+      if (!taken[m] && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
+    }
+    dpp_row_best<8>(bv, bi);
+    dpp_row_best<4>(bv, bi);
+    dpp_row_best<2>(bv, bi);
+    dpp_row_best<1>(bv, bi);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+      const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
+      const int oi = __builtin_amdgcn_readlane(bi, r);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    // every lane of row 0 now holds the wave's best; broadcast it
+    bv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
+    bi = __builtin_amdgcn_readfirstlane(bi);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (lane + 64 * m == bi) taken[m] = true;
+    if (j == 0) lmax = bv;
+    const float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+    denom += z;
+    if (lane == (j & 63)) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if ((j >> 6) == m) { zk[m] = z; ik[m] = bi; }
+    }
+  }
+  const float r = denom > 0.f ? 1.0f / denom : 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = lane + 64 * m;
+    if (j < k) {
+      st_i32<COH>(ids + j, ik[m]);
+      if (ids_lds) ids_lds[j] = ik[m];
+      st_f32<COH>(w + j, denom > 0.f ? zk[m] * r : 1.0f / float(k));
+    }
+  }
+}
+
+// One 16-lane DPP row selects the top-k of one token (E <= 64, k <= 16), so a
+// wave serves 4 tokens at once: lane r of the row holds experts r, r+16, r+32
+// and r+48, rotations within the row find each round's best, and selection j
+// is kept by lane j of the row.  A row with `valid` false still takes part
+// (its lanes hold -inf) and writes nothing.
+template <bool COH>
+__device__ __forceinline__ void topk_row16(const float* l, int E, int k, bool valid, int32_t* ids, float* w, int32_t* ids_lds,
+                           int r) {
+  float v[4];
+  bool taken[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = r + 16 * m;
+    v[m] = (valid && e < E) ? sanitize(l[e]) : -__builtin_inff();
+    taken[m] = e >= E;
+  }
+  float lmax = 0.f, denom = 0.f, zk = 0.f;
+  int ik = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = r + 16 * m;
+      if (!taken[m] && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
+    }
+    dpp_row_best<8>(bv, bi);
+    dpp_row_best<4>(bv, bi);
+    dpp_row_best<2>(bv, bi);
+    dpp_row_best<1>(bv, bi);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (r + 16 * m == bi) taken[m] = true;
+    if (j == 0) lmax = bv;
+    const float z = (bv == -__builtin_inff()) ? 0.f : __expf(bv - lmax);
+    denom += z;
+    if (r == j) { zk = z; ik = bi; }
+  }
+  if (valid && r < k) {
+    st_i32<COH>(ids + r, ik);
+    if (ids_lds) ids_lds[r] = ik;
+    st_f32<COH>(w + r, denom > 0.f ? zk * (1.0f / denom) : 1.0f / float(k));
+  }
+}
+
+// ------------------------------------------------------------ dispatch ---
+
+// Lanes of the wave whose (valid) expert id equals this lane's: 8 ballots, one
+// per bit of the id (E <= 256).
+__device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// Expert-sorted order, built by one work-group.  Deterministic: the rank of an
+// assignment inside its expert's segment is the number of smaller flat ids
+// routed to the same expert (stable counting sort); no atomics decide order.
+template <bool COH>
+__device__ __forceinline__ void dispatch_wg(const RouterArgs a, int* lds, const int32_t* ids) {
+  const RouteBufs& rb = a.rb;
+  const int E = a.E, n = a.T * a.k, M = a.tile_m;
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, wave = tid >> 6, NW = NT >> 6;
+  int* hist = lds;                 // [NW][E]: per-wave counts, then per-wave rank bases
+  int* cnt = hist + NW * E;        // [E]
+  int* off = cnt + E;              // [E+1]
+
+  for (int i = tid; i < NW * E; i += NT) hist[i] = 0;
+  __syncthreads();
+  const int chunk = (n + NW - 1) / NW;
+  const int f0 = min(n, wave * chunk), f1 = min(n, f0 + chunk);
+  // per-wave counts without atomics: the first lane of each group of equal ids adds the group size
+  for (int c0 = f0; c0 < f1; c0 += 64) {
+    const int f = c0 + lane;
+    const bool valid = f < f1;
+    const int e = valid ? ids[f] : 0;
+    const uint64_t m = same_expert_mask(e, valid);
+    if (valid && (m & ((1ull << lane) - 1ull)) == 0) hist[wave * E + e] += __popcll(m);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int s = 0;
+    for (int w = 0; w < NW; ++w) {
+      int c = hist[w * E + e];
+      hist[w * E + e] = s;
+      s += c;
+    }
+    cnt[e] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scans over experts (padded offsets, unpadded prefix) and the
+    // compact active list; experts 4*lane .. 4*lane+3 belong to this lane
+    int c[4], pad[4], act = 0, sp = 0, sc = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane * 4 + m;
+      c[m] = e < E ? cnt[e] : 0;
+      pad[m] = (c[m] + M - 1) / M * M;
+      sp += pad[m];
+      sc += c[m];
+      act += c[m] > 0;
+    }
+    int ip = sp, ic = sc, ia = act;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int up = __shfl_up(ip, d), uc = __shfl_up(ic, d), ua = __shfl_up(ia, d);
+      if (lane >= d) { ip += up; ic += uc; ia += ua; }
+    }
+    int bp = ip - sp, bc = ic - sc, ba = ia - act;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = lane * 4 + m;
+      if (e < E) {
+        off[e] = bp;
+        st_i32<COH>(rb.offsets + e, bp);
+        st_i32<COH>(rb.cprefix + e, bc);
+        st_i32<COH>(rb.counts + e, c[m]);
+        if (c[m] > 0) st_i32<COH>(rb.active + 1 + ba++, e);
+      }
+      bp += pad[m];
+      bc += c[m];
+    }
+    if (lane == 63) {
+      off[E] = ip;
+      st_i32<COH>(rb.offsets + E, ip);
+      st_i32<COH>(rb.cprefix + E, ic);
+      st_i32<COH>(rb.active, ia);
+    }
+  }
+  __syncthreads();
+  for (int c0 = f0; c0 < f1; c0 += 64) {
+    const int f = c0 + lane;
+    const bool valid = f < f1;
+    const int e = valid ? ids[f] : 0;
+    const uint64_t m = same_expert_mask(e, valid);
+    int base = 0;
+    if (valid) base = hist[wave * E + e];
+    if (valid) {
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));
+      const int pos = off[e] + base + rank;
+      st_i32<COH>(rb.sorted_ids + pos, f);
+      st_i32<COH>(rb.inv + f, pos);
+    }
+    if (valid && (m >> lane) == 1ull) hist[wave * E + e] = base + __popcll(m);
+  }
+  __syncthreads();
+  for (int e = wave; e < E; e += NW)
+    for (int p = off[e] + cnt[e] + lane; p < off[e + 1]; p += 64) st_i32<COH>(rb.sorted_ids + p, n);
+  for (int p = off[E] + tid; p < a.capacity; p += NT) st_i32<COH>(rb.sorted_ids + p, n);
+  const int n_tiles = rb.tile_expert ? a.capacity / M : 0;   // the decode path reads no tile table
+  for (int i = tid; i < n_tiles; i += NT) {
+    const int r = i * M;
+    int e = -1;
+    if (r < off[E]) {
+      int lo = 0, hi = E;          // largest e with off[e] <= r
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+      }
+      e = lo;
+    }
+    st_i32<COH>(rb.tile_expert + i, e);
+  }
+}
+
+// --------------------------------------------------------------- kernel --
+
+// One 16-expert x 16-token logits tile: the waves split H, partial sums meet
+// in LDS, wave 0 adds the bias and stores to `dst` ([T, E], row stride E).
+// Logits of one 16-expert x 16-token tile from chunks [cb, cb + n) with n =
+// 4 * (number of groups): each wave computes n / NW chunks into `red` (LDS,
+// n x 64 x 4 floats), then wave 0 adds them in the fixed order.  final: n is
+// all 16 chunks, the bias is added and dst is the [T, E] logits; otherwise
+// the group sum goes to dst as one partial [T, E] plane (bias added by the
+// reader, after the planes, in the same order).
+template <int RT, int XT, bool COH>
+__device__ __forceinline__ void logits_tile(const RouterArgs a, int rtile, int ctile, int cb, int n, float* red,
+                                            float* dst) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
+  const int cpw = n / NW, c0 = cb + wave * cpw;
+  f32x4_t acc[4];
+  if (cpw == 1) router_dot<RT, XT, 1>(a, rtile, ctile, c0, lane, acc);
+  else if (cpw == 2) router_dot<RT, XT, 2>(a, rtile, ctile, c0, lane, acc);
+  else router_dot<RT, XT, 4>(a, rtile, ctile, c0, lane, acc);
+  for (int j = 0; j < cpw; ++j) *reinterpret_cast<f32x4_t*>(red + ((wave * cpw + j) * 64 + lane) * 4) = acc[j];
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < n / 4; ++q) {
+      f32x4_t gsum = *reinterpret_cast<f32x4_t*>(red + (4 * q * 64 + lane) * 4);
+      for (int c = 1; c < 4; ++c) gsum += *reinterpret_cast<f32x4_t*>(red + ((4 * q + c) * 64 + lane) * 4);
+      s = q == 0 ? gsum : s + gsum;
+    }
+    const bool final = n == kLogitChunks;
+    const int tok = ctile * 16 + (lane & 15);
+    if (tok < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = rtile * 16 + (lane >> 4) * 4 + i;
+        if (e < a.E) st_f32<COH>(dst + size_t(tok) * a.E + e, final ? s[i] + (a.bias ? a.bias[e] : 0.f) : s[i]);
+      }
+    }
+  }
+}
+
+// LDS of the selection and dispatch, in ints: dispatch scratch, then the flat
+// ids (when T*k fits), then the logits staging area (select kernel only).
+__host__ __device__ inline int router_disp_ints(int NW, int E) { return NW * E + 2 * E + 1; }
+
+// Top-k of tokens [t0, t0 + nt) whose logit rows start at `l` (row stride E,
+// LDS): a thread per token (E <= 32, k <= 8), a 16-lane row per token
+// (E <= 64, k <= 16), else a wave per token.
+template <bool COH>
+__device__ __forceinline__ void topk_chunk(const RouterArgs a, const float* l, int t0, int nt, int32_t* ids_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NT = blockDim.x, NW = NT >> 6;
+  const int E = a.E, k = a.k;
+  if (E <= 32 && k <= 8) {
+    for (int i = tid; i < nt; i += NT) {
+      const size_t t = size_t(t0 + i);
+      const float* lt = l + size_t(i) * E;
+      int32_t* it = a.rb.topk_ids + t * k;
+      float* wt = a.rb.topk_w + t * k;
+      int32_t* il = ids_lds ? ids_lds + t * k : nullptr;
+      if (E <= 8) topk_thread<8, COH>(lt, E, k, it, wt, il);
+      else if (E <= 16) topk_thread<16, COH>(lt, E, k, it, wt, il);
+      else topk_thread<32, COH>(lt, E, k, it, wt, il);
+    }
+  } else if (E <= 64 && k <= 16) {
+    for (int i0 = wave * 4; i0 < nt; i0 += NW * 4) {        // wave-uniform loop
+      const int i = i0 + (lane >> 4);
+      const bool valid = i < nt;
+      const int ic = valid ? i : 0;
+      const size_t t = size_t(t0 + ic);
+      topk_row16<COH>(l + size_t(ic) * E, E, k, valid, a.rb.topk_ids + t * k, a.rb.topk_w + t * k,
+                 ids_lds ? ids_lds + t * k : nullptr, lane & 15);
+    }
+  } else {
+    for (int i = wave; i < nt; i += NW) {
+      const size_t t = size_t(t0 + i);
+      topk_wave<COH>(l + size_t(i) * E, E, k, a.rb.topk_ids + t * k, a.rb.topk_w + t * k,
+                ids_lds ? ids_lds + t * k : nullptr, lane);
+    }
+  }
+}
+
+// Top-k of every token, then the dispatch; one work-group.  Logits in global
+// memory are staged into LDS a chunk of tokens at a time with every load of a
+// chunk issued before the first store, so the selection waits on memory once
+// per chunk rather than once per token.
+template <bool COH>
+__device__ __forceinline__ void select_and_dispatch(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
+  const int tid = threadIdx.x, NT = blockDim.x, NW = NT >> 6;
+  const int T = a.T, E = a.E, n = T * a.k;
+  const bool ids_fit = n <= kRouterIdsLds;
+  int* ids_lds = ids_fit ? lds + router_disp_ints(NW, E) : nullptr;
+  if (l_in_lds) {
+    topk_chunk<COH>(a, l, 0, T, ids_lds);
+  } else {
+    float* stage = reinterpret_cast<float*>(lds + router_disp_ints(NW, E) + (ids_fit ? n : 0));
+    const int ch = max(1, kRouterStage / E);
+    for (int t0 = 0; t0 < T; t0 += ch) {
+      const int cnt = min(ch, T - t0) * E;
+      const float* src = l + size_t(t0) * E;
+      const size_t plane = size_t(T) * E;
+      for (int b = 0; b < cnt; b += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = b + u * NT + tid;
+          if (a.logit_parts == 1) {
+            v[u] = idx < cnt ? ld_f32<COH>(src + idx) : 0.f;
+          } else {      // group planes of the single-launch path, then the bias
+            float acc = 0.f;
+            if (idx < cnt) {
+              acc = ld_f32<COH>(src + idx);
+              for (int q = 1; q < a.logit_parts; ++q) acc += ld_f32<COH>(src + q * plane + idx);
+              acc += a.bias ? a.bias[idx % E] : 0.f;
+            }
+            v[u] = acc;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = b + u * NT + tid;
+          if (idx < cnt) stage[idx] = v[u];
+        }
+      }
+      __syncthreads();
+      topk_chunk<COH>(a, stage, t0, min(ch, T - t0), ids_lds);
+      __syncthreads();
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+  dispatch_wg<COH>(a, lds, ids_lds ? ids_lds : a.rb.topk_ids);
+}
+
+}  // namespace moe

@@ -54,7 +54,9 @@ def test_strerror(m):
     (dict(router_dtype=7), "MOE_ERR_DTYPE"),
     (dict(w_dtype=5), "MOE_ERR_DTYPE"),
     (dict(w_dtype=2, path=2), "MOE_ERR_DTYPE"),  # prefill needs bf16 experts
-    (dict(path=3), "MOE_ERR_SHAPE"),
+    (dict(path=4), "MOE_ERR_SHAPE"),
+    (dict(path=3, router_dtype=0), "MOE_ERR_DTYPE"),   # single-launch decode: router dtype == x dtype
+    (dict(path=3, E=32, top_k=17), "MOE_ERR_SHAPE"),    # single-launch decode: top_k <= 16
 ])
 def test_shape_validation(m, kw, code):
     base = dict(T=8, H=256, E=8, I=128, top_k=2, n_shared=0, I_shared=0, x_dtype=1, w_dtype=1,
@@ -63,6 +65,17 @@ def test_shape_validation(m, kw, code):
     s = m.moe_shape_t(*[base[n] for n, _ in m.moe_shape_t._fields_])
     n = ctypes.c_size_t(0)
     assert m.load_library().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == getattr(m, code)
+
+
+def test_single_launch_decode_workspace(m):
+    """The single-launch decode adds completion flags to the decode workspace;
+    the multi-launch decode of the same shape needs less."""
+    fused = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE_FUSED))
+    multi = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE))
+    auto = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2))
+    # work list: 1 logits tile, 1 selection, 8 x 896 gate/up tiles, 8 x 256 down tiles, 32 combine blocks
+    n_items = 1 + 1 + 8 * 896 + 8 * 256 + 32
+    assert fused - multi >= n_items * 8 and auto == fused
 
 
 def test_workspace_size_and_dims(m):
