@@ -123,7 +123,8 @@ def layer_flops(wl):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("common.hpp", "decode.hip", "prefill.hip", "router.hip"):
+    for f in ("common.hpp", "decode_items.hpp", "router_items.hpp", "decode.hip", "decode_fused.hip", "prefill.hip",
+              "router.hip"):
         with open(os.path.join(ROOT, "mixture_experts_layer_12_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -209,6 +210,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "fused", "prefill"],
+                    help="execution path (auto: the library's choice for the shape)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -242,7 +245,14 @@ def main():
     inp = synth.make_inputs_torch(wl, args.seed, device=dev, copies=copies)
     if copies == 1:
         inp = {k: [v] for k, v in inp.items()}
-    shape = m.make_shape(wl.T, wl.H, wl.E, wl.I, wl.k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype)
+    path_arg = {"auto": m.MOE_PATH_AUTO, "decode": m.MOE_PATH_DECODE, "fused": m.MOE_PATH_DECODE_FUSED,
+                "prefill": m.MOE_PATH_PREFILL}[args.path]
+    shape = m.make_shape(wl.T, wl.H, wl.E, wl.I, wl.k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype, path_arg)
+    path = m.moe_resolve_path(shape)
+    path_name = {m.MOE_PATH_DECODE: "decode", m.MOE_PATH_PREFILL: "prefill",
+                 m.MOE_PATH_DECODE_FUSED: "decode_fused"}[path]
+    if args.graph and path == m.MOE_PATH_DECODE_FUSED:
+        path_name = "decode"       # a captured single-launch decode records the multi-launch form
     ws = m.alloc_workspace(shape, dev)
     out = torch.empty_like(inp["x"][0])
     stream = torch.cuda.current_stream()
@@ -301,8 +311,9 @@ def main():
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s (eager {eager_value:.1f} tokens/s)")
 
     # stage timing with HIP events recorded on the launch stream
-    prefill = wl.x_dtype == "bf16" and wl.w_dtype == "bf16" and wl.T > 64
-    n_ev = 5 if prefill else 4
+    prefill = path_name == "prefill"
+    fused = path_name == "decode_fused"
+    n_ev = 5 if prefill else (2 if fused else 4)
     hip = HipEvents()
     evs = [hip.create(n_ev) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -314,7 +325,7 @@ def main():
         hip.destroy(e)
     avg = [sum(s[j] for s in stage) / len(stage) for j in range(n_ev - 1)]
     names = (["router", "prefill_gateup", "prefill_down", "cast"] if prefill
-             else ["router", "decode_gateup", "decode_down"])
+             else (["decode_fused"] if fused else ["router", "decode_gateup", "decode_down"]))
     log("[bench] stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, avg)))
 
     # engaged experts per weight copy (from the run's own routing)
@@ -337,6 +348,16 @@ def main():
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(wl.name, kname),
                 "kernel": kname, "launch_ms": round(avg[1], 5), "alg_flops_per_launch": fl,
                 "layer_tflops": round(layer_flops(wl) / (ms_per_step * 1e-3) / 1e12, 2)}
+    elif fused:
+        # one launch runs the whole layer: its algorithmic bytes over its duration
+        kname = "decode_fused"
+        lay = sum(layer_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+        achieved = lay / (avg[0] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name, kname),
+                "kernel": kname, "launch_ms": round(avg[0], 5), "alg_bytes_per_launch": int(lay),
+                "mean_active_experts": round(mean_active, 3),
+                "layer_gbs": round(lay / (ms_per_step * 1e-3) / 1e9, 1)}
     else:
         kname = "decode_gateup"
         alg = sum(gateup_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
@@ -364,7 +385,7 @@ def main():
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "top_k": wl.k, "I": wl.I,
                    "n_shared": wl.S, "I_shared": wl.Is, "weights": wl.w_dtype, "activations": wl.x_dtype,
-                   "router": wl.r_dtype, "path": "prefill" if prefill else "decode", "weight_copies": copies,
+                   "router": wl.r_dtype, "path": path_name, "weight_copies": copies,
                    "timing": timing, "parallelism": "single-gpu"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -53,8 +53,7 @@ enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2 };
 
 /* execution path (moe_shape_t.path) */
 enum {
-  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill;
-                           the single-launch decode where it applies (see below) */
+  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill */
   MOE_PATH_DECODE = 1,  /* weight-streaming mat-vec kernels, any supported dtype, any T */
   MOE_PATH_PREFILL = 2, /* bf16 MFMA grouped GEMMs; needs x, experts bf16 */
   MOE_PATH_DECODE_FUSED = 3  /* the decode kernels as one cooperative launch per pass of
@@ -139,6 +138,11 @@ typedef struct {
 /* Bytes of workspace moe_forward / moe_route need for shape *s (host call,
  * no GPU access).  Returns MOE_OK and writes *bytes, or a validation error. */
 int moe_workspace_size(const moe_shape_t* s, size_t* bytes /* host */);
+
+/* The path moe_forward takes for shape *s when the stream is not being
+ * captured: s->path itself, or what MOE_PATH_AUTO resolves to (host call).
+ * Returns the MOE_PATH_* value (1, 2 or 3) or a validation error (< 0). */
+int moe_resolve_path(const moe_shape_t* s);
 
 /* Dimensions of the expert-sorted order for shape *s (host call):
  * tile_m (padding multiple), capacity = roundup(T*top_k + E*(tile_m-1), tile_m),

@@ -25,7 +25,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
-            "moe_last_hip_error", "moe_strerror")
+            "moe_last_hip_error", "moe_strerror", "moe_resolve_path")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_profiled.restype = ctypes.c_int
     lib.moe_last_hip_error.argtypes = []
     lib.moe_last_hip_error.restype = ctypes.c_int
+    lib.moe_resolve_path.argtypes = [P(moe_shape_t)]
+    lib.moe_resolve_path.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -124,6 +126,14 @@ def hip_error_name(err: int) -> str:
         return f"hipError {err} ({hip.hipGetErrorName(err).decode()})"
     except OSError:
         return f"hipError {err}"
+
+
+def moe_resolve_path(shape: moe_shape_t) -> int:
+    """MOE_PATH_DECODE / _PREFILL / _DECODE_FUSED that moe_forward takes for ``shape``."""
+    rc = load_library().moe_resolve_path(ctypes.byref(shape))
+    if rc < 0:
+        raise MoeError(rc, "moe_resolve_path")
+    return rc
 
 
 def moe_workspace_size(shape: moe_shape_t) -> int:

@@ -69,12 +69,12 @@ int check_shape(const moe_shape_t* s) {
   return MOE_OK;
 }
 
-bool fused_ok(const moe_shape_t* s) { return s->router_dtype == s->x_dtype && s->top_k <= kFusedMaxK; }
-
 int choose_path(const moe_shape_t* s) {
   if (s->path != MOE_PATH_AUTO) return s->path;
   if (s->x_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 && s->T > kDecodeMaxT) return MOE_PATH_PREFILL;
-  return fused_ok(s) ? MOE_PATH_DECODE_FUSED : MOE_PATH_DECODE;
+  // The single-launch decode is measured slower than the multi-launch kernels on every benchmarked
+  // shape (its resident grid runs items one after another per work-group), so AUTO does not pick it.
+  return MOE_PATH_DECODE;
 }
 
 // Work list of one single-launch decode pass of Tc tokens (see decode_fused.hip).
@@ -211,6 +211,11 @@ const char* moe_strerror(int code) {
 }
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_resolve_path(const moe_shape_t* s) {
+  if (int rc = check_shape(s)) return rc;
+  return choose_path(s);
+}
 
 int moe_workspace_size(const moe_shape_t* s, size_t* bytes) {
   if (!s || !bytes) return MOE_ERR_NULL;
