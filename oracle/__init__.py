@@ -26,7 +26,7 @@ selected probabilities renormalised to sum to 1; shared experts added with
 weight 1; optional router bias added to the logits.
 
 Modules:
-  formats -- decoding of the stored input formats (bf16, fp16, Q4_0 SoA)
+  formats -- decoding of the stored input formats (bf16, fp16, Q4_0, Q8_0, fp8 E4M3)
   moe     -- vectorised fp64 reference (numpy)
   loops   -- pure-Python brute force for tiny shapes
 """
@@ -36,7 +36,8 @@ from .moe import (  # noqa: F401
     silu, swiglu_ffn, moe_forward, moe_forward_tokens, dispatch, dense_gate_matrix,
 )
 from .formats import (  # noqa: F401
-    bf16_to_f64, f16_to_f64, q4_0_decode, q4_0_decode_matrix, weights_to_f64, decode_inputs,
+    bf16_to_f64, f16_to_f64, q4_0_decode, q4_0_decode_matrix, q8_0_decode, q8_0_matrix, fp8_e4m3_to_f64,
+    fp8_e4m3_decode, fp8_e4m3_matrix, weights_to_f64, decode_inputs,
     decode_workload_inputs,
 )
 from .moe import padded_rows  # noqa: F401

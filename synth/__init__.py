@@ -30,6 +30,14 @@ fp16 scales [E, N, K/32].  Inside one 32-value block, value j < 16 lives in
 the low nibble of byte j and value j + 16 in the high nibble of byte j.  The
 value it stands for is d * (q - 8).
 
+Q8_0 and fp8 E4M3 stacks are made from normal weights N(0, 0.02^2) drawn
+like the bf16 ones (float32): Q8_0 takes per block of 32 along K the scale
+d = fp16(max|w| / 127) and the codes q = clip(round(w / d), -127, 127); fp8
+takes per row the fp32 scale s = max|w| / 448 and the codes E4M3(w / s)
+(nearest, ties to even; torch's float8_e4m3fn conversion).  Storage: all codes
+[E, N, K] (one byte each) first, then from the next 256-byte boundary the
+scales (Q8_0: fp16 [E, N, K/32]; fp8: fp32 [E, N]).
+
 Large workloads can also be drawn on the GPU with ``torch`` generators
 (``make_inputs_torch``); they then have the same shapes and distributions but
 not the same bits as the numpy recipe.
@@ -41,7 +49,7 @@ from typing import Optional
 
 import numpy as np
 
-F32, BF16, Q4_0 = "f32", "bf16", "q4_0"
+F32, BF16, Q4_0, Q8_0, FP8 = "f32", "bf16", "q4_0", "q8_0", "fp8_e4m3"
 Q4_BLOCK = 32
 Q4_ALIGN = 256
 
@@ -78,6 +86,10 @@ WORKLOADS = {
         Workload("deepseek16b_decode_t8", T=8, H=2048, E=64, k=6, I=1408, S=2, Is=1408),
         Workload("deepseek16b_decode_t64", T=64, H=2048, E=64, k=6, I=1408, S=2, Is=1408),
         Workload("mixtral_prefill_t4096", T=4096, H=4096, E=8, k=2, I=14336, zipf_s=1.2),
+        # 8-bit weight variants of two decode shapes
+        Workload("mixtral_decode_t8_fp8", T=8, H=4096, E=8, k=2, I=14336, w_dtype=FP8),
+        Workload("qwen_a3b_decode_q8", T=1, H=2048, E=256, k=8, I=512, S=1, Is=512,
+                 x_dtype=F32, w_dtype=Q8_0, r_dtype=F32),
     ]
 }
 
@@ -114,6 +126,47 @@ def q4_0_pack(q: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
     buf[: nib.size] = nib
     off = _align(nib.size, Q4_ALIGN)
     buf[off:] = np.ascontiguousarray(d_f16, dtype=np.float16).reshape(-1).view(np.uint8)
+    return buf
+
+
+def weight_nbytes(dtype: str, E: int, N: int, K: int) -> int:
+    """Bytes of one stored weight stack [E, N, K]."""
+    if dtype == F32:
+        return 4 * E * N * K
+    if dtype == BF16:
+        return 2 * E * N * K
+    if dtype == Q4_0:
+        return q4_0_nbytes(E, N, K)
+    if dtype == Q8_0:
+        return _align(E * N * K, Q4_ALIGN) + 2 * E * N * (K // Q4_BLOCK)
+    if dtype == FP8:
+        return _align(E * N * K, Q4_ALIGN) + 4 * E * N
+    raise ValueError(dtype)
+
+
+def pack_weights(w: np.ndarray, dtype: str) -> np.ndarray:
+    """Quantise float32 weights [E, N, K] to a Q8_0 or fp8 E4M3 stack (uint8 buffer)."""
+    import torch
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    E, N, K = w.shape
+    buf = np.zeros(weight_nbytes(dtype, E, N, K), dtype=np.uint8)
+    off = _align(E * N * K, Q4_ALIGN)
+    if dtype == Q8_0:
+        blk = w.reshape(E, N, K // Q4_BLOCK, Q4_BLOCK)
+        d = (np.abs(blk).max(-1) / np.float32(127)).astype(np.float16)
+        dd = d.astype(np.float32)[..., None]
+        q = np.where(dd > 0, np.rint(blk / np.where(dd > 0, dd, 1)), 0)
+        q = np.clip(q, -127, 127).astype(np.int8)
+        buf[:E * N * K] = q.reshape(-1).view(np.uint8)
+        buf[off:] = d.reshape(-1).view(np.uint8)
+    elif dtype == FP8:
+        sc = (np.abs(w).max(-1) / np.float32(448)).astype(np.float32)
+        v = w / np.where(sc > 0, sc, 1)[..., None]
+        codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        buf[:E * N * K] = codes.reshape(-1)
+        buf[off:] = sc.reshape(-1).view(np.uint8)
+    else:
+        raise ValueError(dtype)
     return buf
 
 
@@ -154,6 +207,15 @@ def _q4_matrix(rng, E, N, K, d_std):
 def _expert_stack(rng, w: Workload, n: int, inter: int):
     """gate [n, inter, H], up [n, inter, H], down [n, H, inter]; drawn expert by expert."""
     H = w.H
+    if w.w_dtype in (Q8_0, FP8):
+        g = np.empty((n, inter, H), dtype=np.float32)
+        u = np.empty((n, inter, H), dtype=np.float32)
+        d = np.empty((n, H, inter), dtype=np.float32)
+        for e in range(n):
+            g[e] = _normal(rng, (inter, H), w.w_std, F32)
+            u[e] = _normal(rng, (inter, H), w.w_std, F32)
+            d[e] = _normal(rng, (H, inter), w.w_std, F32)
+        return pack_weights(g, w.w_dtype), pack_weights(u, w.w_dtype), pack_weights(d, w.w_dtype)
     if w.w_dtype == Q4_0:
         gs, us, ds = [], [], []
         for _ in range(n):
@@ -238,9 +300,30 @@ def make_inputs_torch(w: Workload, seed: int, device="cuda", copies: int = 1) ->
         buf[off:] = d.reshape(-1).view(torch.uint8)
         return buf
 
+    def q8_or_fp8(E, N, K):
+        t = torch.randn((E, N, K), generator=gen, device=device, dtype=torch.float32).mul_(w.w_std)
+        buf = torch.zeros(weight_nbytes(w.w_dtype, E, N, K), dtype=torch.uint8, device=device)
+        off = _align(E * N * K, Q4_ALIGN)
+        if w.w_dtype == Q8_0:
+            blk = t.view(E, N, K // Q4_BLOCK, Q4_BLOCK)
+            d = (blk.abs().amax(-1) / 127).to(torch.float16)
+            dd = d.float().unsqueeze(-1)
+            q = torch.where(dd > 0, torch.round(blk / torch.where(dd > 0, dd, torch.ones_like(dd))),
+                            torch.zeros_like(blk)).clamp_(-127, 127).to(torch.int8)
+            buf[: E * N * K] = q.reshape(-1).view(torch.uint8)
+            buf[off:] = d.reshape(-1).view(torch.uint8)
+        else:
+            sc = t.abs().amax(-1) / 448
+            v = t / torch.where(sc > 0, sc, torch.ones_like(sc)).unsqueeze(-1)
+            buf[: E * N * K] = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(-1)
+            buf[off:] = sc.reshape(-1).view(torch.uint8)
+        return buf
+
     def stack(n, inter):
         if w.w_dtype == Q4_0:
             return q4(n, inter, w.H), q4(n, inter, w.H), q4(n, w.H, inter)
+        if w.w_dtype in (Q8_0, FP8):
+            return q8_or_fp8(n, inter, w.H), q8_or_fp8(n, inter, w.H), q8_or_fp8(n, w.H, inter)
         return (normal((n, inter, w.H), w.w_std, w.w_dtype),
                 normal((n, inter, w.H), w.w_std, w.w_dtype),
                 normal((n, w.H, inter), w.w_std, w.w_dtype))

@@ -295,3 +295,83 @@ def test_q4_0_single_matrix_decode_matches_stack_decode():
         assert np.array_equal(oracle.q4_0_decode_matrix(buf, E, N, K, e), full[e])
     # and both equal d * (q - 8) computed from the unpacked draws
     assert np.array_equal(full, d.astype(np.float64).repeat(32, axis=-1) * (q.astype(np.float64) - 8))
+
+
+# ------------------------------------------------------------ Q8_0 / FP8 ----
+
+# E4M3 codes worked out by hand from the OCP 8-bit floating point definition
+# (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 subnormal).
+E4M3_HAND = [
+    (0x00, 0.0), (0x38, 1.0), (0xB8, -1.0), (0x30, 0.5), (0x3C, 1.5), (0x40, 2.0), (0x78, 256.0),
+    (0x7E, 448.0), (0xFE, -448.0), (0x08, 2.0 ** -6), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),
+    (0x0F, 1.875 * 2.0 ** -6), (0x81, -(2.0 ** -9)),
+]
+
+
+def test_fp8_e4m3_hand_values():
+    codes = np.array([c for c, _ in E4M3_HAND], dtype=np.uint8)
+    got = oracle.fp8_e4m3_to_f64(codes)
+    assert got.tolist() == [v for _, v in E4M3_HAND]
+    assert np.signbit(oracle.fp8_e4m3_to_f64(np.array([0x80], np.uint8)))[0]      # -0
+    assert np.isnan(oracle.fp8_e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_fp8_e4m3_all_codes_match_library_decoder():
+    """Every one of the 256 codes against PyTorch's own float8_e4m3fn decoding."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = oracle.fp8_e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(lib[ok], ours[ok])
+
+
+def test_fp8_e4m3_positive_codes_increase():
+    v = oracle.fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(v) > 0) and v[-1] == 448.0
+
+
+def test_q8_0_hand_block_and_scale_offset():
+    """One row of two blocks: codes in the first 64 bytes, the two fp16 scales
+    from byte 256 (the next 256-byte boundary)."""
+    q = np.array(list(range(-16, 16)) + [127, -128] + [0] * 30, dtype=np.int8)
+    buf = np.zeros(256 + 4, dtype=np.uint8)
+    buf[:64] = q.view(np.uint8)
+    buf[256:260] = np.array([0.5, -2.0], dtype=np.float16).view(np.uint8)
+    w = oracle.q8_0_decode(buf, 1, 1, 64)[0, 0]
+    assert w[:32].tolist() == [0.5 * v for v in range(-16, 16)]
+    assert w[32] == -254.0 and w[33] == 256.0 and np.all(w[34:] == 0.0)
+
+
+def test_fp8_stack_row_scales_and_matrix_index():
+    """Two matrices of two rows: matrix e, row n scales by s[e, n]; the scales
+    start at the 256-byte boundary after all codes."""
+    E, N, K = 2, 2, 32
+    codes = np.full((E, N, K), 0x38, dtype=np.uint8)      # 1.0
+    codes[1, 0, 5] = 0xC0                                   # -2.0
+    s = np.array([[1.0, 0.5], [3.0, -0.25]], dtype=np.float32)
+    buf = np.zeros(256 + 16, dtype=np.uint8)
+    buf[:E * N * K] = codes.reshape(-1)
+    buf[256:272] = s.view(np.uint8).reshape(-1)
+    w = oracle.fp8_e4m3_decode(buf, E, N, K)
+    assert np.all(w[0, 0] == 1.0) and np.all(w[0, 1] == 0.5) and np.all(w[1, 1] == -0.25)
+    assert w[1, 0, 5] == -6.0 and np.sum(w[1, 0] == 3.0) == K - 1
+
+
+@pytest.mark.parametrize("dtype", ["q8_0", "fp8_e4m3"])
+def test_generator_8bit_stacks_round_trip(dtype):
+    """Stacks made by the input generator decode to within the format's own
+    rounding of the normal values they were made from."""
+    rng = np.random.default_rng(3)
+    w = rng.normal(0, 0.02, size=(3, 5, 64)).astype(np.float32)
+    buf = synth.pack_weights(w, dtype)
+    assert buf.size == synth.weight_nbytes(dtype, 3, 5, 64)
+    dec = oracle.weights_to_f64(buf, dtype, (3, 5, 64))
+    if dtype == "q8_0":      # |err| <= d/2 per block (plus fp16 rounding of d)
+        d = np.abs(w.reshape(3, 5, 2, 32)).max(-1, keepdims=True) / 127
+        assert np.all(np.abs(dec.reshape(3, 5, 2, 32) - w.reshape(3, 5, 2, 32)) <= 0.51 * d + 1e-7)
+    else:                    # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 for normals
+        rel = np.abs(dec - w) / np.maximum(np.abs(w), 1e-30)
+        s = np.abs(w).max(-1, keepdims=True) / 448
+        assert np.all((rel <= 2.0 ** -4 + 1e-6) | (np.abs(w) < 2.0 ** -6 * s))
