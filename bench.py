@@ -77,40 +77,53 @@ class HipEvents:
 
 # ---------------------------------------------------------- byte counting ----
 
-def weight_bytes_per_value(w_dtype):
-    return {"f32": 4.0, "bf16": 2.0, "q4_0": 18.0 / 32.0}[w_dtype]
+def mat_bytes(w_dtype, N, K):
+    """Stored bytes of one weight matrix [N, K], scales included."""
+    if w_dtype == "f32":
+        return 4 * N * K
+    if w_dtype == "bf16":
+        return 2 * N * K
+    if w_dtype == "q4_0":
+        return N * K // 2 + 2 * N * (K // 32)
+    if w_dtype == "q8_0":
+        return N * K + 2 * N * (K // 32)
+    if w_dtype == "fp8_e4m3":
+        return N * K + 4 * N
+    raise ValueError(w_dtype)
 
 
 def act_bytes(dt):
     return 4 if dt == "f32" else 2
 
 
+def h_elem_bytes(wl):
+    """Bytes per element of the activation rows between the decode launches."""
+    return 2 if wl.w_dtype in ("q4_0", "q8_0") else 4
+
+
 def layer_bytes(wl):
     """Bytes of one full copy of the layer's weights (all experts)."""
-    bw = weight_bytes_per_value(wl.w_dtype)
-    return (3 * wl.E * wl.H * wl.I + 3 * wl.S * wl.H * wl.Is) * bw + wl.E * wl.H * act_bytes(wl.r_dtype)
+    return (wl.E * (2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.I))
+            + wl.S * (2 * mat_bytes(wl.w_dtype, wl.Is, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.Is))
+            + wl.E * wl.H * act_bytes(wl.r_dtype))
 
 
 def gateup_alg_bytes(wl, n_active, T):
     """Algorithmic bytes of one decode gate/up launch: the engaged experts' gate
     and up rows, the activations read and the intermediate rows written."""
-    bw = weight_bytes_per_value(wl.w_dtype)
-    h_elem = 2 if wl.w_dtype == "q4_0" else 4
-    return (n_active * 2 * wl.I * wl.H * bw + wl.S * 2 * wl.Is * wl.H * bw + T * wl.H * act_bytes(wl.x_dtype)
-            + (T * wl.k * wl.I + wl.S * T * wl.Is) * h_elem)
+    return (n_active * 2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + wl.S * 2 * mat_bytes(wl.w_dtype, wl.Is, wl.H)
+            + T * wl.H * act_bytes(wl.x_dtype) + (T * wl.k * wl.I + wl.S * T * wl.Is) * h_elem_bytes(wl))
 
 
 def down_alg_bytes(wl, n_active, T):
-    bw = weight_bytes_per_value(wl.w_dtype)
-    h_elem = 2 if wl.w_dtype == "q4_0" else 4
-    return (n_active * wl.H * wl.I * bw + wl.S * wl.H * wl.Is * bw
-            + (T * wl.k * wl.I + wl.S * T * wl.Is) * h_elem + T * wl.H * act_bytes(wl.x_dtype))
+    return (n_active * mat_bytes(wl.w_dtype, wl.H, wl.I) + wl.S * mat_bytes(wl.w_dtype, wl.H, wl.Is)
+            + (T * wl.k * wl.I + wl.S * T * wl.Is) * h_elem_bytes(wl) + T * wl.H * act_bytes(wl.x_dtype))
 
 
 def layer_alg_bytes(wl, n_active, T):
-    bw = weight_bytes_per_value(wl.w_dtype)
-    return (n_active * 3 * wl.H * wl.I * bw + wl.S * 3 * wl.H * wl.Is * bw + wl.E * wl.H * act_bytes(wl.r_dtype)
-            + T * wl.H * 2 * act_bytes(wl.x_dtype))
+    return (n_active * (2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.I))
+            + wl.S * (2 * mat_bytes(wl.w_dtype, wl.Is, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.Is))
+            + wl.E * wl.H * act_bytes(wl.r_dtype) + T * wl.H * 2 * act_bytes(wl.x_dtype))
 
 
 def gateup_flops(wl):
@@ -165,6 +178,15 @@ def cpu_baseline(wl, t, tokens_max=16, min_seconds=5.0):
         a = t[key]
         if wl.w_dtype == "q4_0":
             return oracle.q4_0_decode_matrix(a.cpu().numpy(), n_mat, N, K, e)
+        if wl.w_dtype in ("q8_0", "fp8_e4m3"):
+            off = (n_mat * N * K + 255) // 256 * 256          # scales after all one-byte codes
+            codes = a[e * N * K:(e + 1) * N * K].cpu().numpy().reshape(N, K)
+            if wl.w_dtype == "q8_0":
+                nb = N * (K // 32) * 2
+                return oracle.q8_0_matrix(codes, a[off + e * nb:off + (e + 1) * nb].cpu().numpy().view(np.uint16)
+                                          .reshape(N, K // 32))
+            return oracle.fp8_e4m3_matrix(codes, a[off + 4 * e * N:off + 4 * (e + 1) * N].cpu().numpy()
+                                          .view(np.float32))
         return f64(a[e])
 
     def once():
@@ -378,7 +400,8 @@ def main():
         cpu = cpu_baseline(wl, t_cpu)
         log(f"[bench] cpu oracle: {cpu}")
 
-    dtype = {"bf16": "bf16", "f32": "f32", "q4_0": "q4_0xf16"}[wl.w_dtype]
+    # arithmetic type of the expert dot products (weights x activations)
+    dtype = {"bf16": "bf16", "f32": "f32", "q4_0": "q4_0xf16", "q8_0": "q8_0xf16", "fp8_e4m3": "fp8e4m3xbf16"}[wl.w_dtype]
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",

@@ -48,8 +48,8 @@
 extern "C" {
 #endif
 
-/* element types */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2 };
+/* element types (MOE_Q8_0 and MOE_FP8_E4M3: expert weights of the decode path only) */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2, MOE_Q8_0 = 3, MOE_FP8_E4M3 = 4 };
 
 /* execution path (moe_shape_t.path) */
 enum {
@@ -85,7 +85,8 @@ enum {
  *   I_shared  shared-expert intermediate size (same rules as I); ignored
  *             when n_shared == 0.
  *   x_dtype   MOE_F32 | MOE_BF16; `out` has the same dtype.
- *   w_dtype   MOE_F32 | MOE_BF16 | MOE_Q4_0, for routed and shared experts.
+ *   w_dtype   MOE_F32 | MOE_BF16 | MOE_Q4_0 | MOE_Q8_0 | MOE_FP8_E4M3, for routed
+ *             and shared experts (the two 8-bit types on MOE_PATH_DECODE only).
  *   router_dtype  MOE_F32 | MOE_BF16.
  *   path      MOE_PATH_*.
  *
@@ -99,6 +100,12 @@ enum {
  * along K, value j < 16 is the low nibble of byte j and value j + 16 the high
  * nibble of byte j; the value is d * (q - 8).  The stored d must satisfy
  * 8 * |d| <= 65504.
+ * A MOE_Q8_0 stack [E, N, K] (K % 32 == 0): all int8 codes [E, N, K] first,
+ * then from the next multiple of 256 bytes all fp16 scales [E, N, K/32];
+ * the value of code q in block b is d_b * q (|d_b| * 128 <= 65504).
+ * A MOE_FP8_E4M3 stack [E, N, K]: all codes [E, N, K] in the OCP E4M3
+ * encoding first, then from the next multiple of 256 bytes the fp32 scales
+ * [E, N], one per row; the value is scale[e][n] * E4M3(code).
  */
 typedef struct {
   int32_t T, H, E, I, top_k;

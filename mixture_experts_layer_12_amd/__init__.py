@@ -18,12 +18,12 @@ LIB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
 
 # enums of moe.h
-MOE_F32, MOE_BF16, MOE_Q4_0 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_Q4_0, MOE_Q8_0, MOE_FP8_E4M3 = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_DECODE_FUSED = 0, 1, 2, 3
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
             "moe_last_hip_error", "moe_strerror", "moe_resolve_path")
 

@@ -59,9 +59,10 @@ int check_shape(const moe_shape_t* s) {
   if (S > 0 && (Is < 32 || Is > 1048576 || Is % 32)) return MOE_ERR_SHAPE;
   if (s->x_dtype != MOE_F32 && s->x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (s->router_dtype != MOE_F32 && s->router_dtype != MOE_BF16) return MOE_ERR_DTYPE;
-  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_Q4_0) return MOE_ERR_DTYPE;
+  if (s->w_dtype < MOE_F32 || s->w_dtype > MOE_FP8_E4M3) return MOE_ERR_DTYPE;
   if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_DECODE_FUSED) return MOE_ERR_SHAPE;
-  if (s->path == MOE_PATH_DECODE_FUSED && s->router_dtype != s->x_dtype) return MOE_ERR_DTYPE;
+  if (s->path == MOE_PATH_DECODE_FUSED && (s->router_dtype != s->x_dtype || s->w_dtype > MOE_Q4_0))
+    return MOE_ERR_DTYPE;
   if (s->path == MOE_PATH_DECODE_FUSED && s->top_k > kFusedMaxK) return MOE_ERR_SHAPE;
   if (s->path == MOE_PATH_PREFILL && (s->x_dtype != MOE_BF16 || s->w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
   // index arithmetic of the largest buffers stays in 32-bit ranges
@@ -131,7 +132,8 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     L.h_stride = int(roundup(L.h_stride, kHRowAlign));
     const long rows = long(Tr) * k + long(S) * Tr;
     L.h_plane = rows * L.h_stride;
-    const size_t elem = s->w_dtype == MOE_Q4_0 ? 2 : 4;   // fp16 | fp32 | bf16 hi + lo planes
+    // fp16 (Q4_0, Q8_0) | fp32 | bf16 hi + lo planes (bf16, fp8)
+    const size_t elem = (s->w_dtype == MOE_Q4_0 || s->w_dtype == MOE_Q8_0) ? 2 : 4;
     L.h = take(size_t(L.h_plane) * elem);
     L.partials = take(size_t(rows) * H * 4);
     if (L.path == MOE_PATH_DECODE_FUSED) {

@@ -17,7 +17,7 @@
 
 namespace moe {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q4 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q4 = 2, DT_Q8 = 3, DT_FP8 = 4 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -116,6 +116,54 @@ __device__ __forceinline__ void q4_dequant_block(u32x4_t raw, uint16_t d_bits, u
       frag[half + 2][2 * wi + 1] = q4_scale_pair(q4_pair(w >> 12), d2);
     }
   }
+}
+
+// ------------------------------------------------------------------ Q8_0 --
+// One block of 32 signed codes (two 16-byte loads) and its fp16 scale d ->
+// four fp16x8 operands (frag f = values 8f .. 8f+7), each d * q.  Flipping the
+// sign bit turns q into q + 128 in 0..255, which is OR-ed into the mantissa of
+// 1024 exactly; subtracting 1152 gives q exactly and one multiply rounds once.
+
+__device__ __forceinline__ uint32_t q8_scale_pair(uint32_t magic, f16x2_t d2) {
+  const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - off;
+  return __builtin_bit_cast(uint32_t, v * d2);
+}
+
+__device__ __forceinline__ void q8_dequant_block(u32x4_t raw0, u32x4_t raw1, uint16_t d_bits, u32x4_t frag[4]) {
+  _Float16 d = __builtin_bit_cast(_Float16, d_bits);
+  f16x2_t d2 = {d, d};
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {                 // word w holds values 4w .. 4w+3
+    const uint32_t t = (w < 4 ? raw0[w] : raw1[w - 4]) ^ 0x80808080u;
+    // bytes [t0 0x64 t1 0x64] and [t2 0x64 t3 0x64]: two fp16 pairs 1024 + u
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
+    frag[w >> 1][2 * (w & 1) + 0] = q8_scale_pair(lo, d2);
+    frag[w >> 1][2 * (w & 1) + 1] = q8_scale_pair(hi, d2);
+  }
+}
+
+// ------------------------------------------------------------ fp8 E4M3 --
+// 16 E4M3 codes -> two bf16x8 operands (codes 0..7, 8..15).  The hardware
+// conversion reads the OCP E4M3 encoding on this architecture; every E4M3
+// value is exact in bf16, and the scale 1.0 leaves it unchanged.
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4_t raw, u32x4_t out[2]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    out[w >> 1][2 * (w & 1) + 0] =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(raw[w]), 1.0f, false));
+    out[w >> 1][2 * (w & 1) + 1] =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(raw[w]), 1.0f, true));
+  }
+}
+
+// Byte offset of the scale array of a one-byte-code stack (Q8_0, fp8) [n_mat, N, K].
+__host__ __device__ __forceinline__ size_t byte_code_scale_offset(long n_mat, long N, long K) {
+  return (size_t(n_mat) * size_t(N) * size_t(K) + 255) / 256 * 256;
 }
 
 // Byte offset of the scale array of a Q4_0 stack [n_mat, N, K].

@@ -51,9 +51,17 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_til
   } else if (wdt == DT_BF16) {
     if (xdt == DT_F32) launch_decode_x<DT_BF16, DT_F32>(a, n_gu_row_tiles, st, mark);
     else launch_decode_x<DT_BF16, DT_BF16>(a, n_gu_row_tiles, st, mark);
-  } else {
+  } else if (wdt == DT_Q4) {
     if (xdt == DT_F32) launch_decode_x<DT_Q4, DT_F32>(a, n_gu_row_tiles, st, mark);
     else launch_decode_x<DT_Q4, DT_BF16>(a, n_gu_row_tiles, st, mark);
+  } else if (wdt == DT_Q8) {
+    if (xdt == DT_F32) launch_decode_x<DT_Q8, DT_F32>(a, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_Q8, DT_BF16>(a, n_gu_row_tiles, st, mark);
+  } else if (wdt == DT_FP8) {
+    if (xdt == DT_F32) launch_decode_x<DT_FP8, DT_F32>(a, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_FP8, DT_BF16>(a, n_gu_row_tiles, st, mark);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

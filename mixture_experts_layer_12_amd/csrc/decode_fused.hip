@@ -168,7 +168,9 @@ hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t
   if (wdt == DT_F32) return xdt == DT_F32 ? launch_fused_x<DT_F32, DT_F32>(f, st) : launch_fused_x<DT_F32, DT_BF16>(f, st);
   if (wdt == DT_BF16)
     return xdt == DT_F32 ? launch_fused_x<DT_BF16, DT_F32>(f, st) : launch_fused_x<DT_BF16, DT_BF16>(f, st);
-  return xdt == DT_F32 ? launch_fused_x<DT_Q4, DT_F32>(f, st) : launch_fused_x<DT_Q4, DT_BF16>(f, st);
+  if (wdt == DT_Q4)
+    return xdt == DT_F32 ? launch_fused_x<DT_Q4, DT_F32>(f, st) : launch_fused_x<DT_Q4, DT_BF16>(f, st);
+  return hipErrorInvalidValue;       // the 8-bit weight types run the multi-launch decode only
 }
 
 }  // namespace moe

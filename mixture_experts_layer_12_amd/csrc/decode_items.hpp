@@ -40,92 +40,150 @@
 
 namespace moe {
 
-template <int WT> struct KPL;
-template <> struct KPL<DT_F32> { static constexpr int v = 4; };
-template <> struct KPL<DT_BF16> { static constexpr int v = 8; };
-template <> struct KPL<DT_Q4> { static constexpr int v = 32; };
+// Operand family of a stored weight type: the MFMA it feeds, the activation
+// (B operand) layout and the format of the activation rows between gate/up
+// and down.  Q8_0 shares Q4_0's (one 32-value block per lane group, fp16);
+// fp8 has its own (16 codes per lane group, two bf16 k-slices of 8).
+template <int WT> struct Fam { static constexpr int v = WT; };
+template <> struct Fam<DT_Q8> { static constexpr int v = DT_Q4; };
 
 // Number of 4-lane-group steps along a reduction of length K.
 template <int WT>
 __host__ __device__ __forceinline__ int n_steps(int K) {
-  if constexpr (WT == DT_Q4) return (K / 32 + 3) / 4;
-  else return K / (4 * KPL<WT>::v);
+  if constexpr (WT == DT_F32) return K / 16;
+  else if constexpr (WT == DT_BF16) return K / 32;
+  else if constexpr (WT == DT_FP8) return (K + 63) / 64;
+  else return (K / 32 + 3) / 4;                    // Q4_0, Q8_0
 }
 
 // Row r of matrix `e` in a stack [n_mat, N, K].
 template <int WT>
 struct RowPtr {
-  const uint8_t* p;        // first byte of the row (nibbles for Q4_0)
-  const uint16_t* sc;      // Q4_0 scales of the row
+  const uint8_t* p;        // first byte of the row (codes for the quantised types)
+  const uint16_t* sc;      // Q4_0 / Q8_0 block scales of the row
   __device__ __forceinline__ void init(const uint8_t* base, long n_mat, long N, long K, long e, long r) {
-    if constexpr (WT == DT_F32) p = base + (size_t(e) * N + r) * K * 4;
-    else if constexpr (WT == DT_BF16) p = base + (size_t(e) * N + r) * K * 2;
-    else {
-      p = base + (size_t(e) * N + r) * (K / 2);
-      sc = reinterpret_cast<const uint16_t*>(base + q4_scale_offset(n_mat, N, K)) + (size_t(e) * N + r) * (K / 32);
+    const size_t row = size_t(e) * N + r;
+    if constexpr (WT == DT_F32) p = base + row * K * 4;
+    else if constexpr (WT == DT_BF16) p = base + row * K * 2;
+    else if constexpr (WT == DT_Q4) {
+      p = base + row * (K / 2);
+      sc = reinterpret_cast<const uint16_t*>(base + q4_scale_offset(n_mat, N, K)) + row * (K / 32);
+    } else if constexpr (WT == DT_Q8) {
+      p = base + row * K;
+      sc = reinterpret_cast<const uint16_t*>(base + byte_code_scale_offset(n_mat, N, K)) + row * (K / 32);
+    } else {
+      p = base + row * K;
     }
   }
 };
 
-// A operand fragments of one step.
+// fp8 row scales of output rows r0 .. r0+3 of matrix e (one 16-byte load).
+__device__ __forceinline__ f32x4_t fp8_row_scales(const uint8_t* base, long n_mat, long N, long K, long e, long r0) {
+  return *reinterpret_cast<const f32x4_t*>(base + byte_code_scale_offset(n_mat, N, K) + (size_t(e) * N + r0) * 4);
+}
+
+// A operand fragments of one step, as loaded.
 template <int WT> struct AFrag;
 template <> struct AFrag<DT_F32> { u32x4_t v; };
 template <> struct AFrag<DT_BF16> { u32x4_t v; };
 template <> struct AFrag<DT_Q4> { u32x4_t raw; uint16_t d; };
+template <> struct AFrag<DT_Q8> { u32x4_t raw0, raw1; uint16_t d; };
+template <> struct AFrag<DT_FP8> { u32x4_t raw; bool ok; };
 
 template <int WT>
 __device__ __forceinline__ AFrag<WT> load_a(const RowPtr<WT>& r, int s, int g, int K) {
   AFrag<WT> f;
   if constexpr (WT == DT_F32) f.v = ldg16(r.p + size_t(s * 16 + g * 4) * 4);
   else if constexpr (WT == DT_BF16) f.v = ldg16(r.p + size_t(s * 32 + g * 8) * 2);
-  else {
+  else if constexpr (WT == DT_FP8) {
+    const int k0 = s * 64 + g * 16;
+    f.ok = k0 < K;
+    f.raw = ldg16(r.p + (f.ok ? k0 : K - 16));     // past the end: a valid address, zeroed in prep_a
+  } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
     const bool ok = blk < nblk;
     blk = ok ? blk : nblk - 1;
-    f.raw = ldg16(r.p + size_t(blk) * 16);
+    if constexpr (WT == DT_Q4) {
+      f.raw = ldg16(r.p + size_t(blk) * 16);
+    } else {
+      f.raw0 = ldg16(r.p + size_t(blk) * 32);
+      f.raw1 = ldg16(r.p + size_t(blk) * 32 + 16);
+    }
     f.d = ok ? r.sc[blk] : uint16_t(0);
   }
   return f;
 }
 
-// -------------------------------------------------- B operand: activations --
-// x rows (gate/up) in fp32 or bf16; for each weight type the lane supplies the
-// k positions that its A fragment covers.
+// A operand ready for the MFMA of its family (quantised codes expanded once
+// per step and used for every column tile).
+template <int F> struct AReady;
+template <> struct AReady<DT_F32> { u32x4_t v; };
+template <> struct AReady<DT_BF16> { u32x4_t v; };
+template <> struct AReady<DT_Q4> { u32x4_t fr[4]; };
+template <> struct AReady<DT_FP8> { u32x4_t v[2]; };
 
-template <int WT, int XT> struct XFrag;
+template <int WT>
+__device__ __forceinline__ AReady<Fam<WT>::v> prep_a(const AFrag<WT>& a) {
+  AReady<Fam<WT>::v> r;
+  if constexpr (WT == DT_F32 || WT == DT_BF16) r.v = a.v;
+  else if constexpr (WT == DT_Q4) q4_dequant_block(a.raw, a.d, r.fr);
+  else if constexpr (WT == DT_Q8) q8_dequant_block(a.raw0, a.raw1, a.d, r.fr);
+  else fp8x16_to_bf16(a.ok ? a.raw : u32x4_t{0, 0, 0, 0}, r.v);
+  return r;
+}
+
+// -------------------------------------------------- B operand: activations --
+// x rows (gate/up) in fp32 or bf16; for each family the lane supplies the k
+// positions that its A fragment covers.
+
+template <int F, int XT> struct XFrag;
 template <int XT> struct XFrag<DT_F32, XT> { float v[4]; };
 template <> struct XFrag<DT_BF16, DT_BF16> { u32x4_t v; };
 template <> struct XFrag<DT_BF16, DT_F32> { u32x4_t hi, lo; };
 template <int XT> struct XFrag<DT_Q4, XT> { u32x4_t v[4]; };
+template <int XT> struct XFrag<DT_FP8, XT> { XFrag<DT_BF16, XT> p[2]; };
 
 // Raw activation words of one step, loaded with the step's weights and only
 // turned into MFMA operands (cook_x) when the step is computed, so that no
 // wait for them is placed where the loads are issued.
-template <int WT, int XT> struct XRaw;
+template <int F, int XT> struct XRaw;
 template <> struct XRaw<DT_F32, DT_F32> { u32x4_t t; };
 template <> struct XRaw<DT_F32, DT_BF16> { u32x2_t t; };
 template <> struct XRaw<DT_BF16, DT_BF16> { u32x4_t t; };
 template <> struct XRaw<DT_BF16, DT_F32> { u32x4_t t0, t1; };
 template <> struct XRaw<DT_Q4, DT_F32> { u32x4_t t[8]; };
 template <> struct XRaw<DT_Q4, DT_BF16> { u32x4_t t[4]; };
+template <int XT> struct XRaw<DT_FP8, XT> { XRaw<DT_BF16, XT> p[2]; };
 
-template <int WT, int XT>
-__device__ __forceinline__ XRaw<WT, XT> load_x_raw(const uint8_t* xrow, int s, int g, int K) {
-  XRaw<WT, XT> r;
-  if constexpr (WT == DT_F32) {
+// 8 activations from k0 as one bf16-family operand.
+template <int XT>
+__device__ __forceinline__ XRaw<DT_BF16, XT> load_x8(const uint8_t* xrow, int k0) {
+  XRaw<DT_BF16, XT> r;
+  if constexpr (XT == DT_BF16) {
+    r.t = ldg16(xrow + size_t(k0) * 2);
+  } else {
+    const float* xp = reinterpret_cast<const float*>(xrow) + k0;
+    r.t0 = ldg16(xp);
+    r.t1 = ldg16(xp + 4);
+  }
+  return r;
+}
+
+template <int F, int XT>
+__device__ __forceinline__ XRaw<F, XT> load_x_raw(const uint8_t* xrow, int s, int g, int K) {
+  XRaw<F, XT> r;
+  if constexpr (F == DT_F32) {
     const int k0 = s * 16 + g * 4;
     if constexpr (XT == DT_F32) r.t = ldg16(xrow + size_t(k0) * 4);
     else r.t = ldg8(xrow + size_t(k0) * 2);
-  } else if constexpr (WT == DT_BF16) {
-    const int k0 = s * 32 + g * 8;
-    if constexpr (XT == DT_BF16) {
-      r.t = ldg16(xrow + size_t(k0) * 2);
-    } else {
-      const float* xp = reinterpret_cast<const float*>(xrow) + k0;
-      r.t0 = ldg16(xp);
-      r.t1 = ldg16(xp + 4);
-    }
+  } else if constexpr (F == DT_BF16) {
+    r = load_x8<XT>(xrow, s * 32 + g * 8);
+  } else if constexpr (F == DT_FP8) {
+    int k0 = s * 64 + g * 16;
+    k0 = k0 < K ? k0 : K - 16;
+    r.p[0] = load_x8<XT>(xrow, k0);
+    r.p[1] = load_x8<XT>(xrow, k0 + 8);
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
@@ -145,10 +203,28 @@ __device__ __forceinline__ XRaw<WT, XT> load_x_raw(const uint8_t* xrow, int s, i
   return r;
 }
 
-template <int WT, int XT>
-__device__ __forceinline__ XFrag<WT, XT> cook_x(const XRaw<WT, XT>& r, bool ok, int s, int g, int K) {
-  XFrag<WT, XT> b;
-  if constexpr (WT == DT_F32) {
+template <int XT>
+__device__ __forceinline__ XFrag<DT_BF16, XT> cook_x8(const XRaw<DT_BF16, XT>& r, bool ok) {
+  XFrag<DT_BF16, XT> b;
+  if constexpr (XT == DT_BF16) {
+    const u32x4_t z = {0, 0, 0, 0};
+    b.v = ok ? r.t : z;
+  } else {
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[m] = ok ? __uint_as_float(r.t0[m]) : 0.f;
+      v[m + 4] = ok ? __uint_as_float(r.t1[m]) : 0.f;
+    }
+    split_bf16x8(v, b.hi, b.lo);
+  }
+  return b;
+}
+
+template <int F, int XT>
+__device__ __forceinline__ XFrag<F, XT> cook_x(const XRaw<F, XT>& r, bool ok, int s, int g, int K) {
+  XFrag<F, XT> b;
+  if constexpr (F == DT_F32) {
     if constexpr (XT == DT_F32) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) b.v[m] = ok ? __uint_as_float(r.t[m]) : 0.f;
@@ -156,19 +232,12 @@ __device__ __forceinline__ XFrag<WT, XT> cook_x(const XRaw<WT, XT>& r, bool ok, 
       b.v[0] = ok ? bf16_lo(r.t[0]) : 0.f; b.v[1] = ok ? bf16_hi(r.t[0]) : 0.f;
       b.v[2] = ok ? bf16_lo(r.t[1]) : 0.f; b.v[3] = ok ? bf16_hi(r.t[1]) : 0.f;
     }
-  } else if constexpr (WT == DT_BF16) {
-    if constexpr (XT == DT_BF16) {
-      const u32x4_t z = {0, 0, 0, 0};
-      b.v = ok ? r.t : z;
-    } else {
-      float v[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v[m] = ok ? __uint_as_float(r.t0[m]) : 0.f;
-        v[m + 4] = ok ? __uint_as_float(r.t1[m]) : 0.f;
-      }
-      split_bf16x8(v, b.hi, b.lo);
-    }
+  } else if constexpr (F == DT_BF16) {
+    b = cook_x8<XT>(r, ok);
+  } else if constexpr (F == DT_FP8) {
+    ok = ok && s * 64 + g * 16 < K;
+    b.p[0] = cook_x8<XT>(r.p[0], ok);
+    b.p[1] = cook_x8<XT>(r.p[1], ok);
   } else {
     ok = ok && (4 * s + g) < K / 32;
 #pragma unroll
@@ -189,49 +258,25 @@ __device__ __forceinline__ XFrag<WT, XT> cook_x(const XRaw<WT, XT>& r, bool ok, 
   return b;
 }
 
-template <int WT, int XT>
-__device__ __forceinline__ f32x4_t mma(const AFrag<WT>& a, const XFrag<WT, XT>& b, f32x4_t c) {
-  if constexpr (WT == DT_F32) {
+template <int F, int XT>
+__device__ __forceinline__ f32x4_t mma_ready(const AReady<F>& a, const XFrag<F, XT>& b, f32x4_t c) {
+  if constexpr (F == DT_F32) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) c = mfma_f32(__uint_as_float(a.v[m]), b.v[m], c);
-  } else if constexpr (WT == DT_BF16) {
+  } else if constexpr (F == DT_BF16) {
     if constexpr (XT == DT_BF16) c = mfma_bf16(a.v, b.v, c);
     else {
       c = mfma_bf16(a.v, b.hi, c);
       c = mfma_bf16(a.v, b.lo, c);
     }
-  } else {
-    u32x4_t fr[4];
-    q4_dequant_block(a.raw, a.d, fr);
+  } else if constexpr (F == DT_FP8) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) c = mfma_f16(fr[f], b.v[f], c);
-  }
-  return c;
-}
-
-// Q4_0 A fragments are dequantised once and used for every column tile.
-template <int WT>
-struct AReady { AFrag<WT> a; };
-template <>
-struct AReady<DT_Q4> { u32x4_t fr[4]; };
-
-template <int WT>
-__device__ __forceinline__ AReady<WT> prep_a(const AFrag<WT>& a) {
-  AReady<WT> r;
-  if constexpr (WT == DT_Q4) q4_dequant_block(a.raw, a.d, r.fr);
-  else r.a = a;
-  return r;
-}
-
-template <int WT, int XT>
-__device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT, XT>& b, f32x4_t c) {
-  if constexpr (WT == DT_Q4) {
+    for (int i = 0; i < 2; ++i) c = mma_ready<DT_BF16, XT>(AReady<DT_BF16>{a.v[i]}, b.p[i], c);
+  } else {
 #pragma unroll
     for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
-    return c;
-  } else {
-    return mma<WT, XT>(a.a, b, c);
   }
+  return c;
 }
 
 // Unroll depth: keep several 16-byte weight loads in flight per lane.
@@ -241,13 +286,16 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<WT>& a, const XFrag<WT
 #ifndef MOE_DN_UNROLL_BF16
 #define MOE_DN_UNROLL_BF16 4
 #endif
+// bf16 and fp8 load one 16-byte word per matrix and step, the others more.
 template <int WT, int NCT>
 struct Unroll {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 2 : 1);
+  static constexpr bool one_word = WT == DT_BF16 || WT == DT_FP8;
+  static constexpr int v = one_word ? (NCT == 1 ? MOE_GU_UNROLL_BF16 : 2) : (NCT == 1 ? 2 : 1);
 };
 template <int WT, int NCT>
 struct UnrollDown {
-  static constexpr int v = (WT == DT_BF16) ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 1) : (NCT == 1 ? 2 : 1);
+  static constexpr bool one_word = WT == DT_BF16 || WT == DT_FP8;
+  static constexpr int v = one_word ? (NCT == 1 ? MOE_DN_UNROLL_BF16 : 1) : (NCT == 1 ? 2 : 1);
 };
 
 // Steps [s0, s1) in groups of U with the weight loads of group i+1 issued
@@ -301,7 +349,7 @@ __device__ __forceinline__ void stream_steps(int s0, int s1, Load load, Body bod
 }
 
 template <int WT, int XT, int NCT>
-struct GUStep { AFrag<WT> g, u; XRaw<WT, XT> x[NCT]; };
+struct GUStep { AFrag<WT> g, u; XRaw<Fam<WT>::v, XT> x[NCT]; };
 
 
 // ------------------------------------------------------------- gate/up --
@@ -329,10 +377,19 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
     N = a.Is; bg = a.sg; bu = a.su; n_mat = a.S;
   }
   if (rt * 16 >= N) return;
+  constexpr int F = Fam<WT>::v;
   const int K = a.H, g = lane >> 4;
   RowPtr<WT> rg, ru;
   rg.init(bg, n_mat, N, K, e, rt * 16 + (lane & 15));
   ru.init(bu, n_mat, N, K, e, rt * 16 + (lane & 15));
+  // fp8: the row scales of this lane's output rows, fetched early and applied to the sums
+  f32x4_t sg_rows = {1.f, 1.f, 1.f, 1.f}, su_rows = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (WT == DT_FP8) {
+    if (wave == 0) {
+      sg_rows = fp8_row_scales(bg, n_mat, N, K, e, rt * 16 + (lane >> 4) * 4);
+      su_rows = fp8_row_scales(bu, n_mat, N, K, e, rt * 16 + (lane >> 4) * 4);
+    }
+  }
 
   constexpr int xb = XT == DT_F32 ? 4 : 2;
   const uint8_t* xrow[NCT];
@@ -361,18 +418,18 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       if (NCT == 1 || ct < nct) {
-        if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<WT, XT>(xrow[ct], s, g, K);
+        if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<F, XT>(xrow[ct], s, g, K);
       }
     return st;
   };
   auto body = [&](int s, const GUStep<WT, XT, NCT>& st) {
-    const AReady<WT> ag = prep_a<WT>(st.g), au = prep_a<WT>(st.u);
+    const AReady<F> ag = prep_a<WT>(st.g), au = prep_a<WT>(st.u);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (NCT == 1 || ct < nct) {
-        const XFrag<WT, XT> b = cook_x<WT, XT>(st.x[ct], xok[ct], s, g, K);
-        accg[ct] = mma_ready<WT, XT>(ag, b, accg[ct]);
-        accu[ct] = mma_ready<WT, XT>(au, b, accu[ct]);
+        const XFrag<F, XT> b = cook_x<F, XT>(st.x[ct], xok[ct], s, g, K);
+        accg[ct] = mma_ready<F, XT>(ag, b, accg[ct]);
+        accu[ct] = mma_ready<F, XT>(au, b, accu[ct]);
       }
     }
   };
@@ -399,11 +456,11 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
     const float wr = routed ? ld_f32<COH>(a.topk_w + ld_i32<COH>(a.sorted_ids + seg + c)) : 1.0f;
     float hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = silu_f(gs[i]) * us[i] * wr;
+    for (int i = 0; i < 4; ++i) hv[i] = silu_f(gs[i] * sg_rows[i]) * (us[i] * su_rows[i]) * wr;
     const size_t off = size_t(hrow0 + c) * a.h_stride + rt * 16 + (lane >> 4) * 4;
-    if constexpr (WT == DT_F32) {
+    if constexpr (F == DT_F32) {
       st_f32x4<COH>(reinterpret_cast<float*>(a.h) + off, f32x4_t{hv[0], hv[1], hv[2], hv[3]});
-    } else if constexpr (WT == DT_BF16) {
+    } else if constexpr (F == DT_BF16 || F == DT_FP8) {
       uint32_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]), h2 = f32_to_bf16(hv[2]), h3 = f32_to_bf16(hv[3]);
       float r0 = hv[0] - __uint_as_float(h0 << 16), r1 = hv[1] - __uint_as_float(h1 << 16);
       float r2 = hv[2] - __uint_as_float(h2 << 16), r3 = hv[3] - __uint_as_float(h3 << 16);
@@ -419,23 +476,33 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
 
 // ---------------------------------------------------------------- down --
 
-// B operand of the down projection: activation rows written by gate/up.
-template <int WT> struct HFrag;
+// B operand of the down projection: activation rows written by gate/up, in
+// the format of the weight family (fp32; bf16 hi + lo planes; fp16).
+template <int F> struct HFrag;
 template <> struct HFrag<DT_F32> { float v[4]; };
 template <> struct HFrag<DT_BF16> { u32x4_t hi, lo; };
 template <> struct HFrag<DT_Q4> { u32x4_t v[4]; };
+template <> struct HFrag<DT_FP8> { HFrag<DT_BF16> p[2]; };
 
-template <int WT>
-__device__ __forceinline__ HFrag<WT> load_h_raw(const DecodeArgs a, size_t row_off, int s, int g, int K) {
-  HFrag<WT> b;
-  if constexpr (WT == DT_F32) {
+__device__ __forceinline__ HFrag<DT_BF16> load_h8(const void* h, long h_plane, size_t row_off, int k0) {
+  const uint16_t* hp = reinterpret_cast<const uint16_t*>(h) + row_off + k0;
+  return HFrag<DT_BF16>{ldg16(hp), ldg16(hp + h_plane)};
+}
+
+template <int F>
+__device__ __forceinline__ HFrag<F> load_h_raw(const DecodeArgs a, size_t row_off, int s, int g, int K) {
+  HFrag<F> b;
+  if constexpr (F == DT_F32) {
     const u32x4_t t = ldg16(reinterpret_cast<const float*>(a.h) + row_off + s * 16 + g * 4);
 #pragma unroll
     for (int m = 0; m < 4; ++m) b.v[m] = __uint_as_float(t[m]);
-  } else if constexpr (WT == DT_BF16) {
-    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + s * 32 + g * 8;
-    b.hi = ldg16(hp);
-    b.lo = ldg16(hp + a.h_plane);
+  } else if constexpr (F == DT_BF16) {
+    b = load_h8(a.h, a.h_plane, row_off, s * 32 + g * 8);
+  } else if constexpr (F == DT_FP8) {
+    int k0 = s * 64 + g * 16;
+    k0 = k0 < K ? k0 : K - 16;
+    b.p[0] = load_h8(a.h, a.h_plane, row_off, k0);
+    b.p[1] = load_h8(a.h, a.h_plane, row_off, k0 + 8);
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
@@ -447,15 +514,22 @@ __device__ __forceinline__ HFrag<WT> load_h_raw(const DecodeArgs a, size_t row_o
   return b;
 }
 
-template <int WT>
-__device__ __forceinline__ HFrag<WT> cook_h(HFrag<WT> b, bool ok, int s, int g, int K) {
+template <int F>
+__device__ __forceinline__ HFrag<F> cook_h(HFrag<F> b, bool ok, int s, int g, int K) {
   const u32x4_t z = {0, 0, 0, 0};
-  if constexpr (WT == DT_F32) {
+  if constexpr (F == DT_F32) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) b.v[m] = ok ? b.v[m] : 0.f;
-  } else if constexpr (WT == DT_BF16) {
+  } else if constexpr (F == DT_BF16) {
     b.hi = ok ? b.hi : z;
     b.lo = ok ? b.lo : z;
+  } else if constexpr (F == DT_FP8) {
+    ok = ok && s * 64 + g * 16 < K;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      b.p[i].hi = ok ? b.p[i].hi : z;
+      b.p[i].lo = ok ? b.p[i].lo : z;
+    }
   } else {
     ok = ok && (4 * s + g) < K / 32;
 #pragma unroll
@@ -464,14 +538,20 @@ __device__ __forceinline__ HFrag<WT> cook_h(HFrag<WT> b, bool ok, int s, int g, 
   return b;
 }
 
-template <int WT>
-__device__ __forceinline__ f32x4_t mma_h(const AReady<WT>& a, const HFrag<WT>& b, f32x4_t c) {
-  if constexpr (WT == DT_F32) {
+template <int F>
+__device__ __forceinline__ f32x4_t mma_h(const AReady<F>& a, const HFrag<F>& b, f32x4_t c) {
+  if constexpr (F == DT_F32) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) c = mfma_f32(__uint_as_float(a.a.v[m]), b.v[m], c);
-  } else if constexpr (WT == DT_BF16) {
-    c = mfma_bf16(a.a.v, b.hi, c);
-    c = mfma_bf16(a.a.v, b.lo, c);
+    for (int m = 0; m < 4; ++m) c = mfma_f32(__uint_as_float(a.v[m]), b.v[m], c);
+  } else if constexpr (F == DT_BF16) {
+    c = mfma_bf16(a.v, b.hi, c);
+    c = mfma_bf16(a.v, b.lo, c);
+  } else if constexpr (F == DT_FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      c = mfma_bf16(a.v[i], b.p[i].hi, c);
+      c = mfma_bf16(a.v[i], b.p[i].lo, c);
+    }
   } else {
 #pragma unroll
     for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
@@ -480,7 +560,7 @@ __device__ __forceinline__ f32x4_t mma_h(const AReady<WT>& a, const HFrag<WT>& b
 }
 
 template <int WT, int NCT>
-struct DNStep { AFrag<WT> a; HFrag<WT> h[NCT]; };
+struct DNStep { AFrag<WT> a; HFrag<Fam<WT>::v> h[NCT]; };
 
 // One work-group: 16 hidden outputs (rows of the down projection) of one
 // expert slot, for every token of that slot.  Its 4 waves split the slot's
@@ -506,9 +586,14 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
     hrow0 = a.T * a.k + e * a.T;
     K = a.Is; base = a.sd; n_mat = a.S;
   }
+  constexpr int F = Fam<WT>::v;
   const int H = a.H, g = lane >> 4;
   RowPtr<WT> rw;
   rw.init(base, n_mat, H, K, e, rt * 16 + (lane & 15));
+  f32x4_t sd_rows = {1.f, 1.f, 1.f, 1.f};      // fp8: row scales of this lane's output rows
+  if constexpr (WT == DT_FP8) {
+    if (wave == 0) sd_rows = fp8_row_scales(base, n_mat, H, K, e, rt * 16 + (lane >> 4) * 4);
+  }
   size_t hoff[NCT];
   bool hok[NCT];
 #pragma unroll
@@ -531,15 +616,15 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       if (NCT == 1 || ct < nct) {
-        if (!MOE_DN_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<WT>(a, hoff[ct], s, g, K);
+        if (!MOE_DN_MASKED_B || hok[ct]) st.h[ct] = load_h_raw<F>(a, hoff[ct], s, g, K);
       }
     return st;
   };
   auto body = [&](int s, const DNStep<WT, NCT>& st) {
-    const AReady<WT> ar = prep_a<WT>(st.a);
+    const AReady<F> ar = prep_a<WT>(st.a);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      if (NCT == 1 || ct < nct) acc[ct] = mma_h<WT>(ar, cook_h<WT>(st.h[ct], hok[ct], s, g, K), acc[ct]);
+      if (NCT == 1 || ct < nct) acc[ct] = mma_h<F>(ar, cook_h<F>(st.h[ct], hok[ct], s, g, K), acc[ct]);
     }
   };
   stream_steps<U>(s0, s1, load, body);
@@ -557,7 +642,7 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
     const int c = ct * 16 + (lane & 15);
     if (c >= n_e) continue;
     // lane holds rows 4*(lane/16) + 0..3 of this tile for token column c
-    st_f32x4<COH>(a.partials + size_t(hrow0 + c) * H + rt * 16 + (lane >> 4) * 4, v);
+    st_f32x4<COH>(a.partials + size_t(hrow0 + c) * H + rt * 16 + (lane >> 4) * 4, v * sd_rows);
   }
 }
 

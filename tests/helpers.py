@@ -117,6 +117,16 @@ def expert_f64(t, key, wl, e, n_mat, N, K):
     a = t[key]
     if wl.w_dtype == "q4_0":
         return oracle.q4_0_decode_matrix(a.cpu().numpy(), n_mat, N, K, e)
+    if wl.w_dtype in ("q8_0", "fp8_e4m3"):
+        # one-byte codes [n_mat, N, K], then the scales from the next 256-byte boundary
+        off = (n_mat * N * K + 255) // 256 * 256
+        codes = a[e * N * K:(e + 1) * N * K].cpu().numpy().reshape(N, K)
+        if wl.w_dtype == "q8_0":
+            nb = N * (K // 32) * 2
+            d = a[off + e * nb:off + (e + 1) * nb].cpu().numpy().view(np.uint16).reshape(N, K // 32)
+            return oracle.q8_0_matrix(codes, d)
+        s = a[off + e * N * 4:off + (e + 1) * N * 4].cpu().numpy().view(np.float32)
+        return oracle.fp8_e4m3_matrix(codes, s)
     return to_f64(a[e])
 
 

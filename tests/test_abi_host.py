@@ -55,6 +55,8 @@ def test_strerror(m):
     (dict(w_dtype=5), "MOE_ERR_DTYPE"),
     (dict(w_dtype=2, path=2), "MOE_ERR_DTYPE"),  # prefill needs bf16 experts
     (dict(path=4), "MOE_ERR_SHAPE"),
+    (dict(w_dtype=3, path=2), "MOE_ERR_DTYPE"),   # the 8-bit weight types run the decode path only
+    (dict(w_dtype=4, path=3), "MOE_ERR_DTYPE"),
     (dict(path=3, router_dtype=0), "MOE_ERR_DTYPE"),   # single-launch decode: router dtype == x dtype
     (dict(path=3, E=32, top_k=17), "MOE_ERR_SHAPE"),    # single-launch decode: top_k <= 16
 ])

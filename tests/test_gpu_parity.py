@@ -44,6 +44,16 @@ SMALL = {
     "n10k_prefill": W("n10k_prefill", T=5000, H=64, E=8, k=2, I=32),
     # 33..64 experts (one DPP row per token) with k > 8 and a ragged expert count
     "e40_k10": W("e40_k10", T=37, H=96, E=40, k=10, I=64),
+    # 8-bit expert weights: Q8_0 blocks with a partly filled last step (9 and 5 blocks per row),
+    # fp8 rows whose length is 32 past a multiple of 64 (a half-filled last step)
+    "q8_small_t5": W("q8_small_t5", T=5, H=288, E=64, k=8, I=160, S=1, Is=96,
+                     x_dtype="f32", w_dtype="q8_0", r_dtype="f32"),
+    "q8_bf16x_t40": W("q8_bf16x_t40", T=40, H=256, E=16, k=6, I=96, S=2, Is=160, w_dtype="q8_0"),
+    "q8_f32_t70": W("q8_f32_t70", T=70, H=128, E=8, k=2, I=64, x_dtype="f32", w_dtype="q8_0", r_dtype="f32"),
+    "fp8_small_t8": W("fp8_small_t8", T=8, H=512, E=8, k=2, I=1024, w_dtype="fp8_e4m3"),
+    "fp8_tails_t40": W("fp8_tails_t40", T=40, H=352, E=16, k=6, I=96, S=2, Is=160, w_dtype="fp8_e4m3"),
+    "fp8_f32x_t3": W("fp8_f32x_t3", T=3, H=96, E=5, k=2, I=64, x_dtype="f32", w_dtype="fp8_e4m3",
+                     r_dtype="f32"),
 }
 BF16_BOTH_PATHS = ["mixtral_small_bf16", "deepseek_small_t8", "deepseek_small_t40", "prefill_small_zipf",
                    "k_equals_E", "t1_k1"]
@@ -102,7 +112,7 @@ def test_forward_forced_paths(m, name, path):
 
 
 def _fused_ok(wl):
-    return wl.r_dtype == wl.x_dtype and wl.k <= 16
+    return wl.r_dtype == wl.x_dtype and wl.k <= 16 and wl.w_dtype in ("f32", "bf16", "q4_0")
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
@@ -205,7 +215,7 @@ def test_workspace_needs_no_initialisation(m):
 # -------------------------------------------------------------- full size ----
 
 FULL = ["mixtral_decode_t8", "qwen_a3b_decode_q4", "deepseek16b_decode_t8", "deepseek16b_decode_t64",
-        "mixtral_prefill_t4096"]
+        "mixtral_prefill_t4096", "mixtral_decode_t8_fp8", "qwen_a3b_decode_q8"]
 
 
 @pytest.fixture(scope="module")
@@ -258,7 +268,7 @@ def test_full_size_forward_sampled(m, full_inputs, name):
     assert err <= 1e-2, err
 
 
-@pytest.mark.parametrize("name", [n for n in FULL if "decode" in n])
+@pytest.mark.parametrize("name", [n for n in FULL if "decode" in n and _fused_ok(synth.WORKLOADS[n])])
 def test_full_size_decode_paths_agree(m, full_inputs, name):
     """At the benchmarked sizes the single-launch and multi-launch decode give
     the same bits."""
