@@ -98,7 +98,7 @@ def act_bytes(dt):
 
 def h_elem_bytes(wl):
     """Bytes per element of the activation rows between the decode launches."""
-    return 2 if wl.w_dtype in ("q4_0", "q8_0") else 4
+    return 4 if wl.w_dtype in ("f32", "bf16") else 2
 
 
 def layer_bytes(wl):

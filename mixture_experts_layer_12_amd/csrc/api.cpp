@@ -132,8 +132,8 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     L.h_stride = int(roundup(L.h_stride, kHRowAlign));
     const long rows = long(Tr) * k + long(S) * Tr;
     L.h_plane = rows * L.h_stride;
-    // fp16 (Q4_0, Q8_0) | fp32 | bf16 hi + lo planes (bf16, fp8)
-    const size_t elem = (s->w_dtype == MOE_Q4_0 || s->w_dtype == MOE_Q8_0) ? 2 : 4;
+    // fp16 (Q4_0, Q8_0, fp8) | fp32 | bf16 hi + lo planes
+    const size_t elem = (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16) ? 4 : 2;
     L.h = take(size_t(L.h_plane) * elem);
     L.partials = take(size_t(rows) * H * 4);
     if (L.path == MOE_PATH_DECODE_FUSED) {

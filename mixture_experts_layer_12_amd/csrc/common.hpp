@@ -145,19 +145,18 @@ __device__ __forceinline__ void q8_dequant_block(u32x4_t raw0, u32x4_t raw1, uin
 }
 
 // ------------------------------------------------------------ fp8 E4M3 --
-// 16 E4M3 codes -> two bf16x8 operands (codes 0..7, 8..15).  The hardware
+// 16 E4M3 codes -> two fp16x8 operands (codes 0..7, 8..15).  The hardware
 // conversion reads the OCP E4M3 encoding on this architecture; every E4M3
-// value is exact in bf16, and the scale 1.0 leaves it unchanged.
+// value (at most 448, at least 2^-9 in magnitude) is exact in fp16, and the
+// scale 1.0 leaves it unchanged.
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void fp8x16_to_bf16(u32x4_t raw, u32x4_t out[2]) {
+__device__ __forceinline__ void fp8x16_to_f16(u32x4_t raw, u32x4_t out[2]) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     out[w >> 1][2 * (w & 1) + 0] =
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(raw[w]), 1.0f, false));
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(raw[w]), 1.0f, false));
     out[w >> 1][2 * (w & 1) + 1] =
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(raw[w]), 1.0f, true));
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(raw[w]), 1.0f, true));
   }
 }
 

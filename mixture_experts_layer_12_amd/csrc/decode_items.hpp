@@ -43,7 +43,8 @@ namespace moe {
 // Operand family of a stored weight type: the MFMA it feeds, the activation
 // (B operand) layout and the format of the activation rows between gate/up
 // and down.  Q8_0 shares Q4_0's (one 32-value block per lane group, fp16);
-// fp8 has its own (16 codes per lane group, two bf16 k-slices of 8).
+// fp8 has its own (16 codes per lane group, two fp16 k-slices of 8, fp16
+// activation rows).
 template <int WT> struct Fam { static constexpr int v = WT; };
 template <> struct Fam<DT_Q8> { static constexpr int v = DT_Q4; };
 
@@ -121,7 +122,7 @@ template <int F> struct AReady;
 template <> struct AReady<DT_F32> { u32x4_t v; };
 template <> struct AReady<DT_BF16> { u32x4_t v; };
 template <> struct AReady<DT_Q4> { u32x4_t fr[4]; };
-template <> struct AReady<DT_FP8> { u32x4_t v[2]; };
+template <> struct AReady<DT_FP8> { u32x4_t v[2]; };       // fp16x8 each
 
 template <int WT>
 __device__ __forceinline__ AReady<Fam<WT>::v> prep_a(const AFrag<WT>& a) {
@@ -129,7 +130,7 @@ __device__ __forceinline__ AReady<Fam<WT>::v> prep_a(const AFrag<WT>& a) {
   if constexpr (WT == DT_F32 || WT == DT_BF16) r.v = a.v;
   else if constexpr (WT == DT_Q4) q4_dequant_block(a.raw, a.d, r.fr);
   else if constexpr (WT == DT_Q8) q8_dequant_block(a.raw0, a.raw1, a.d, r.fr);
-  else fp8x16_to_bf16(a.ok ? a.raw : u32x4_t{0, 0, 0, 0}, r.v);
+  else fp8x16_to_f16(a.ok ? a.raw : u32x4_t{0, 0, 0, 0}, r.v);
   return r;
 }
 
@@ -142,7 +143,7 @@ template <int XT> struct XFrag<DT_F32, XT> { float v[4]; };
 template <> struct XFrag<DT_BF16, DT_BF16> { u32x4_t v; };
 template <> struct XFrag<DT_BF16, DT_F32> { u32x4_t hi, lo; };
 template <int XT> struct XFrag<DT_Q4, XT> { u32x4_t v[4]; };
-template <int XT> struct XFrag<DT_FP8, XT> { XFrag<DT_BF16, XT> p[2]; };
+template <int XT> struct XFrag<DT_FP8, XT> { u32x4_t v[2]; };       // fp16x8 each
 
 // Raw activation words of one step, loaded with the step's weights and only
 // turned into MFMA operands (cook_x) when the step is computed, so that no
@@ -154,7 +155,8 @@ template <> struct XRaw<DT_BF16, DT_BF16> { u32x4_t t; };
 template <> struct XRaw<DT_BF16, DT_F32> { u32x4_t t0, t1; };
 template <> struct XRaw<DT_Q4, DT_F32> { u32x4_t t[8]; };
 template <> struct XRaw<DT_Q4, DT_BF16> { u32x4_t t[4]; };
-template <int XT> struct XRaw<DT_FP8, XT> { XRaw<DT_BF16, XT> p[2]; };
+template <> struct XRaw<DT_FP8, DT_F32> { u32x4_t t[4]; };
+template <> struct XRaw<DT_FP8, DT_BF16> { u32x4_t t[2]; };
 
 // 8 activations from k0 as one bf16-family operand.
 template <int XT>
@@ -182,8 +184,14 @@ __device__ __forceinline__ XRaw<F, XT> load_x_raw(const uint8_t* xrow, int s, in
   } else if constexpr (F == DT_FP8) {
     int k0 = s * 64 + g * 16;
     k0 = k0 < K ? k0 : K - 16;
-    r.p[0] = load_x8<XT>(xrow, k0);
-    r.p[1] = load_x8<XT>(xrow, k0 + 8);
+    if constexpr (XT == DT_F32) {
+      const float* xp = reinterpret_cast<const float*>(xrow) + k0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r.t[q] = ldg16(xp + 4 * q);
+    } else {
+      r.t[0] = ldg16(xrow + size_t(k0) * 2);
+      r.t[1] = ldg16(xrow + size_t(k0 + 8) * 2);
+    }
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
@@ -236,8 +244,20 @@ __device__ __forceinline__ XFrag<F, XT> cook_x(const XRaw<F, XT>& r, bool ok, in
     b = cook_x8<XT>(r, ok);
   } else if constexpr (F == DT_FP8) {
     ok = ok && s * 64 + g * 16 < K;
-    b.p[0] = cook_x8<XT>(r.p[0], ok);
-    b.p[1] = cook_x8<XT>(r.p[1], ok);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (XT == DT_F32) {
+        const u32x4_t t0 = r.t[2 * i], t1 = r.t[2 * i + 1];
+        b.v[i][0] = pack_f16(__uint_as_float(t0[0]), __uint_as_float(t0[1]));
+        b.v[i][1] = pack_f16(__uint_as_float(t0[2]), __uint_as_float(t0[3]));
+        b.v[i][2] = pack_f16(__uint_as_float(t1[0]), __uint_as_float(t1[1]));
+        b.v[i][3] = pack_f16(__uint_as_float(t1[2]), __uint_as_float(t1[3]));
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) b.v[i][m] = bf16x2_to_f16x2(r.t[i][m]);
+      }
+      if (!ok) b.v[i] = u32x4_t{0, 0, 0, 0};
+    }
   } else {
     ok = ok && (4 * s + g) < K / 32;
 #pragma unroll
@@ -271,7 +291,7 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<F>& a, const XFrag<F, 
     }
   } else if constexpr (F == DT_FP8) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) c = mma_ready<DT_BF16, XT>(AReady<DT_BF16>{a.v[i]}, b.p[i], c);
+    for (int i = 0; i < 2; ++i) c = mfma_f16(a.v[i], b.v[i], c);
   } else {
 #pragma unroll
     for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
@@ -460,7 +480,7 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
     const size_t off = size_t(hrow0 + c) * a.h_stride + rt * 16 + (lane >> 4) * 4;
     if constexpr (F == DT_F32) {
       st_f32x4<COH>(reinterpret_cast<float*>(a.h) + off, f32x4_t{hv[0], hv[1], hv[2], hv[3]});
-    } else if constexpr (F == DT_BF16 || F == DT_FP8) {
+    } else if constexpr (F == DT_BF16) {
       uint32_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]), h2 = f32_to_bf16(hv[2]), h3 = f32_to_bf16(hv[3]);
       float r0 = hv[0] - __uint_as_float(h0 << 16), r1 = hv[1] - __uint_as_float(h1 << 16);
       float r2 = hv[2] - __uint_as_float(h2 << 16), r3 = hv[3] - __uint_as_float(h3 << 16);
@@ -477,12 +497,13 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
 // ---------------------------------------------------------------- down --
 
 // B operand of the down projection: activation rows written by gate/up, in
-// the format of the weight family (fp32; bf16 hi + lo planes; fp16).
+// the format of the weight family (fp32; bf16 hi + lo planes; fp16 for the
+// Q4_0 / Q8_0 and the fp8 families).
 template <int F> struct HFrag;
 template <> struct HFrag<DT_F32> { float v[4]; };
 template <> struct HFrag<DT_BF16> { u32x4_t hi, lo; };
 template <> struct HFrag<DT_Q4> { u32x4_t v[4]; };
-template <> struct HFrag<DT_FP8> { HFrag<DT_BF16> p[2]; };
+template <> struct HFrag<DT_FP8> { u32x4_t v[2]; };
 
 __device__ __forceinline__ HFrag<DT_BF16> load_h8(const void* h, long h_plane, size_t row_off, int k0) {
   const uint16_t* hp = reinterpret_cast<const uint16_t*>(h) + row_off + k0;
@@ -501,8 +522,9 @@ __device__ __forceinline__ HFrag<F> load_h_raw(const DecodeArgs a, size_t row_of
   } else if constexpr (F == DT_FP8) {
     int k0 = s * 64 + g * 16;
     k0 = k0 < K ? k0 : K - 16;
-    b.p[0] = load_h8(a.h, a.h_plane, row_off, k0);
-    b.p[1] = load_h8(a.h, a.h_plane, row_off, k0 + 8);
+    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.h) + row_off + k0;
+    b.v[0] = ldg16(hp);
+    b.v[1] = ldg16(hp + 8);
   } else {
     const int nblk = K / 32;
     int blk = 4 * s + g;
@@ -525,11 +547,8 @@ __device__ __forceinline__ HFrag<F> cook_h(HFrag<F> b, bool ok, int s, int g, in
     b.lo = ok ? b.lo : z;
   } else if constexpr (F == DT_FP8) {
     ok = ok && s * 64 + g * 16 < K;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      b.p[i].hi = ok ? b.p[i].hi : z;
-      b.p[i].lo = ok ? b.p[i].lo : z;
-    }
+    b.v[0] = ok ? b.v[0] : z;
+    b.v[1] = ok ? b.v[1] : z;
   } else {
     ok = ok && (4 * s + g) < K / 32;
 #pragma unroll
@@ -547,11 +566,8 @@ __device__ __forceinline__ f32x4_t mma_h(const AReady<F>& a, const HFrag<F>& b, 
     c = mfma_bf16(a.v, b.hi, c);
     c = mfma_bf16(a.v, b.lo, c);
   } else if constexpr (F == DT_FP8) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      c = mfma_bf16(a.v[i], b.p[i].hi, c);
-      c = mfma_bf16(a.v[i], b.p[i].lo, c);
-    }
+    c = mfma_f16(a.v[0], b.v[0], c);
+    c = mfma_f16(a.v[1], b.v[1], c);
   } else {
 #pragma unroll
     for (int f = 0; f < 4; ++f) c = mfma_f16(a.fr[f], b.v[f], c);
