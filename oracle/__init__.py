@@ -27,13 +27,15 @@ weight 1; optional router bias added to the logits.
 
 Modules:
   formats -- decoding of the stored input formats (bf16, fp16, Q4_0, Q8_0, fp8 E4M3)
-  moe     -- vectorised fp64 reference (numpy)
+  moe     -- vectorised fp64 reference (numpy), including the budgeted
+             channel-sparse experts
   loops   -- pure-Python brute force for tiny shapes
 """
 from . import formats, moe, loops  # noqa: F401
 from .moe import (  # noqa: F401
     router_logits, softmax, select_topk, renormalize, route, near_ties,
     silu, swiglu_ffn, moe_forward, moe_forward_tokens, dispatch, dense_gate_matrix,
+    select_channels, masked_swiglu, moe_forward_channel_sparse,
 )
 from .formats import (  # noqa: F401
     bf16_to_f64, f16_to_f64, q4_0_decode, q4_0_decode_matrix, q8_0_decode, q8_0_matrix, fp8_e4m3_to_f64,

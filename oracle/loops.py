@@ -98,3 +98,18 @@ def dispatch(ids, E, M):
     active = [e for e in range(E) if counts[e] > 0]
     return dict(counts=counts, offsets=offsets, sorted_ids=sorted_ids,
                 tile_expert=tile_expert, inv=inv, active=active, capacity=cap)
+
+
+def sparse_ffn_one(x, Wg, Wu, Wd, scores, c):
+    """Brute force: rank channels by score (higher first, equal scores by
+    lower index), keep the first c, and sum their contributions one by one."""
+    I = len(Wg)
+    ranked = sorted(range(I), key=lambda i: (-scores[i], i))[:c]
+    y = [0.0] * len(x)
+    for i in ranked:
+        g = _dot(Wg[i], x)
+        u = _dot(Wu[i], x)
+        a = g / (1.0 + math.exp(-g)) * u
+        for h in range(len(x)):
+            y[h] += Wd[h][i] * a
+    return y

@@ -68,6 +68,7 @@ class Workload:
     w_dtype: str = BF16
     r_dtype: str = BF16
     zipf_s: Optional[float] = None   # router bias ln p_e, p_e ~ (e+1)^-s
+    channel_budget: Optional[float] = None   # channel-sparse experts: share of channels kept
     w_std: float = 0.02
     q4_d_std: float = 0.002
 
@@ -90,6 +91,8 @@ WORKLOADS = {
         Workload("mixtral_decode_t8_fp8", T=8, H=4096, E=8, k=2, I=14336, w_dtype=FP8),
         Workload("qwen_a3b_decode_q8", T=1, H=2048, E=256, k=8, I=512, S=1, Is=512,
                  x_dtype=F32, w_dtype=Q8_0, r_dtype=F32),
+        # batch one with budgeted channel sparsity (17.8 % of each engaged expert's channels)
+        Workload("mixtral_decode_t1_sparse", T=1, H=4096, E=8, k=2, I=14336, channel_budget=0.178),
     ]
 }
 
@@ -168,6 +171,25 @@ def pack_weights(w: np.ndarray, dtype: str) -> np.ndarray:
     else:
         raise ValueError(dtype)
     return buf
+
+
+def channel_count(w: Workload) -> int:
+    """Channels kept per (token, engaged expert) for a channel-sparse workload."""
+    return max(1, min(w.I, int(round(w.channel_budget * w.I))))
+
+
+def channel_scores(w: Workload, seed: int) -> np.ndarray:
+    """Per-token channel scores [T, E, I] (float32, N(0, 1)), from their own
+    stream so that the other inputs of the same seed do not change.  They stand
+    in for a selector's scores (the selector itself is not modelled)."""
+    rng = np.random.default_rng([seed, 0x5C0E])
+    return rng.standard_normal(size=(w.T, w.E, w.I), dtype=np.float32)
+
+
+def down_transposed(a: np.ndarray, n: int, H: int, inter: int) -> np.ndarray:
+    """A dense down stack [n, H, inter] (float32 or bf16 bits) laid out as
+    [n, inter, H], so that one intermediate channel is one contiguous row."""
+    return np.ascontiguousarray(np.asarray(a).reshape(n, H, inter).transpose(0, 2, 1))
 
 
 def zipf_bias(E: int, s: float) -> np.ndarray:
