@@ -126,6 +126,18 @@ def layer_alg_bytes(wl, n_active, T):
             + wl.E * wl.H * act_bytes(wl.r_dtype) + T * wl.H * 2 * act_bytes(wl.x_dtype))
 
 
+def sparse_layer_alg_bytes(wl, T):
+    """Channel-sparse layer: the kept rows of gate, up and (transposed) down of
+    each engaged expert, the routed experts' channel scores, the dense shared
+    experts, the router, and x / out."""
+    import synth
+    c = synth.channel_count(wl)
+    row = mat_bytes(wl.w_dtype, 1, wl.H)
+    return (T * wl.k * (3 * c * row + wl.I * 4)
+            + wl.S * (2 * mat_bytes(wl.w_dtype, wl.Is, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.Is))
+            + wl.E * wl.H * act_bytes(wl.r_dtype) + T * wl.H * 2 * act_bytes(wl.x_dtype))
+
+
 def gateup_flops(wl):
     return 2.0 * (wl.T * wl.k * 2 * wl.I * wl.H + wl.T * wl.S * 2 * wl.Is * wl.H)
 
@@ -220,6 +232,83 @@ def cpu_baseline(wl, t, tokens_max=16, min_seconds=5.0):
             "host_cpus": os.cpu_count()}
 
 
+# ------------------------------------------------------- channel-sparse -----
+
+def bench_sparse(args, m, wl, inp, copies, dev):
+    """The budgeted channel-sparse layer (moe_forward_channel_sparse): per-copy
+    channel scores and transposed down stacks, whole-layer timing."""
+    import torch
+    c = synth.channel_count(wl)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 1)
+    scores = [torch.randn((wl.T, wl.E, wl.I), generator=gen, device=dev) for _ in range(copies)]
+    wdt = [w.transpose(1, 2).contiguous() for w in inp["w_down"]]
+    shape = m.make_shape(wl.T, wl.H, wl.E, wl.I, wl.k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype)
+    ws = m.alloc_sparse_workspace(shape, c, dev)
+    out = torch.empty_like(inp["x"][0])
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        j = i % copies
+        m.moe_forward_channel_sparse(shape, c, scores[j], inp["x"][j], inp["router_w"][j], inp["router_b"][j],
+                                     inp["w_gate"][j], inp["w_up"][j], wdt[j], inp["ws_gate"][j], inp["ws_up"][j],
+                                     inp["ws_down"][j], out, ws, stream=sh)
+
+    for i in range(max(args.warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = wl.T * args.steps / elapsed
+    alg = sparse_layer_alg_bytes(wl, wl.T)
+    achieved = alg / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] sparse c={c} of I={wl.I}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s, {achieved:.0f} GB/s")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "layer (all launches of one call)",
+            "launch_ms": round(ms_per_step, 5), "alg_bytes_per_launch": int(alg), "channels_kept": c}
+    cpu = None
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        x = inp["x"][0].float().cpu().numpy().astype(np.float64)
+        Wr = inp["router_w"][0].float().cpu().numpy().astype(np.float64)
+        sc = scores[0].cpu().numpy().astype(np.float64)
+        t_start = time.perf_counter()
+        n = 0
+        while True:
+            l, p, ids, w = oracle.route(x, Wr, None, wl.k)
+            for t in range(wl.T):
+                for j in range(wl.k):
+                    e = int(ids[t, j])
+                    Wg = inp["w_gate"][0][e].float().cpu().numpy().astype(np.float64)
+                    Wu = inp["w_up"][0][e].float().cpu().numpy().astype(np.float64)
+                    Wd = inp["w_down"][0][e].float().cpu().numpy().astype(np.float64)
+                    oracle.masked_swiglu(x[t:t + 1], Wg, Wu, Wd, oracle.select_channels(sc[t, e], c))
+            n += 1
+            if time.perf_counter() - t_start > 5.0:
+                break
+        el = time.perf_counter() - t_start
+        cpu = {"value": wl.T * n / el, "unit": "tokens/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"{n} calls of the whole batch ({wl.T} token(s)), fp64 numpy oracle including decoding the "
+                         f"engaged experts' weights; {el:.1f} s"}
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.w_dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "top_k": wl.k, "I": wl.I,
+                   "n_shared": wl.S, "I_shared": wl.Is, "weights": wl.w_dtype, "activations": wl.x_dtype,
+                   "router": wl.r_dtype, "path": "channel_sparse", "channels_kept": c, "weight_copies": copies,
+                   "timing": "eager launches", "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 # ------------------------------------------------------------------ main ----
 
 def main():
@@ -267,6 +356,8 @@ def main():
     inp = synth.make_inputs_torch(wl, args.seed, device=dev, copies=copies)
     if copies == 1:
         inp = {k: [v] for k, v in inp.items()}
+    if wl.channel_budget is not None:
+        return bench_sparse(args, m, wl, inp, copies, dev)
     path_arg = {"auto": m.MOE_PATH_AUTO, "decode": m.MOE_PATH_DECODE, "fused": m.MOE_PATH_DECODE_FUSED,
                 "prefill": m.MOE_PATH_PREFILL}[args.path]
     shape = m.make_shape(wl.T, wl.H, wl.E, wl.I, wl.k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype, path_arg)

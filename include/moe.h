@@ -188,6 +188,34 @@ int moe_forward_profiled(const moe_shape_t* s, const void* x, const void* router
                          void* out, void* workspace, size_t ws_bytes, void* stream,
                          void* const* events /* host array of hipEvent_t */, int n_events);
 
+/*
+ * Budgeted channel-sparse routed experts ("KAIST removed calibration from MoE
+ * decoding and sped up blocks up to 2.69x over vLLM", news.hamidun.com,
+ * sections "A threshold promises a budget but does not keep it" and "Top-k
+ * instead of a threshold"): for every token and each of its top_k experts,
+ * only the `budget` intermediate channels with the highest scores are used --
+ * rows of that expert's gate and up matrices and the matching columns of its
+ * down matrix -- so the bytes read per token are fixed in advance.  Equal
+ * scores keep the lower channel index; NaN scores rank below every number.
+ * Routing, renormalisation and the shared experts are as in moe_forward
+ * (shared experts stay dense).  The scorer is the caller's.
+ *
+ *   channel_scores f32 [T, E, I]: score of channel i of expert e for token t
+ *   budget         channels kept per (token, engaged expert), 1 <= budget <= I
+ *   w_down_t       routed down stack transposed: [E, I, H] (row i = channel i)
+ *   ws_down        shared down stack as in moe_forward: [n_shared, H, I_shared]
+ * Requirements: w_dtype MOE_F32 or MOE_BF16; I <= 16384; `path` is ignored
+ * (the decode kernels run the routing and the shared experts, in passes of
+ * at most 64 tokens).  Workspace: moe_sparse_workspace_size bytes, no initial
+ * contents required.  Errors as moe_forward.
+ */
+int moe_sparse_workspace_size(const moe_shape_t* s, int32_t budget, size_t* bytes /* host */);
+int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float* channel_scores,
+                               const void* x, const void* router_w, const float* router_b,
+                               const void* w_gate, const void* w_up, const void* w_down_t,
+                               const void* ws_gate, const void* ws_up, const void* ws_down,
+                               void* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* The hipError_t value behind the most recent MOE_ERR_HIP returned to the
  * calling thread (0 if there was none).  Host call. */
 int moe_last_hip_error(void);

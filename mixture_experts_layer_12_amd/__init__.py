@@ -25,7 +25,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
-            "moe_last_hip_error", "moe_strerror", "moe_resolve_path")
+            "moe_last_hip_error", "moe_strerror", "moe_resolve_path", "moe_sparse_workspace_size",
+            "moe_forward_channel_sparse")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -73,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_profiled.restype = ctypes.c_int
     lib.moe_last_hip_error.argtypes = []
     lib.moe_last_hip_error.restype = ctypes.c_int
+    lib.moe_sparse_workspace_size.argtypes = [P(moe_shape_t), i32, P(sz)]
+    lib.moe_sparse_workspace_size.restype = ctypes.c_int
+    lib.moe_forward_channel_sparse.argtypes = [P(moe_shape_t), i32] + [vp] * 12 + [sz, vp]
+    lib.moe_forward_channel_sparse.restype = ctypes.c_int
     lib.moe_resolve_path.argtypes = [P(moe_shape_t)]
     lib.moe_resolve_path.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
@@ -126,6 +131,27 @@ def hip_error_name(err: int) -> str:
         return f"hipError {err} ({hip.hipGetErrorName(err).decode()})"
     except OSError:
         return f"hipError {err}"
+
+
+def moe_sparse_workspace_size(shape: moe_shape_t, budget: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_sparse_workspace_size(ctypes.byref(shape), int(budget), ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_sparse_workspace_size")
+    return n.value
+
+
+def moe_forward_channel_sparse(shape: moe_shape_t, budget: int, channel_scores, x, router_w, router_b, w_gate, w_up,
+                               w_down_t, ws_gate, ws_up, ws_down, out, workspace, ws_bytes=None, stream=None,
+                               check=True) -> int:
+    nb = _nbytes(workspace) if ws_bytes is None else ws_bytes
+    rc = load_library().moe_forward_channel_sparse(
+        ctypes.byref(shape), int(budget), _ptr(channel_scores), _ptr(x), _ptr(router_w), _ptr(router_b),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out),
+        _ptr(workspace), nb, _stream(stream))
+    if check and rc:
+        raise MoeError(rc, "moe_forward_channel_sparse")
+    return rc
 
 
 def moe_resolve_path(shape: moe_shape_t) -> int:
@@ -188,6 +214,12 @@ def moe_forward_profiled(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up
     if check and rc:
         raise MoeError(rc, "moe_forward_profiled")
     return rc
+
+
+def alloc_sparse_workspace(shape: moe_shape_t, budget: int, device="cuda"):
+    """A workspace of moe_sparse_workspace_size(shape, budget) bytes (contents irrelevant)."""
+    import torch
+    return torch.empty(max(moe_sparse_workspace_size(shape, budget), 256), dtype=torch.uint8, device=device)
 
 
 def alloc_workspace(shape: moe_shape_t, device="cuda"):

@@ -9,7 +9,8 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/api.cpp", "csrc/router.hip", "csrc/decode.hip", "csrc/decode_fused.hip", "csrc/prefill.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/router.hip", "csrc/decode.hip", "csrc/decode_fused.hip", "csrc/sparse.hip",
+           "csrc/prefill.hip"]
 HEADERS = ["csrc/common.hpp", "csrc/router_items.hpp", "csrc/decode_items.hpp", "../include/moe.h"]
 OUT = os.path.join(HERE, "lib", "libmoe.so")
 

@@ -20,6 +20,7 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_til
                          StageMarker* mark);
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
 hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t st);
+hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, StageMarker* mark);
 }  // namespace moe
 
 namespace {
@@ -395,7 +396,121 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
   return MOE_OK;
 }
 
+// ------------------------------------------------ channel-sparse experts --
+
+constexpr int kSparseMaxI = 16384;   // the channel selection keeps one expert's scores in LDS
+
+int sparse_check(const moe_shape_t* s, int budget) {
+  if (int rc = check_shape(s)) return rc;
+  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (budget < 1 || budget > s->I || s->I > kSparseMaxI) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// Splits of the kept channels in the down projection for a pass of Tc tokens:
+// enough work-groups to fill the chip, few enough that the partial rows stay
+// near a tenth of the weight bytes, and each split small enough for LDS.
+int sparse_splits(const moe_shape_t* s, int Tc, int c) {
+  const int ctiles = (s->H + 2047) / 2048, n = Tc * s->top_k;
+  int R = std::min(std::max(1, c / 40), std::max(1, (1024 + ctiles * n - 1) / (ctiles * n)));
+  return std::max(R, (c + moe::kSparseMaxRows - 1) / moe::kSparseMaxRows);
+}
+
+struct SparseLayout {
+  Layout L;            // routing, and h / partials of the shared experts (decode layout)
+  size_t sel, hs, spart, total;
+};
+
+SparseLayout make_sparse_layout(const moe_shape_t* s0, int c) {
+  moe_shape_t s = *s0;
+  s.path = MOE_PATH_DECODE;
+  SparseLayout S{};
+  S.L = make_layout(&s, false);
+  const int Tr = std::max(S.L.Tr, 1);
+  size_t off = S.L.total;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  S.sel = take(size_t(Tr) * s.top_k * c * 4);
+  S.hs = take(size_t(Tr) * s.top_k * c * 4);
+  size_t rows = 0;
+  for (int Tc = 1; Tc <= Tr; ++Tc) rows = std::max(rows, size_t(Tc) * s.top_k * sparse_splits(&s, Tc, c));
+  S.spart = take(rows * s.H * 4);
+  S.total = off;
+  return S;
+}
+
 }  // namespace
+
+extern "C" {
+
+int moe_sparse_workspace_size(const moe_shape_t* s, int32_t budget, size_t* bytes) {
+  if (!s || !bytes) return MOE_ERR_NULL;
+  if (int rc = sparse_check(s, budget)) return rc;
+  *bytes = make_sparse_layout(s, budget).total;
+  return MOE_OK;
+}
+
+int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float* channel_scores,
+                               const void* x, const void* router_w, const float* router_b,
+                               const void* w_gate, const void* w_up, const void* w_down_t,
+                               const void* ws_gate, const void* ws_up, const void* ws_down,
+                               void* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!s) return MOE_ERR_NULL;
+  if (int rc = sparse_check(s, budget)) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!channel_scores || !x || !router_w || !w_gate || !w_up || !w_down_t || !out || !workspace) return MOE_ERR_NULL;
+  const bool has_shared = s->n_shared > 0;
+  if (has_shared != (ws_gate != nullptr) || has_shared != (ws_up != nullptr) || has_shared != (ws_down != nullptr))
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {channel_scores, x, router_w, router_b, w_gate, w_up, w_down_t, ws_gate, ws_up, ws_down,
+                        out, workspace};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return MOE_ERR_ALIGN;
+  const SparseLayout SL = make_sparse_layout(s, budget);
+  if (ws_bytes < SL.total) return MOE_ERR_WORKSPACE;
+  const Layout& L = SL.L;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int xb = s->x_dtype == MOE_F32 ? 4 : 2;
+  const moe::RouteBufs rb = route_bufs(ws, L);
+  for (int t0 = 0; t0 < s->T; t0 += kDecodeMaxT) {
+    const int Tc = std::min(kDecodeMaxT, s->T - t0);
+    const uint8_t* xc = static_cast<const uint8_t*>(x) + size_t(t0) * s->H * xb;
+    moe::RouteBufs rbd = rb;
+    rbd.tile_expert = nullptr;
+    moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rbd, 1);
+    const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
+    moe::SparseArgs a{};
+    moe::DecodeArgs& d = a.d;
+    d.x = xc;
+    d.wg = static_cast<const uint8_t*>(w_gate); d.wu = static_cast<const uint8_t*>(w_up);
+    d.sg = static_cast<const uint8_t*>(ws_gate); d.su = static_cast<const uint8_t*>(ws_up);
+    d.sd = static_cast<const uint8_t*>(ws_down);
+    d.T = Tc; d.H = s->H; d.E = s->E; d.I = s->I; d.k = s->top_k; d.S = s->n_shared;
+    d.Is = has_shared ? s->I_shared : 0;
+    d.n_routed_slots = 0;                     // the decode kernels run the shared experts only
+    d.active = rb.active; d.counts = rb.counts; d.offsets = rb.offsets; d.cprefix = rb.cprefix;
+    d.sorted_ids = rb.sorted_ids; d.topk_w = rb.topk_w; d.inv = rb.inv;
+    d.h = ws + L.h;
+    d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
+    d.h_stride = L.h_stride;
+    d.partials = reinterpret_cast<float*>(ws + L.partials);
+    d.n_row_tiles = (std::max(s->I, d.Is) + 15) / 16;
+    d.out = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
+    a.topk_ids = rb.topk_ids;
+    a.scores = channel_scores + size_t(t0) * s->E * s->I;
+    a.wdt = static_cast<const uint8_t*>(w_down_t);
+    a.c = budget;
+    a.R = sparse_splits(s, Tc, budget);
+    a.sel = reinterpret_cast<int32_t*>(ws + SL.sel);
+    a.hs = reinterpret_cast<float*>(ws + SL.hs);
+    a.spart = reinterpret_cast<float*>(ws + SL.spart);
+    if (int e = hip_status(moe::launch_sparse(a, s->w_dtype, s->x_dtype, st, nullptr))) return e;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"
 
 extern "C" {
 

@@ -299,6 +299,21 @@ struct FusedArgs {
   unsigned long long* error;        // holds the epoch when a wait of this call gave up
 };
 
+// Budgeted channel-sparse routed experts (decode).
+constexpr int kSparseMaxRows = 2048;      // kept channels of one down split (staged in LDS)
+
+struct SparseArgs {
+  DecodeArgs d;               // x, routed gate/up stacks, shared stacks, routing, h / partials of the shared experts
+  const int32_t* topk_ids;    // [T*k]
+  const float* scores;        // [T, E, I] of this pass
+  const uint8_t* wdt;         // routed down, transposed: [E, I, H]
+  int c;                      // channels kept per (token, engaged expert)
+  int R;                      // splits of the kept channels in the down projection
+  int32_t* sel;               // [T*k, c] kept channels, ascending
+  float* hs;                  // [T*k, c] routing-weighted activations of the kept channels
+  float* spart;               // [T*k, R, H] down partial rows
+};
+
 struct PrefillArgs {
   const void* x;
   const uint16_t* wg; const uint16_t* wu; const uint16_t* wd;

@@ -43,6 +43,35 @@ static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
   else launch_decode_t<WT, XT, 4>(a, n_gu_row_tiles, st, mark);
 }
 
+// Gate/up and down of the shared experts only (a.n_routed_slots must be 0):
+// rows T*k + s*T + t of h and of the partials, as in the full decode pass.
+template <int WT, int XT, int NCT>
+static void launch_shared_t(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_down_kernel<WT, NCT>), dim3(a.H / 16, a.S), dim3(256), 0, st, a);
+}
+
+template <int WT, int XT>
+static void launch_shared_x(const DecodeArgs& a, hipStream_t st) {
+  if (a.T <= 16) launch_shared_t<WT, XT, 1>(a, st);
+  else launch_shared_t<WT, XT, 4>(a, st);
+}
+
+hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream_t st) {
+  if (a.S == 0) return hipSuccess;
+  if (a.n_routed_slots != 0) return hipErrorInvalidValue;
+  if (wdt == DT_F32) {
+    if (xdt == DT_F32) launch_shared_x<DT_F32, DT_F32>(a, st);
+    else launch_shared_x<DT_F32, DT_BF16>(a, st);
+  } else if (wdt == DT_BF16) {
+    if (xdt == DT_F32) launch_shared_x<DT_BF16, DT_F32>(a, st);
+    else launch_shared_x<DT_BF16, DT_BF16>(a, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
   if (wdt == DT_F32) {

@@ -1,0 +1,342 @@
+// Budgeted top-c channel-sparse routed experts (decode, small batches).
+//
+// Source: "KAIST removed calibration from MoE decoding and sped up blocks up
+// to 2.69x over vLLM" (news.hamidun.com), sections "A threshold promises a
+// budget but does not keep it" and "Top-k instead of a threshold": per token
+// only a fixed number c of each engaged expert's intermediate channels is
+// read -- the c with the highest selector scores -- so the bytes read per
+// token are known in advance.  Given the kept set the expert FFN runs on those
+// channels only: rows of the gate and up matrices and columns of the down
+// matrix.  The down matrix is taken transposed ([E, I, H]), so that one kept
+// channel is one contiguous row of H values.  Shared experts stay dense.
+//
+// Launches of one pass (T <= 64 tokens): router (+ dispatch), channel
+// selection, sparse gate/up and the shared experts' gate/up, sparse down and
+// the shared experts' down, combine.
+//
+//   select:  one work-group of 16 waves per (token, engaged expert).  Scores
+//            become order-preserving 32-bit keys in LDS; a radix select over 4
+//            bytes (per-wave histograms, one update per distinct byte per wave)
+//            finds the c-th largest key, then a stable compaction in index
+//            order keeps the keys above it and the first equal ones.
+//   gate/up: the decode gate/up operand code with gathered rows: a work-group
+//            takes 16 kept channels (A rows) against the one token (B column),
+//            its 8 waves split H, and writes silu(g) * u * (routing weight).
+//   down:    y = sum over kept channels q of h_q * WdT[q, :].  Each lane owns 8
+//            consecutive outputs (one 16-byte row slice per channel), a wave
+//            512, a work-group 2048; the kept channels are split R ways over
+//            work-groups, and the R partial rows are summed in a fixed order
+//            by the combine.  Plain FMAs: the work is a weighted sum of rows.
+#include "decode_items.hpp"
+
+namespace moe {
+
+
+// ------------------------------------------------------------- select ----
+
+// Order-preserving key of a score: larger score, larger key; -0 and +0 are
+// one value; NaN is below every number.
+__device__ __forceinline__ uint32_t score_key(float v) {
+  if (v != v) return 0u;
+  if (v == 0.f) v = 0.f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kSelWaves = 16;
+
+// Exclusive prefix sum over the threads of the work-group (in thread order).
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* lds_nw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) lds_nw[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += lds_nw[w];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Lanes of the wave whose (valid) byte value equals this lane's (8 ballots).
+__device__ __forceinline__ uint64_t same_byte_mask(uint32_t b, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const bool bit = (b >> q) & 1u;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// One work-group of 16 waves per (token, engaged expert).
+__global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArgs a) {
+  extern __shared__ uint32_t keys[];                 // [I], then hist [16][256], then scratch
+  const int f = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NT = kSelWaves * 64;
+  const int I = a.d.I, c = a.c, k = a.d.k;
+  const int t = f / k, e = a.topk_ids[f];
+  const float* s = a.scores + (size_t(t) * a.d.E + e) * I;
+  uint32_t* hist = keys + I;
+  int* misc = reinterpret_cast<int*>(hist + kSelWaves * 256);   // [0] bin, [1] remaining, [4..20) scan scratch
+  for (int i = tid; i < I; i += NT) keys[i] = score_key(s[i]);
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = c;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < kSelWaves * 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    // per-wave counts: the first lane of each group of equal bytes adds the group size
+    for (int i0 = wave * 64; i0 < I; i0 += NT) {
+      const int i = i0 + lane;
+      const uint32_t kk = i < I ? keys[i] : 0u;
+      const bool valid = i < I && (kk & pmask) == prefix;
+      const uint32_t b = (kk >> shift) & 0xFFu;
+      const uint64_t msk = same_byte_mask(b, valid);
+      if (valid && (msk & ((1ull << lane) - 1ull)) == 0) hist[wave * 256 + b] += uint32_t(__popcll(msk));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 255-4l .. 252-4l, highest first
+      uint32_t cnt[4], sum = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int b = 255 - 4 * lane - m;
+        uint32_t v = 0;
+        for (int w = 0; w < kSelWaves; ++w) v += hist[w * 256 + b];
+        cnt[m] = v;
+        sum += v;
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      uint32_t before = incl - sum;      // keys in higher bins
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (before < uint32_t(remaining) && before + cnt[m] >= uint32_t(remaining)) {
+          misc[0] = 255 - 4 * lane - m;
+          misc[1] = remaining - int(before);
+        }
+        before += cnt[m];
+      }
+    }
+    __syncthreads();
+    prefix |= uint32_t(misc[0]) << shift;
+    pmask |= 0xFFu << shift;
+    remaining = misc[1];
+    __syncthreads();
+  }
+  // prefix is now the c-th largest key; keep every larger key and the first
+  // `remaining` equal ones in index order.  Thread tid owns a contiguous chunk.
+  const int ch = (I + NT - 1) / NT;
+  const int i0 = min(I, tid * ch), i1 = min(I, i0 + ch);
+  int n_gt = 0, n_eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    n_gt += keys[i] > prefix;
+    n_eq += keys[i] == prefix;
+  }
+  const int eq_base = wg_exclusive_scan(n_eq, misc + 4);
+  const int take_eq = min(max(remaining - eq_base, 0), n_eq);
+  int pos = wg_exclusive_scan(n_gt + take_eq, misc + 4);
+  int32_t* out = a.sel + size_t(f) * c;
+  int eq_seen = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t kk = keys[i];
+    bool keep = kk > prefix;
+    if (kk == prefix) keep = eq_seen++ < take_eq;
+    if (keep && pos < c) out[pos++] = i;      // exactly c are kept; the bound only guards the buffer
+  }
+}
+
+// ------------------------------------------------------------- gate/up ---
+
+constexpr int kGuWaves = 8;
+
+template <int WT, int XT>
+__global__ void __launch_bounds__(kGuWaves * 64) sparse_gateup_kernel(SparseArgs a) {
+  __shared__ f32x4_t red[kGuWaves][2][64];
+  const DecodeArgs d = a.d;
+  constexpr int F = Fam<WT>::v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+  const int rt = blockIdx.x, f = blockIdx.y, c = a.c, K = d.H;
+  const int t = f / d.k, e = a.topk_ids[f];
+  const int r = rt * 16 + (lane & 15);
+  const int chan = a.sel[size_t(f) * c + (r < c ? r : c - 1)];     // past the end: a kept row, output dropped
+  RowPtr<WT> rg, ru;
+  rg.init(d.wg, d.E, d.I, K, e, chan);
+  ru.init(d.wu, d.E, d.I, K, e, chan);
+  constexpr int xb = XT == DT_F32 ? 4 : 2;
+  const uint8_t* xrow = reinterpret_cast<const uint8_t*>(d.x) + size_t(t) * K * xb;
+  const bool xok = (lane & 15) == 0;                                // one token: B column 0
+  const int nsteps = n_steps<WT>(K);
+  const int s0 = wave * nsteps / kGuWaves, s1 = (wave + 1) * nsteps / kGuWaves;
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
+  auto load = [&](int s) {
+    GUStep<WT, XT, 1> st;
+    st.g = load_a<WT>(rg, s, g, K);
+    st.u = load_a<WT>(ru, s, g, K);
+    if (xok) st.x[0] = load_x_raw<F, XT>(xrow, s, g, K);
+    return st;
+  };
+  auto body = [&](int s, const GUStep<WT, XT, 1>& st) {
+    const AReady<F> ag = prep_a<WT>(st.g), au = prep_a<WT>(st.u);
+    const XFrag<F, XT> b = cook_x<F, XT>(st.x[0], xok, s, g, K);
+    accg = mma_ready<F, XT>(ag, b, accg);
+    accu = mma_ready<F, XT>(au, b, accu);
+  };
+  stream_steps<Unroll<WT, 1>::v>(s0, s1, load, body);
+  red[wave][0][lane] = accg;
+  red[wave][1][lane] = accu;
+  __syncthreads();
+  if (wave != 0 || !xok) return;
+  f32x4_t gs = red[0][0][lane], us = red[0][1][lane];
+  for (int w = 1; w < kGuWaves; ++w) {
+    gs += red[w][0][lane];
+    us += red[w][1][lane];
+  }
+  const float wr = d.topk_w[f];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = rt * 16 + g * 4 + i;            // D rows of this lane: 4g .. 4g+3
+    if (rr < c) a.hs[size_t(f) * c + rr] = silu_f(gs[i]) * us[i] * wr;
+  }
+}
+
+// --------------------------------------------------------------- down ----
+
+template <int WT>
+__global__ void __launch_bounds__(256) sparse_down_kernel(SparseArgs a) {
+  __shared__ int qsel[kSparseMaxRows];
+  __shared__ float qh[kSparseMaxRows];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int f = blockIdx.z, r = blockIdx.y, c = a.c, H = a.d.H, I = a.d.I;
+  const int e = a.topk_ids[f];
+  const int q0 = int(long(r) * c / a.R), q1 = int(long(r + 1) * c / a.R);
+  for (int q = q0 + threadIdx.x; q < q1; q += 256) {
+    qsel[q - q0] = a.sel[size_t(f) * c + q];
+    qh[q - q0] = a.hs[size_t(f) * c + q];
+  }
+  __syncthreads();
+  const int col = (blockIdx.x * 4 + wave) * 512 + lane * 8;
+  if (col >= H) return;
+  constexpr int eb = WT == DT_F32 ? 4 : 2;
+  const uint8_t* base = a.wdt + (size_t(e) * I) * size_t(H) * eb + size_t(col) * eb;
+  float acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = 0.f;
+  constexpr int U = 8;
+  for (int q = q0; q < q1; q += U) {
+    u32x4_t w[U][eb / 2];
+    float hv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = q + u < q1;
+      const int qi = in ? q + u - q0 : 0;
+      hv[u] = in ? qh[qi] : 0.f;
+      const uint8_t* rowp = base + size_t(qsel[qi]) * H * eb;
+#pragma unroll
+      for (int p = 0; p < eb / 2; ++p) w[u][p] = ldg16(rowp + 16 * p);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (WT == DT_F32) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = fmaf(hv[u], __uint_as_float(w[u][m >> 2][m & 3]), acc[m]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc[2 * m] = fmaf(hv[u], bf16_lo(w[u][0][m]), acc[2 * m]);
+          acc[2 * m + 1] = fmaf(hv[u], bf16_hi(w[u][0][m]), acc[2 * m + 1]);
+        }
+      }
+    }
+  }
+  float* dst = a.spart + (size_t(f) * a.R + r) * H + col;
+  *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// ------------------------------------------------------------ combine ----
+
+// out[t]: the routed partial rows (all j, all splits r) and the shared
+// experts' rows.  A work-group takes 32 column quads; its 8 row groups each sum
+// a fixed share of the k*R partial rows with 8 loads in flight, and the group
+// sums and the shared rows are added in a fixed order.
+constexpr int kCmbCols = 32, kCmbGroups = 8;
+
+template <int OT>
+__global__ void __launch_bounds__(kCmbCols * kCmbGroups) sparse_combine_kernel(SparseArgs a) {
+  __shared__ f32x4_t red[kCmbGroups][kCmbCols];
+  const DecodeArgs d = a.d;
+  const int H4 = d.H / 4;
+  const int q = threadIdx.x % kCmbCols, grp = threadIdx.x / kCmbCols;
+  const long i4 = long(blockIdx.x) * kCmbCols + q;
+  const bool ok = i4 < long(d.T) * H4;
+  const int t = ok ? int(i4 / H4) : 0, h4 = ok ? int(i4 % H4) : 0;
+  const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(a.spart);
+  const int nrows = d.k * a.R;                                    // rows (j, r) of token t, j-major
+  const int n0 = grp * nrows / kCmbGroups, n1 = (grp + 1) * nrows / kCmbGroups;
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  for (int n = n0; n < n1; n += 8) {
+    f32x4_t b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      b[u] = (ok && n + u < n1) ? sp[(size_t(t) * nrows + n + u) * H4 + h4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += b[u];
+  }
+  red[grp][q] = v;
+  __syncthreads();
+  if (grp != 0 || !ok) return;
+  v = red[0][q];
+  for (int g = 1; g < kCmbGroups; ++g) v += red[g][q];
+  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(d.partials);
+  for (int s = 0; s < d.S; ++s) v += p[size_t(d.T * d.k + s * d.T + t) * H4 + h4];
+  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(d.out)[i4] = v;
+  else reinterpret_cast<u32x2_t*>(d.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+
+// ------------------------------------------------------------- launch ----
+
+hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream_t st);
+
+size_t sparse_select_lds_bytes(int I) { return (size_t(I) + kSelWaves * 256 + 4 + kSelWaves) * 4; }
+
+template <int WT, int XT>
+static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t st, StageMarker* mark) {
+  const int n = a.d.T * a.d.k;
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_select_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(sparse_select_lds_bytes(16384)));
+    return true;
+  }();
+  (void)attr;
+  hipLaunchKernelGGL(sparse_select_kernel, dim3(n), dim3(kSelWaves * 64), sparse_select_lds_bytes(a.d.I), st, a);
+  if (mark) mark->mark(st);
+  hipLaunchKernelGGL((sparse_gateup_kernel<WT, XT>), dim3((a.c + 15) / 16, n), dim3(kGuWaves * 64), 0, st, a);
+  if (hipError_t e = launch_decode_shared(a.d, WT, XT, st)) return e;     // shared experts: dense
+  if (mark) mark->mark(st);
+  hipLaunchKernelGGL((sparse_down_kernel<WT>), dim3((a.d.H + 2047) / 2048, a.R, n), dim3(256), 0, st, a);
+  const long n4 = long(a.d.T) * a.d.H / 4;
+  hipLaunchKernelGGL((sparse_combine_kernel<XT>), dim3(int((n4 + kCmbCols - 1) / kCmbCols)),
+                     dim3(kCmbCols * kCmbGroups), 0, st, a);
+  if (mark) mark->mark(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, StageMarker* mark) {
+  if (wdt == DT_F32) return xdt == DT_F32 ? launch_sparse_t<DT_F32, DT_F32>(a, st, mark)
+                                          : launch_sparse_t<DT_F32, DT_BF16>(a, st, mark);
+  if (wdt == DT_BF16) return xdt == DT_F32 ? launch_sparse_t<DT_BF16, DT_F32>(a, st, mark)
+                                           : launch_sparse_t<DT_BF16, DT_BF16>(a, st, mark);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

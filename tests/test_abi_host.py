@@ -69,6 +69,26 @@ def test_shape_validation(m, kw, code):
     assert m.load_library().moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == getattr(m, code)
 
 
+@pytest.mark.parametrize("kw, budget, code", [
+    (dict(), 0, "MOE_ERR_SHAPE"),
+    (dict(), 129, "MOE_ERR_SHAPE"),                       # budget > I
+    (dict(w_dtype=2), 8, "MOE_ERR_DTYPE"),                # dense f32 / bf16 experts only
+    (dict(I=16416), 8, "MOE_ERR_SHAPE"),                  # I above the selection's LDS limit
+])
+def test_sparse_validation(m, kw, budget, code):
+    base = dict(T=4, H=256, E=8, I=128, top_k=2, n_shared=0, I_shared=0, x_dtype=1, w_dtype=1,
+                router_dtype=1, path=0)
+    base.update(kw)
+    s = m.moe_shape_t(*[base[n] for n, _ in m.moe_shape_t._fields_])
+    n = ctypes.c_size_t(0)
+    assert m.load_library().moe_sparse_workspace_size(ctypes.byref(s), budget, ctypes.byref(n)) == getattr(m, code)
+
+
+def test_sparse_workspace_grows_with_budget(m):
+    s = m.make_shape(1, 4096, 8, 14336, 2)
+    assert m.moe_sparse_workspace_size(s, 2552) > m.moe_sparse_workspace_size(s, 256) > 0
+
+
 def test_resolve_path(m):
     P = m
     assert m.moe_resolve_path(m.make_shape(8, 4096, 8, 14336, 2)) == P.MOE_PATH_DECODE
