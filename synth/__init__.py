@@ -91,7 +91,8 @@ WORKLOADS = {
         Workload("mixtral_decode_t8_fp8", T=8, H=4096, E=8, k=2, I=14336, w_dtype=FP8),
         Workload("qwen_a3b_decode_q8", T=1, H=2048, E=256, k=8, I=512, S=1, Is=512,
                  x_dtype=F32, w_dtype=Q8_0, r_dtype=F32),
-        # batch one with budgeted channel sparsity (17.8 % of each engaged expert's channels)
+        # batch one, dense, and with budgeted channel sparsity (17.8 % of each engaged expert's channels)
+        Workload("mixtral_decode_t1", T=1, H=4096, E=8, k=2, I=14336),
         Workload("mixtral_decode_t1_sparse", T=1, H=4096, E=8, k=2, I=14336, channel_budget=0.178),
     ]
 }
