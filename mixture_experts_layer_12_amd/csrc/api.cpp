@@ -25,7 +25,8 @@ hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, 
 
 namespace {
 
-constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (prefill row tile)
+constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
+constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
 constexpr int kFusedMaxK = 16;       // top_k limit of the single-launch decode
 constexpr int kHRowAlign = 64;       // decode activation rows padded to 64 elements (whole 128-byte lines)
@@ -37,6 +38,7 @@ long roundup(long n, long m) { return (n + m - 1) / m * m; }
 struct Layout {
   int path;            // MOE_PATH_DECODE | MOE_PATH_PREFILL | MOE_PATH_DECODE_FUSED
   int Tr;              // tokens per routing pass
+  int tile_m;          // padding multiple of the expert-sorted order
   int cap, n_tiles;    // sorted-order capacity and tiles for Tr tokens
   size_t logits, topk_ids, topk_w, counts, offsets, cprefix, active, sorted_ids, tile_expert, inv;
   size_t h, partials, acc;
@@ -47,6 +49,13 @@ struct Layout {
   int t_pad;
   size_t total;
 };
+
+// The prefill kernels address one weight matrix and x with 32-bit element
+// offsets from a per-matrix base.
+bool prefill_fits(const moe_shape_t* s) {
+  const long n = std::max(s->I, s->n_shared > 0 ? s->I_shared : 0);
+  return n * s->H < (1L << 31) && long(s->T) * s->H < (1L << 31);
+}
 
 int check_shape(const moe_shape_t* s) {
   if (!s) return MOE_ERR_NULL;
@@ -66,14 +75,17 @@ int check_shape(const moe_shape_t* s) {
     return MOE_ERR_DTYPE;
   if (s->path == MOE_PATH_DECODE_FUSED && s->top_k > kFusedMaxK) return MOE_ERR_SHAPE;
   if (s->path == MOE_PATH_PREFILL && (s->x_dtype != MOE_BF16 || s->w_dtype != MOE_BF16)) return MOE_ERR_DTYPE;
+  if (s->path == MOE_PATH_PREFILL && !prefill_fits(s)) return MOE_ERR_SHAPE;
   // index arithmetic of the largest buffers stays in 32-bit ranges
-  if (roundup(T * k + E * (kTileM - 1), kTileM) + S * roundup(T, kTileM) > 2147483647L / 8) return MOE_ERR_SHAPE;
+  if (roundup(T * k + E * (kPrefillTileM - 1), kPrefillTileM) + S * roundup(T, kPrefillTileM) > 2147483647L / 8)
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
 int choose_path(const moe_shape_t* s) {
   if (s->path != MOE_PATH_AUTO) return s->path;
-  if (s->x_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 && s->T > kDecodeMaxT) return MOE_PATH_PREFILL;
+  if (s->x_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 && s->T > kDecodeMaxT && prefill_fits(s))
+    return MOE_PATH_PREFILL;
   // The single-launch decode is measured slower than the multi-launch kernels on every benchmarked
   // shape (its resident grid runs items one after another per work-group), so AUTO does not pick it.
   return MOE_PATH_DECODE;
@@ -114,8 +126,9 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
   const int I = s->I, Is = S > 0 ? s->I_shared : 0;
   L.Tr = (route_only || L.path == MOE_PATH_PREFILL) ? T : std::min(T, kDecodeMaxT);
   const int Tr = std::max(L.Tr, 1);
-  L.cap = int(roundup(long(Tr) * k + long(E) * (kTileM - 1), kTileM));
-  L.n_tiles = L.cap / kTileM;
+  L.tile_m = (!route_only && L.path == MOE_PATH_PREFILL) ? kPrefillTileM : kTileM;
+  L.cap = int(roundup(long(Tr) * k + long(E) * (L.tile_m - 1), L.tile_m));
+  L.n_tiles = L.cap / L.tile_m;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
   L.logits = take(size_t(Tr) * E * 4 * (L.path == MOE_PATH_DECODE_FUSED ? 4 : 1));
@@ -144,7 +157,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     }
   }
   if (!route_only && L.path == MOE_PATH_PREFILL) {
-    L.t_pad = int(roundup(T, kTileM));
+    L.t_pad = int(roundup(T, L.tile_m));
     const long rows = long(L.cap) + long(S) * L.t_pad;
     L.h_plane = rows * L.h_stride;
     L.h = take(size_t(L.h_plane) * 2);
@@ -312,7 +325,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
   if (L.path == MOE_PATH_PREFILL) {
     StageEvents sev{events, n_events};
     sev.mark(st);
-    moe::RouterArgs ra = router_args(s, s->T, x, router_w, router_b, rb);
+    moe::RouterArgs ra = router_args(s, s->T, x, router_w, router_b, rb, L.tile_m);
     ra.zero_f32 = reinterpret_cast<float*>(ws + L.acc);
     ra.zero_n = long(s->T) * s->H;
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
@@ -326,8 +339,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     p.sd = static_cast<const uint16_t*>(ws_down);
     p.T = s->T; p.H = s->H; p.E = s->E; p.I = s->I; p.k = s->top_k; p.S = s->n_shared;
     p.Is = has_shared ? s->I_shared : 0;
-    p.capacity = L.cap; p.tile_m = kTileM; p.t_pad = L.t_pad;
-    p.n_row_tiles = L.cap / kTileM + s->n_shared * (L.t_pad / kTileM);
+    p.capacity = L.cap; p.tile_m = L.tile_m; p.t_pad = L.t_pad;
     p.tile_expert = rb.tile_expert; p.sorted_ids = rb.sorted_ids; p.topk_w = rb.topk_w; p.offsets = rb.offsets;
     p.h = reinterpret_cast<uint16_t*>(ws + L.h);
     p.h_stride = L.h_stride;
