@@ -50,11 +50,13 @@ struct Layout {
   size_t total;
 };
 
-// The prefill kernels address one weight matrix and x with 32-bit element
-// offsets from a per-matrix base.
+// The prefill kernels address one weight matrix, x and the activation rows
+// with 32-bit element offsets from a per-matrix base.
 bool prefill_fits(const moe_shape_t* s) {
   const long n = std::max(s->I, s->n_shared > 0 ? s->I_shared : 0);
-  return n * s->H < (1L << 31) && long(s->T) * s->H < (1L << 31);
+  const long rows = roundup(long(s->T) * s->top_k + long(s->E) * (kPrefillTileM - 1), kPrefillTileM) +
+                    long(s->n_shared) * roundup(s->T, kPrefillTileM);   // activation rows
+  return n * s->H < (1L << 31) && long(s->T) * s->H < (1L << 31) && rows * n < (1L << 31);
 }
 
 int check_shape(const moe_shape_t* s) {

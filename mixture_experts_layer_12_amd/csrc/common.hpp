@@ -329,6 +329,7 @@ struct PrefillArgs {
   int T, H, E, I, k, S, Is;
   int capacity, tile_m, t_pad;        // routed rows, padding tile, shared rows per expert
   int n_row_tiles, n_col_tiles;
+  int k_split;           // down projection: k ranges per output tile (partial sums add up in acc)
   const int32_t* tile_expert; const int32_t* sorted_ids; const float* topk_w; const int32_t* offsets;
   uint16_t* h;           // [capacity + S*t_pad, h_stride] bf16
   int h_stride;
