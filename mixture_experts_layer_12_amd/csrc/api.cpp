@@ -133,7 +133,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
   L.n_tiles = L.cap / L.tile_m;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
-  L.logits = take(size_t(Tr) * E * 4 * (L.path == MOE_PATH_DECODE_FUSED ? 4 : 1));
+  L.logits = take(size_t(Tr) * E * 4 * (route_only || L.path == MOE_PATH_PREFILL ? 1 : 4));   // decode: 4 planes
   L.topk_ids = take(size_t(Tr) * k * 4);
   L.topk_w = take(size_t(Tr) * k * 4);
   L.counts = take(size_t(E) * 4);
@@ -402,6 +402,8 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       continue;
     }
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
+    ra.logit_parts = (nblocks > 1 && nblocks < 64) ? 4 : 1;
     if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))

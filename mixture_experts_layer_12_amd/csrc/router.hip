@@ -27,12 +27,22 @@ __global__ void __launch_bounds__(1024) router_fused_kernel(RouterArgs a) {
 
 // Larger grids: the logits go to the workspace; the selection and dispatch run
 // in a second launch (the kernel boundary orders them, no device-wide fences).
+// With a.logit_parts == 4 (grids of few tiles) each tile is split over four
+// work-groups, one per group of 4 chunks, which write partial planes; the
+// selection adds the planes in order and then the bias, the same sums in the
+// same order as the single-plane form.
 template <int RT, int XT>
 __global__ void __launch_bounds__(1024) router_logits_kernel(RouterArgs a) {
   extern __shared__ int lds[];
   clear_accumulator(a);
-  logits_tile<RT, XT, false>(a, blockIdx.x % a.n_row_tiles, blockIdx.x / a.n_row_tiles, 0, kLogitChunks,
-                             reinterpret_cast<float*>(lds), a.rb.logits);
+  if (a.logit_parts == 4) {
+    const int tile = blockIdx.x >> 2, q = blockIdx.x & 3;
+    logits_tile<RT, XT, false>(a, tile % a.n_row_tiles, tile / a.n_row_tiles, 4 * q, 4, reinterpret_cast<float*>(lds),
+                               a.rb.logits + size_t(q) * a.T * a.E);
+  } else {
+    logits_tile<RT, XT, false>(a, blockIdx.x % a.n_row_tiles, blockIdx.x / a.n_row_tiles, 0, kLogitChunks,
+                               reinterpret_cast<float*>(lds), a.rb.logits);
+  }
 }
 
 __global__ void __launch_bounds__(1024) router_select_kernel(RouterArgs a) {
@@ -63,8 +73,12 @@ static void launch_router_t(const RouterArgs& a, int NW, hipStream_t st) {
       return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((router_logits_kernel<RT, XT>), dim3(nblocks), dim3(NW * 64),
-                       size_t(kLogitChunks) * 64 * 4 * sizeof(float), st, a);
+    if (a.logit_parts == 4)      // a wave per chunk of each group
+      hipLaunchKernelGGL((router_logits_kernel<RT, XT>), dim3(4 * nblocks), dim3(4 * 64),
+                         size_t(kLogitChunks) * 64 * 4 * sizeof(float), st, a);
+    else
+      hipLaunchKernelGGL((router_logits_kernel<RT, XT>), dim3(nblocks), dim3(NW * 64),
+                         size_t(kLogitChunks) * 64 * 4 * sizeof(float), st, a);
     hipLaunchKernelGGL(router_select_kernel, dim3(1), dim3(1024), router_lds_bytes(16, a.E, a.T * a.k, true), st, a);
   }
 }
