@@ -12,10 +12,27 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
 }
 
-template <int WT, int NCT>
+template <int WT, int NCT, int RPW>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
-  __shared__ f32x4_t red[4][NCT][64];
-  down_item<WT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
+  __shared__ f32x4_t red[4][RPW * NCT][64];
+  down_item<WT, NCT, false, RPW>(a, blockIdx.x, blockIdx.y, red);
+}
+
+// Row tiles of 16 outputs per down-projection work-group: two when the
+// token columns fit one MFMA tile (they share every activation load).  Four
+// measured slower: too few work-groups for the memory stream.
+#ifndef MOE_DN_RPW
+#define MOE_DN_RPW 2
+#endif
+template <int WT, int NCT>
+static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
+  constexpr int R = NCT == 1 ? MOE_DN_RPW : 1;
+  if (R >= 4 && a.H % 64 == 0)
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
+  else if (R >= 2 && a.H % 32 == 0)
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1)>), dim3(a.H / 32, n_slots), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
 }
 
 template <int OT>
@@ -30,8 +47,7 @@ static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
-  dim3 g2(a.H / 16, a.n_routed_slots + a.S);
-  hipLaunchKernelGGL((decode_down_kernel<WT, NCT>), g2, b, 0, st, a);
+  launch_down<WT, NCT>(a, a.n_routed_slots + a.S, st);
   const long n4 = long(a.T) * a.H / 4;
   hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n4 + 255) / 256)), b, 0, st, a);
   if (mark) mark->mark(st);
@@ -48,7 +64,7 @@ static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
 template <int WT, int XT, int NCT>
 static void launch_shared_t(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((decode_down_kernel<WT, NCT>), dim3(a.H / 16, a.S), dim3(256), 0, st, a);
+  launch_down<WT, NCT>(a, a.S, st);
 }
 
 template <int WT, int XT>

@@ -575,16 +575,20 @@ __device__ __forceinline__ f32x4_t mma_h(const AReady<F>& a, const HFrag<F>& b, 
   return c;
 }
 
-template <int WT, int NCT>
-struct DNStep { AFrag<WT> a; HFrag<Fam<WT>::v> h[NCT]; };
+template <int WT, int NCT, int RPW>
+struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 
-// One work-group: 16 hidden outputs (rows of the down projection) of one
-// expert slot, for every token of that slot.  Its 4 waves split the slot's
-// intermediate dimension; partial sums meet in LDS.  The result rows are the
-// routing-weighted expert outputs; they go to `partials` at the same row the
-// activations use (one row per routed assignment, then the shared tokens).
-template <int WT, int NCT, bool COH>
-__device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[NCT][64]) {
+// One work-group: RPW x 16 hidden outputs (rows of the down projection) of
+// one expert slot, for every token of that slot.  Its 4 waves split the
+// slot's intermediate dimension; partial sums meet in LDS.  A wave's RPW row
+// tiles share each activation fragment it loads, which cuts the activation
+// loads per weight byte by RPW (they otherwise add a fifth of the weight
+// stream's load instructions).  The result rows are the routing-weighted
+// expert outputs; they go to `partials` at the same row the activations use
+// (one row per routed assignment, then the shared tokens).  `red` holds
+// [4 waves][RPW * NCT][64] accumulators.
+template <int WT, int NCT, bool COH, int RPW = 1>
+__device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   int e, n_e, hrow0, K;
@@ -604,11 +608,16 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
   }
   constexpr int F = Fam<WT>::v;
   const int H = a.H, g = lane >> 4;
-  RowPtr<WT> rw;
-  rw.init(base, n_mat, H, K, e, rt * 16 + (lane & 15));
-  f32x4_t sd_rows = {1.f, 1.f, 1.f, 1.f};      // fp8: row scales of this lane's output rows
-  if constexpr (WT == DT_FP8) {
-    if (wave == 0) sd_rows = fp8_row_scales(base, n_mat, H, K, e, rt * 16 + (lane >> 4) * 4);
+  const int row0 = rt * RPW * 16;               // first output row of this work-group
+  RowPtr<WT> rw[RPW];
+  f32x4_t sd_rows[RPW];                         // fp8: row scales of this lane's output rows
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rw[r].init(base, n_mat, H, K, e, row0 + r * 16 + (lane & 15));
+    sd_rows[r] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+    if constexpr (WT == DT_FP8) {
+      if (wave == 0) sd_rows[r] = fp8_row_scales(base, n_mat, H, K, e, row0 + r * 16 + (lane >> 4) * 4);
+    }
   }
   size_t hoff[NCT];
   bool hok[NCT];
@@ -621,14 +630,17 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
   const int nct = (n_e + 15) >> 4;
   const int nsteps = n_steps<WT>(K);
   const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
-  f32x4_t acc[NCT];
+  f32x4_t acc[RPW][NCT];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[r][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   constexpr int U = UnrollDown<WT, NCT>::v;
   auto load = [&](int s) {
-    DNStep<WT, NCT> st;
-    st.a = load_a<WT>(rw, s, g, K);
+    DNStep<WT, NCT, RPW> st;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) st.a[r] = load_a<WT>(rw[r], s, g, K);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
       if (NCT == 1 || ct < nct) {
@@ -636,30 +648,37 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
       }
     return st;
   };
-  auto body = [&](int s, const DNStep<WT, NCT>& st) {
-    const AReady<F> ar = prep_a<WT>(st.a);
+  auto body = [&](int s, const DNStep<WT, NCT, RPW>& st) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      if (NCT == 1 || ct < nct) acc[ct] = mma_h<F>(ar, cook_h<F>(st.h[ct], hok[ct], s, g, K), acc[ct]);
+      if (NCT == 1 || ct < nct) {
+        const auto hc = cook_h<F>(st.h[ct], hok[ct], s, g, K);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) acc[r][ct] = mma_h<F>(prep_a<WT>(st.a[r]), hc, acc[r][ct]);
+      }
     }
   };
   stream_steps<U>(s0, s1, load, body);
 
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) red[wave][ct][lane] = acc[ct];
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) red[wave][r * NCT + ct][lane] = acc[r][ct];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if (!(NCT == 1 || ct < nct)) continue;
-    f32x4_t v = red[0][ct][lane];
+  for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[w][ct][lane];
-    const int c = ct * 16 + (lane & 15);
-    if (c >= n_e) continue;
-    // lane holds rows 4*(lane/16) + 0..3 of this tile for token column c
-    st_f32x4<COH>(a.partials + size_t(hrow0 + c) * H + rt * 16 + (lane >> 4) * 4, v * sd_rows);
-  }
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (!(NCT == 1 || ct < nct)) continue;
+      f32x4_t v = red[0][r * NCT + ct][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += red[w][r * NCT + ct][lane];
+      const int c = ct * 16 + (lane & 15);
+      if (c >= n_e) continue;
+      // lane holds rows 4*(lane/16) + 0..3 of row tile r for token column c
+      st_f32x4<COH>(a.partials + size_t(hrow0 + c) * H + row0 + r * 16 + (lane >> 4) * 4, v * sd_rows[r]);
+    }
 }
 
 // out[t] = sum over j of the partial row of assignment t*k + j (found through
