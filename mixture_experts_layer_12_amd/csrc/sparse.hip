@@ -62,74 +62,71 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* lds_nw) {
   return base + incl - v;
 }
 
-// Lanes of the wave whose (valid) byte value equals this lane's (8 ballots).
-__device__ __forceinline__ uint64_t same_byte_mask(uint32_t b, bool valid) {
-  uint64_t m = __ballot(valid);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const bool bit = (b >> q) & 1u;
-    const uint64_t bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
-  return m;
-}
+// Radix digits of the selection: 11, 11 and 10 bits from the top of the key.
+__host__ __device__ constexpr int sel_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__host__ __device__ constexpr int sel_bits(int pass) { return pass == 2 ? 10 : 11; }
+constexpr int kSelBins = 2048;
+static_assert(kSelBins <= 2 * kSelWaves * 64 && (1 << 10) >= kSelWaves * 64, "two bins or one per thread");
 
-// One work-group of 16 waves per (token, engaged expert).
+// One work-group of 16 waves per (token, engaged expert): an exact radix
+// select of the c-th largest key in three passes (11, 11, 10 bits), each a
+// histogram of the keys that match the digits chosen so far, counted with LDS
+// atomics (a wave's lanes rarely share a bin once 11 bits are used), then one
+// ordered compaction.  Keys stay in LDS.
 __global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArgs a) {
-  extern __shared__ uint32_t keys[];                 // [I], then hist [16][256], then scratch
+  extern __shared__ uint32_t keys[];                 // [I], then hist [2048], then scratch
   const int f = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NT = kSelWaves * 64;
   const int I = a.d.I, c = a.c, k = a.d.k;
   const int t = f / k, e = a.topk_ids[f];
   const float* s = a.scores + (size_t(t) * a.d.E + e) * I;
   uint32_t* hist = keys + I;
-  int* misc = reinterpret_cast<int*>(hist + kSelWaves * 256);   // [0] bin, [1] remaining, [4..20) scan scratch
-  for (int i = tid; i < I; i += NT) keys[i] = score_key(s[i]);
+  int* misc = reinterpret_cast<int*>(hist + kSelBins);   // [0] bin, [1] remaining, [4..20) scan scratch
+  {
+    // all score loads first (I <= 16 * NT), so their latencies overlap
+    static_assert(16 * NT >= 16384, "one batch of loads covers the largest I");
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = tid + u * NT;
+      v[u] = i < I ? s[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = tid + u * NT;
+      if (i < I) keys[i] = score_key(v[u]);
+    }
+  }
   uint32_t prefix = 0, pmask = 0;
   int remaining = c;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kSelWaves * 256; i += NT) hist[i] = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = sel_shift(pass), nb = 1 << sel_bits(pass);
+    for (int i = tid; i < kSelBins; i += NT) hist[i] = 0;
     __syncthreads();
-    // per-wave counts: the first lane of each group of equal bytes adds the group size
-    for (int i0 = wave * 64; i0 < I; i0 += NT) {
-      const int i = i0 + lane;
-      const uint32_t kk = i < I ? keys[i] : 0u;
-      const bool valid = i < I && (kk & pmask) == prefix;
-      const uint32_t b = (kk >> shift) & 0xFFu;
-      const uint64_t msk = same_byte_mask(b, valid);
-      if (valid && (msk & ((1ull << lane) - 1ull)) == 0) hist[wave * 256 + b] += uint32_t(__popcll(msk));
+    for (int i = tid; i < I; i += NT) {
+      const uint32_t kk = keys[i];
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & uint32_t(nb - 1)], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 255-4l .. 252-4l, highest first
-      uint32_t cnt[4], sum = 0;
+    {
+      // thread t holds bins nb-1-per*t .. nb-per*(t+1) (highest first); a
+      // work-group scan in thread order counts the keys in higher bins
+      const int per = nb / NT;
+      uint32_t cnt[2] = {0u, 0u}, sum = 0;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int b = 255 - 4 * lane - m;
-        uint32_t v = 0;
-        for (int w = 0; w < kSelWaves; ++w) v += hist[w * 256 + b];
-        cnt[m] = v;
-        sum += v;
-      }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      uint32_t before = incl - sum;      // keys in higher bins
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (before < uint32_t(remaining) && before + cnt[m] >= uint32_t(remaining)) {
-          misc[0] = 255 - 4 * lane - m;
-          misc[1] = remaining - int(before);
-        }
-        before += cnt[m];
+      for (int m = 0; m < 2; ++m)
+        if (m < per) { cnt[m] = hist[nb - 1 - per * tid - m]; sum += cnt[m]; }
+      uint32_t before = uint32_t(wg_exclusive_scan(int(sum), misc + 4));
+      if (before < uint32_t(remaining) && before + sum >= uint32_t(remaining)) {
+        const int m = before + cnt[0] >= uint32_t(remaining) ? 0 : 1;
+        misc[0] = nb - 1 - per * tid - m;
+        misc[1] = remaining - int(before + (m ? cnt[0] : 0u));
       }
     }
     __syncthreads();
     prefix |= uint32_t(misc[0]) << shift;
-    pmask |= 0xFFu << shift;
+    pmask |= uint32_t(nb - 1) << shift;
     remaining = misc[1];
     __syncthreads();
   }
@@ -307,7 +304,7 @@ __global__ void __launch_bounds__(kCmbCols * kCmbGroups) sparse_combine_kernel(S
 
 hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream_t st);
 
-size_t sparse_select_lds_bytes(int I) { return (size_t(I) + kSelWaves * 256 + 4 + kSelWaves) * 4; }
+size_t sparse_select_lds_bytes(int I) { return (size_t(I) + kSelBins + 4 + kSelWaves) * 4; }
 
 template <int WT, int XT>
 static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t st, StageMarker* mark) {
