@@ -53,9 +53,14 @@ enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q4_0 = 2, MOE_Q8_0 = 3, MOE_FP8_E4M3 = 4 }
 
 /* execution path (moe_shape_t.path) */
 enum {
-  MOE_PATH_AUTO = 0,    /* decode path when T <= 64 or the dtypes need it, else prefill */
+  MOE_PATH_AUTO = 0,    /* decode path when T <= 64, the dtypes need it or the sizes exceed
+                           the prefill limits below, else prefill */
   MOE_PATH_DECODE = 1,  /* weight-streaming mat-vec kernels, any supported dtype, any T */
-  MOE_PATH_PREFILL = 2, /* bf16 MFMA grouped GEMMs; needs x, experts bf16 */
+  MOE_PATH_PREFILL = 2, /* bf16 MFMA grouped GEMMs; needs x, experts bf16, and (32-bit element
+                           offsets inside one matrix) max(I, I_shared) * H, T * H and
+                           (roundup(T*top_k + E*255, 256) + n_shared*roundup(T, 256)) *
+                           max(I, I_shared) all below 2^31; its expert segments are padded
+                           to multiples of 256 rows */
   MOE_PATH_DECODE_FUSED = 3  /* the decode kernels as one cooperative launch per pass of
                            at most 64 tokens; needs router_dtype == x_dtype and
                            top_k <= 16.  While `stream` is being captured into a
