@@ -85,14 +85,20 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
   for (int i = blockIdx.x; i < f.n_items; i += gridDim.x) {
     if (i < f.n_logit) {      // one group of 4 chunks of one tile -> its partial plane
       const int tile = i >> 2, q = i & 3;
-      logits_tile<XT, XT, true>(f.r, tile % f.r.n_row_tiles, tile / f.r.n_row_tiles, 4 * q, 4,
+      logits_tile<XT, XT, true, 1>(f.r, tile % f.r.n_row_tiles, tile / f.r.n_row_tiles, 4 * q, 4,
                                 reinterpret_cast<float*>(smem), f.r.rb.logits + size_t(q) * a.T * a.E);
     } else if (i < f.end_shared_gu) {
       const int j = i - f.n_logit;
       gateup_item<WT, XT, NCT, true>(a, j % f.gu_rt_shared, a.n_routed_slots + j / f.gu_rt_shared, red_gu);
     } else if (i < f.end_select) {
       wait_items(f, 0, f.n_logit);
-      select_and_dispatch<true>(f.r, f.r.rb.logits, false, smem);
+      switch (topk_mode(a.E, a.k)) {
+        case kTopkT8: select_and_dispatch<true, kTopkT8>(f.r, f.r.rb.logits, false, smem); break;
+        case kTopkT16: select_and_dispatch<true, kTopkT16>(f.r, f.r.rb.logits, false, smem); break;
+        case kTopkT32: select_and_dispatch<true, kTopkT32>(f.r, f.r.rb.logits, false, smem); break;
+        case kTopkRow16: select_and_dispatch<true, kTopkRow16>(f.r, f.r.rb.logits, false, smem); break;
+        default: select_and_dispatch<true, kTopkWave>(f.r, f.r.rb.logits, false, smem); break;
+      }
     } else if (i < f.end_gu) {
       const int j = i - f.end_select;
       wait_items(f, f.end_shared_gu, f.end_select);

@@ -440,21 +440,19 @@ __device__ __forceinline__ void dispatch_wg(const RouterArgs a, int* lds, const 
 // One 16-expert x 16-token logits tile: the waves split H, partial sums meet
 // in LDS, wave 0 adds the bias and stores to `dst` ([T, E], row stride E).
 // Logits of one 16-expert x 16-token tile from chunks [cb, cb + n) with n =
-// 4 * (number of groups): each wave computes n / NW chunks into `red` (LDS,
+// 4 * (number of groups): each wave computes CPW = n / NW chunks into `red` (LDS,
 // n x 64 x 4 floats), then wave 0 adds them in the fixed order.  final: n is
 // all 16 chunks, the bias is added and dst is the [T, E] logits; otherwise
 // the group sum goes to dst as one partial [T, E] plane (bias added by the
 // reader, after the planes, in the same order).
-template <int RT, int XT, bool COH>
+template <int RT, int XT, bool COH, int CPW>
 __device__ __forceinline__ void logits_tile(const RouterArgs a, int rtile, int ctile, int cb, int n, float* red,
                                             float* dst) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
-  const int cpw = n / NW, c0 = cb + wave * cpw;
-  f32x4_t acc[4];
-  if (cpw == 1) router_dot<RT, XT, 1>(a, rtile, ctile, c0, lane, acc);
-  else if (cpw == 2) router_dot<RT, XT, 2>(a, rtile, ctile, c0, lane, acc);
-  else router_dot<RT, XT, 4>(a, rtile, ctile, c0, lane, acc);
-  for (int j = 0; j < cpw; ++j) *reinterpret_cast<f32x4_t*>(red + ((wave * cpw + j) * 64 + lane) * 4) = acc[j];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c0 = cb + wave * CPW;
+  f32x4_t acc[CPW];
+  router_dot<RT, XT, CPW>(a, rtile, ctile, c0, lane, acc);
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) *reinterpret_cast<f32x4_t*>(red + ((wave * CPW + j) * 64 + lane) * 4) = acc[j];
   __syncthreads();
   if (wave == 0) {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -475,29 +473,48 @@ __device__ __forceinline__ void logits_tile(const RouterArgs a, int rtile, int c
   }
 }
 
+// Few assignments (decode): at most kSmallN of them (T * k), T * E <= 1024 and
+// T * E * E <= kRankWork take route_small below.
+constexpr int kSmallN = 64;
+constexpr int kRankWork = 65536;
+constexpr int kSmallDispInts = 3 * 64 + 2 * 65 + 1;    // slot tables of the one-wave dispatch
+
+__host__ __device__ inline bool small_route(int T, int E, int k) {
+  return T * k <= kSmallN && T * E <= 1024 && long(T) * E * E <= kRankWork;
+}
+
 // LDS of the selection and dispatch, in ints: dispatch scratch, then the flat
 // ids (when T*k fits), then the logits staging area (select kernel only).
-__host__ __device__ inline int router_disp_ints(int NW, int E) { return NW * E + 2 * E + 1; }
+// A multiple of 4 ints, so that what follows stays 16-byte aligned.
+__host__ __device__ inline int router_disp_ints(int NW, int E) {
+  const int d = NW * E + 2 * E + 1 > kSmallDispInts ? NW * E + 2 * E + 1 : kSmallDispInts;
+  return (d + 3) & ~3;
+}
+
+// Selection strategies of the general path; each kernel is built for one of
+// them, so that its code holds only the loops it runs.
+enum : int { kTopkT8 = 0, kTopkT16 = 1, kTopkT32 = 2, kTopkRow16 = 3, kTopkWave = 4 };
+
+__host__ __device__ inline int topk_mode(int E, int k) {
+  if (E <= 32 && k <= 8) return E <= 8 ? kTopkT8 : (E <= 16 ? kTopkT16 : kTopkT32);
+  return (E <= 64 && k <= 16) ? kTopkRow16 : kTopkWave;
+}
 
 // Top-k of tokens [t0, t0 + nt) whose logit rows start at `l` (row stride E,
 // LDS): a thread per token (E <= 32, k <= 8), a 16-lane row per token
-// (E <= 64, k <= 16), else a wave per token.
-template <bool COH>
+// (E <= 64, k <= 16), else a wave per token; MODE is topk_mode(E, k).
+template <bool COH, int MODE>
 __device__ __forceinline__ void topk_chunk(const RouterArgs a, const float* l, int t0, int nt, int32_t* ids_lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NT = blockDim.x, NW = NT >> 6;
   const int E = a.E, k = a.k;
-  if (E <= 32 && k <= 8) {
+  if constexpr (MODE <= kTopkT32) {
+    constexpr int EMAX = MODE == kTopkT8 ? 8 : (MODE == kTopkT16 ? 16 : 32);
     for (int i = tid; i < nt; i += NT) {
       const size_t t = size_t(t0 + i);
-      const float* lt = l + size_t(i) * E;
-      int32_t* it = a.rb.topk_ids + t * k;
-      float* wt = a.rb.topk_w + t * k;
-      int32_t* il = ids_lds ? ids_lds + t * k : nullptr;
-      if (E <= 8) topk_thread<8, COH>(lt, E, k, it, wt, il);
-      else if (E <= 16) topk_thread<16, COH>(lt, E, k, it, wt, il);
-      else topk_thread<32, COH>(lt, E, k, it, wt, il);
+      topk_thread<EMAX, COH>(l + size_t(i) * E, E, k, a.rb.topk_ids + t * k, a.rb.topk_w + t * k,
+                             ids_lds ? ids_lds + t * k : nullptr);
     }
-  } else if (E <= 64 && k <= 16) {
+  } else if constexpr (MODE == kTopkRow16) {
     for (int i0 = wave * 4; i0 < nt; i0 += NW * 4) {        // wave-uniform loop
       const int i = i0 + (lane >> 4);
       const bool valid = i < nt;
@@ -515,50 +532,293 @@ __device__ __forceinline__ void topk_chunk(const RouterArgs a, const float* l, i
   }
 }
 
-// Top-k of every token, then the dispatch; one work-group.  Logits in global
-// memory are staged into LDS a chunk of tokens at a time with every load of a
-// chunk issued before the first store, so the selection waits on memory once
-// per chunk rather than once per token.
+// Logits [0, cnt) of the [T, E] block at `src` into LDS.  With partial planes
+// (logit_parts 4, `plane` floats apart) the four group sums are added in
+// order and then the bias.  Every load of a batch is issued before the first
+// store: the loads use a clamped index and the stores are predicated.
 template <bool COH>
+__device__ __forceinline__ void stage_logits(const RouterArgs a, const float* src, int cnt, size_t plane, float* stage) {
+  const int tid = threadIdx.x, NT = blockDim.x, E = a.E;
+  for (int b = 0; b < cnt; b += 8 * NT) {
+    float v[8];
+    if (a.logit_parts == 1) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_f32<COH>(src + min(b + u * NT + tid, cnt - 1));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = min(b + u * NT + tid, cnt - 1);
+        float acc = ld_f32<COH>(src + idx);
+        acc += ld_f32<COH>(src + plane + idx);
+        acc += ld_f32<COH>(src + 2 * plane + idx);
+        acc += ld_f32<COH>(src + 3 * plane + idx);
+        acc += a.bias ? a.bias[idx % E] : 0.f;
+        v[u] = acc;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = b + u * NT + tid;
+      if (idx < cnt) stage[idx] = v[u];
+    }
+  }
+}
+
+// Candidate order as one unsigned key (larger key = earlier candidate): the
+// order-preserving bits of the logit (NaN read as -inf, -0 as +0) above the
+// complemented expert index, so equal logits go to the lower index.
+__device__ __forceinline__ uint64_t cand_key(float v, int j) {
+  v = sanitize(v) + 0.f;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(o) << 32) | uint32_t(~uint32_t(j));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = uint32_t(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Selection and dispatch of few assignments (small_route), in five phases:
+//  1. the logits of every token become candidate keys in LDS (rows padded to
+//     E4 = E rounded up to 4 with key 0, which precedes nothing);
+//  2. the rank of each expert of each token, the number of keys above its
+//     own, is counted in parts: a work item takes 4 experts and one part of
+//     the row, loads each key pair once and compares it with all 4;
+//  3. the parts are summed; experts of rank < k are the selection, in rank
+//     order (the list the round-by-round selections produce);
+//  4. wave 0, lane f = flat id t * k + j: the weight of selection j (softmax
+//     over the selected logits, the denominator summed in selection order, as
+//     in the other strategies) and, with ballots over the 8 bits of the
+//     expert ids, each assignment's group of equal experts, its rank in the
+//     group (smaller flat id first), and the assignments and active experts
+//     with a smaller expert id; active experts' segments follow in expert
+//     order, each padded to a multiple of tile_m;
+//  5. the work-group writes the per-expert tables, the padding and the tile
+//     table.  The results are those of dispatch_wg.
+template <bool COH>
+__device__ __forceinline__ void route_small(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
+  const RouteBufs& rb = a.rb;
+  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, NW = NT >> 6;
+  const int T = a.T, E = a.E, k = a.k, n = T * k, M = a.tile_m;
+  const int E4 = (E + 3) & ~3, G = E4 >> 2;
+  int* s_e = lds;                  // [64]: expert of active slot j (slots in expert order)
+  int* s_cnt = s_e + 64;           // [64]: its assignments
+  int* s_pad = s_cnt + 64;         // [64]: its padded length
+  int* s_off = s_pad + 64;         // [65]: start of its segment; [A]: end of the last segment
+  int* s_cpre = s_off + 65;        // [65]: assignments with a smaller expert; [A]: n
+  int* s_na = s_cpre + 65;         // [1]: A, the number of active experts
+  int32_t* ids_lds = lds + router_disp_ints(NW, E);                       // [n]
+  float* selv = reinterpret_cast<float*>(ids_lds + n);                     // [n]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ids_lds + ((2 * n + 3) & ~3));       // [T][E4], 16-byte aligned
+  int* part = reinterpret_cast<int*>(keys + T * E4);                        // [Q][T][E4]
+
+  // 1. keys
+  const size_t plane = size_t(T) * E;
+  for (int b = 0; b < T * E4; b += 4 * NT) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(b + u * NT + tid, T * E4 - 1);
+      const int i = p / E4, idx = i * E + min(p - i * E4, E - 1);
+      if (l_in_lds) {
+        v[u] = l[idx];
+      } else if (a.logit_parts == 1) {
+        v[u] = ld_f32<COH>(l + idx);
+      } else {
+        float acc = ld_f32<COH>(l + idx);
+        acc += ld_f32<COH>(l + plane + idx);
+        acc += ld_f32<COH>(l + 2 * plane + idx);
+        acc += ld_f32<COH>(l + 3 * plane + idx);
+        acc += a.bias ? a.bias[idx % E] : 0.f;
+        v[u] = acc;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = b + u * NT + tid;
+      if (p < T * E4) {
+        const int j = p % E4;
+        keys[p] = j < E ? cand_key(v[u], j) : 0ull;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. partial ranks: item (part q, token i, group g of 4 experts)
+  const int W = T * G;
+  int Q = 1;
+  while (2 * Q <= G && 2 * Q * W <= NT) Q *= 2;
+  const int span = ((E4 + Q - 1) / Q + 1) & ~1;
+  for (int w = tid; w < Q * W; w += NT) {
+    const int q = w / W, r = w - q * W, i = r / G, g = r - i * G;
+    const uint64_t* row = keys + i * E4;
+    const u32x4_t o01 = *reinterpret_cast<const u32x4_t*>(row + 4 * g);
+    const u32x4_t o23 = *reinterpret_cast<const u32x4_t*>(row + 4 * g + 2);
+    const uint64_t k0 = uint64_t(o01[0]) | (uint64_t(o01[1]) << 32), k1 = uint64_t(o01[2]) | (uint64_t(o01[3]) << 32);
+    const uint64_t k2 = uint64_t(o23[0]) | (uint64_t(o23[1]) << 32), k3 = uint64_t(o23[2]) | (uint64_t(o23[3]) << 32);
+    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    const int j1 = min(E4, (q + 1) * span);
+#pragma unroll 8
+    for (int j = q * span; j < j1; j += 2) {
+      const u32x4_t t = *reinterpret_cast<const u32x4_t*>(row + j);
+      const uint64_t x0 = uint64_t(t[0]) | (uint64_t(t[1]) << 32), x1 = uint64_t(t[2]) | (uint64_t(t[3]) << 32);
+      c0 += (x0 > k0) + (x1 > k0);
+      c1 += (x0 > k1) + (x1 > k1);
+      c2 += (x0 > k2) + (x1 > k2);
+      c3 += (x0 > k3) + (x1 > k3);
+    }
+    *reinterpret_cast<u32x4_t*>(part + (q * T + i) * E4 + 4 * g) =
+        u32x4_t{uint32_t(c0), uint32_t(c1), uint32_t(c2), uint32_t(c3)};
+  }
+  __syncthreads();
+
+  // 3. ranks -> selection
+  for (int p = tid; p < T * E; p += NT) {
+    const int i = p / E, e = p - i * E;
+    int rnk = 0;
+    for (int q = 0; q < Q; ++q) rnk += part[(q * T + i) * E4 + e];
+    if (rnk < k) {
+      ids_lds[i * k + rnk] = e;
+      selv[i * k + rnk] = key_value(keys[i * E4 + e]);
+    }
+  }
+  __syncthreads();
+
+  // 4. weights and the assignments' places (wave 0)
+  int rk = 0, slot = 0;
+  if (tid < 64) {
+    const bool valid = lane < n;
+    const int f = valid ? lane : 0;
+    const int i = f / k;
+    const float* si = selv + i * k;
+    const float lmax = si[0];
+    float denom = 0.f, zf = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float z = (si[j] == -__builtin_inff()) ? 0.f : __expf(si[j] - lmax);
+      denom += z;
+      if (j == f - i * k) zf = z;
+    }
+    const int e = valid ? ids_lds[f] : 0;
+    if (valid) {
+      st_i32<COH>(rb.topk_ids + f, e);
+      st_f32<COH>(rb.topk_w + f, denom > 0.f ? zf * (1.0f / denom) : 1.0f / float(k));   // see topk_thread
+    }
+    uint64_t same = __ballot(valid), lt = 0;     // same expert / smaller expert (valid lanes)
+#pragma unroll
+    for (int bt = 7; bt >= 0; --bt) {
+      const bool bit = (e >> bt) & 1;
+      const uint64_t bb = __ballot(bit);
+      if (bit) { lt |= same & ~bb; same &= bb; }
+      else same &= ~bb;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    const bool leader = valid && (same & below) == 0;
+    const uint64_t lead = __ballot(leader);
+    const int A = __popcll(lead);
+    rk = __popcll(same & below);
+    slot = __popcll(lt & lead);
+    if (leader) {
+      const int c = __popcll(same);
+      s_e[slot] = e;
+      s_cnt[slot] = c;
+      s_pad[slot] = (c + M - 1) / M * M;
+      s_cpre[slot] = __popcll(lt);
+      if (M == 1) s_off[slot] = __popcll(lt);
+    }
+    if (lane == 0) {
+      s_na[0] = A;
+      s_cpre[A] = n;
+      if (M == 1) s_off[A] = n;
+    }
+    if (M != 1) {
+      // padded starts: exclusive scan of the pads over the slots
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int v = lane < A ? s_pad[lane] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+      }
+      if (lane < A) s_off[lane] = incl - v;
+      if (lane == 63) s_off[A] = incl;
+    }
+  }
+  __syncthreads();
+
+  // 5. tables
+  const int A = s_na[0];
+  const int total = s_off[A];
+  if (tid < n) {
+    const int pos = s_off[slot] + rk;
+    st_i32<COH>(rb.sorted_ids + pos, tid);
+    st_i32<COH>(rb.inv + tid, pos);
+  }
+  for (int e = tid; e < E; e += NT) {
+    int lo = 0, hi = A;            // first slot whose expert is >= e
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_e[mid] < e) lo = mid + 1; else hi = mid;
+    }
+    st_i32<COH>(rb.counts + e, (lo < A && s_e[lo] == e) ? s_cnt[lo] : 0);
+    st_i32<COH>(rb.offsets + e, s_off[lo]);
+    st_i32<COH>(rb.cprefix + e, s_cpre[lo]);
+  }
+  if (tid < A) st_i32<COH>(rb.active + 1 + tid, s_e[tid]);
+  if (tid == 0) {
+    st_i32<COH>(rb.offsets + E, total);
+    st_i32<COH>(rb.cprefix + E, n);
+    st_i32<COH>(rb.active, A);
+  }
+  if (M != 1) {                    // padding rows inside the segments, then past the last one
+    for (int w = tid; w < A * M; w += NT) {
+      const int j = w / M, p = s_off[j] + s_cnt[j] + (w - j * M);
+      if (p < s_off[j + 1]) st_i32<COH>(rb.sorted_ids + p, n);
+    }
+    for (int p = total + tid; p < a.capacity; p += NT) st_i32<COH>(rb.sorted_ids + p, n);
+  }
+  const int n_tiles = rb.tile_expert ? a.capacity / M : 0;
+  for (int i = tid; i < n_tiles; i += NT) {
+    const int r = i * M;
+    int e = -1;
+    if (r < total) {
+      int lo = 0, hi = A;          // last slot starting at or before r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= r) lo = mid; else hi = mid;
+      }
+      e = s_e[lo];
+    }
+    st_i32<COH>(rb.tile_expert + i, e);
+  }
+}
+
+// Top-k of every token, then the dispatch; one work-group.  Few assignments
+// take route_small.  Otherwise logits in global
+// memory are staged into LDS a chunk of tokens at a time, and the selection
+// and dispatch_wg follow.
+template <bool COH, int MODE>
 __device__ __forceinline__ void select_and_dispatch(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
-  const int tid = threadIdx.x, NT = blockDim.x, NW = NT >> 6;
+  const int NW = blockDim.x >> 6;
   const int T = a.T, E = a.E, n = T * a.k;
   const bool ids_fit = n <= kRouterIdsLds;
   int* ids_lds = ids_fit ? lds + router_disp_ints(NW, E) : nullptr;
+  if (small_route(T, E, a.k)) {
+    route_small<COH>(a, l, l_in_lds, lds);
+    return;
+  }
   if (l_in_lds) {
-    topk_chunk<COH>(a, l, 0, T, ids_lds);
+    topk_chunk<COH, MODE>(a, l, 0, T, ids_lds);
   } else {
     float* stage = reinterpret_cast<float*>(lds + router_disp_ints(NW, E) + (ids_fit ? n : 0));
     const int ch = max(1, kRouterStage / E);
     for (int t0 = 0; t0 < T; t0 += ch) {
-      const int cnt = min(ch, T - t0) * E;
-      const float* src = l + size_t(t0) * E;
-      const size_t plane = size_t(T) * E;
-      for (int b = 0; b < cnt; b += 8 * NT) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = b + u * NT + tid;
-          if (a.logit_parts == 1) {
-            v[u] = idx < cnt ? ld_f32<COH>(src + idx) : 0.f;
-          } else {      // group planes of the single-launch path, then the bias
-            float acc = 0.f;
-            if (idx < cnt) {
-              acc = ld_f32<COH>(src + idx);
-              for (int q = 1; q < a.logit_parts; ++q) acc += ld_f32<COH>(src + q * plane + idx);
-              acc += a.bias ? a.bias[idx % E] : 0.f;
-            }
-            v[u] = acc;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = b + u * NT + tid;
-          if (idx < cnt) stage[idx] = v[u];
-        }
-      }
+      stage_logits<COH>(a, l + size_t(t0) * E, min(ch, T - t0) * E, size_t(T) * E, stage);
       __syncthreads();
-      topk_chunk<COH>(a, stage, t0, min(ch, T - t0), ids_lds);
+      topk_chunk<COH, MODE>(a, stage, t0, min(ch, T - t0), ids_lds);
       __syncthreads();
     }
   }

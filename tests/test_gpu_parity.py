@@ -44,6 +44,10 @@ SMALL = {
     "n10k_prefill": W("n10k_prefill", T=5000, H=64, E=8, k=2, I=32),
     # 33..64 experts (one DPP row per token) with k > 8 and a ragged expert count
     "e40_k10": W("e40_k10", T=37, H=96, E=40, k=10, I=64),
+    # few assignments (the rank top-k and one-wave dispatch): one token over 256 experts, and
+    # exactly 64 assignments over 32 experts
+    "e256_t1_k8": W("e256_t1_k8", T=1, H=64, E=256, k=8, I=32),
+    "n64_e32": W("n64_e32", T=8, H=64, E=32, k=8, I=32, S=1, Is=32),
     # 8-bit expert weights: Q8_0 blocks with a partly filled last step (9 and 5 blocks per row),
     # fp8 rows whose length is 32 past a multiple of 64 (a half-filled last step)
     "q8_small_t5": W("q8_small_t5", T=5, H=288, E=64, k=8, I=160, S=1, Is=96,
@@ -160,7 +164,8 @@ def test_empty_batch_is_noop(m):
 
 @pytest.mark.parametrize("name", ["mixtral_small_bf16", "qwen_small_q4_t5", "deepseek_small_t40",
                                   "prefill_small_zipf", "k_equals_E", "tiny_f32", "e20_k12", "e256_k70",
-                                  "n10k_prefill", "e40_k10"])
+                                  "n10k_prefill", "e40_k10", "e256_t1_k8", "n64_e32", "qwen_small_q4_t1",
+                                  "t1_k1"])
 def test_route_bit_exact(m, name):
     wl = SMALL[name]
     inp = _inputs(wl, 4)
@@ -176,6 +181,21 @@ def test_route_bit_exact(m, name):
         assert np.array_equal(r[key], d[key]), key
     act = r["active"]
     assert act[0] == len(d["active"]) and np.array_equal(act[1:1 + act[0]], d["active"])
+
+
+@pytest.mark.parametrize("T, E, k", [(1, 256, 8), (3, 64, 8), (4, 8, 2), (40, 16, 6), (5, 256, 70)])
+def test_equal_logits_pick_lowest_indices(m, T, E, k):
+    """All logits equal (zero router weights, no bias): every token takes experts
+    0..k-1 in index order with weight 1/k, on each selection strategy."""
+    wl = W(f"ties_{T}_{E}_{k}", T=T, H=64, E=E, k=k, I=32)
+    inp = _inputs(wl, 7)
+    inp["router_w"] = np.zeros_like(inp["router_w"])
+    r = H.run_route(m, wl, synth.to_torch(inp))
+    assert np.array_equal(r["topk_ids"], np.tile(np.arange(k), (T, 1)))
+    assert np.allclose(r["topk_w"], 1.0 / k, rtol=1e-6)
+    d = oracle.dispatch(r["topk_ids"].astype(np.int64), E, r["tile_m"])
+    for key in ("counts", "offsets", "sorted_ids", "tile_expert", "inv"):
+        assert np.array_equal(r[key], d[key]), key
 
 
 @pytest.mark.parametrize("path", [1, 3])
