@@ -25,6 +25,7 @@ hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, 
 
 namespace {
 
+constexpr int kEpilogueMaxSlots = 16;   // decode: expert slots per output row group for the combine epilogue
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
 constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
@@ -42,6 +43,7 @@ struct Layout {
   int cap, n_tiles;    // sorted-order capacity and tiles for Tr tokens
   size_t logits, topk_ids, topk_w, counts, offsets, cprefix, active, sorted_ids, tile_expert, inv;
   size_t h, partials, acc;
+  size_t dn_count;     // multi-launch decode: down arrival counters [H / 16, rounded up to 4]
   size_t flags, error;  // single-launch decode: completion flags [n_items], error tag
   long n_items;
   long h_plane;
@@ -152,6 +154,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     const size_t elem = (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16) ? 4 : 2;
     L.h = take(size_t(L.h_plane) * elem);
     L.partials = take(size_t(rows) * H * 4);
+    L.dn_count = take(size_t(roundup(H / 16, 4)) * 4);
     if (L.path == MOE_PATH_DECODE_FUSED) {
       L.n_items = fused_plan(s, Tr).n_items;
       L.flags = take(size_t(L.n_items) * 8);
@@ -386,6 +389,9 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.h_stride = L.h_stride;
     d.partials = reinterpret_cast<float*>(ws + L.partials);
     d.out = oc;
+    // combine in the down launch's epilogue when few work-groups write each output row group
+    // (their arrival counts serialise on one counter per group); else in a launch of its own
+    d.dn_count = d.n_routed_slots + d.S <= kEpilogueMaxSlots ? reinterpret_cast<unsigned*>(ws + L.dn_count) : nullptr;
     const int n_gu_rt = (std::max(s->I, d.Is) + 15) / 16;
     d.n_row_tiles = n_gu_rt;
     sev.mark(st);
@@ -404,6 +410,10 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
     ra.logit_parts = (nblocks > 1 && nblocks < 64) ? 4 : 1;
+    if (d.dn_count) {             // the router launch clears the down launch's arrival counters
+      ra.zero_f32 = reinterpret_cast<float*>(d.dn_count);
+      ra.zero_n = roundup(s->H / 16, 4);
+    }
     if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))

@@ -231,6 +231,18 @@ __device__ __forceinline__ int32_t ld_i32(const int32_t* p) {
   else return *p;
 }
 template <bool COH>
+__device__ __forceinline__ f32x4_t ld_f32x4(const float* p) {
+  if constexpr (COH) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4_t{__uint_as_float(uint32_t(lo)), __uint_as_float(uint32_t(lo >> 32)), __uint_as_float(uint32_t(hi)),
+                   __uint_as_float(uint32_t(hi >> 32))};
+  } else {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  }
+}
+template <bool COH>
 __device__ __forceinline__ float ld_f32(const float* p) {
   if constexpr (COH)
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
@@ -287,6 +299,7 @@ struct DecodeArgs {
   int h_stride;         // elements per h row
   float* partials;      // down: [T*k + S*T][H] weighted expert output rows
   void* out;            // [T, H]
+  unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
 };
 
 // Single-launch decode: one work list of items in a fixed order, taken

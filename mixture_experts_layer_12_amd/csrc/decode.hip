@@ -12,10 +12,13 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
 }
 
-template <int WT, int NCT, int RPW>
+// OT >= 0: with the combine epilogue, outputs of dtype OT (partials stored
+// with device-scope stores); OT < 0: partials only.
+template <int WT, int NCT, int RPW, int OT>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][RPW * NCT][64];
-  down_item<WT, NCT, false, RPW>(a, blockIdx.x, blockIdx.y, red);
+  down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red);
+  if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, blockIdx.y, RPW * 16);
 }
 
 // Row tiles of 16 outputs per down-projection work-group: two when the
@@ -24,15 +27,16 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
 #ifndef MOE_DN_RPW
 #define MOE_DN_RPW 2
 #endif
-template <int WT, int NCT>
+template <int WT, int NCT, int OT>
 static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
   constexpr int R = NCT == 1 ? MOE_DN_RPW : 1;
   if (R >= 4 && a.H % 64 == 0)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R, OT>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
   else if (R >= 2 && a.H % 32 == 0)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1)>), dim3(a.H / 32, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1), OT>), dim3(a.H / 32, n_slots), dim3(256), 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
 }
 
 template <int OT>
@@ -42,14 +46,20 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 
 // -------------------------------------------------------------- launch --
 
+// With a.dn_count the combine runs in the down launch's epilogue; without,
+// in a launch of its own.
 template <int WT, int XT, int NCT>
 static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
-  launch_down<WT, NCT>(a, a.n_routed_slots + a.S, st);
-  const long n4 = long(a.T) * a.H / 4;
-  hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n4 + 255) / 256)), b, 0, st, a);
+  if (a.dn_count) {
+    launch_down<WT, NCT, XT>(a, a.n_routed_slots + a.S, st);
+  } else {
+    launch_down<WT, NCT, -1>(a, a.n_routed_slots + a.S, st);
+    const long n4 = long(a.T) * a.H / 4;
+    hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n4 + 255) / 256)), b, 0, st, a);
+  }
   if (mark) mark->mark(st);
 }
 
@@ -64,7 +74,7 @@ static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
 template <int WT, int XT, int NCT>
 static void launch_shared_t(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
-  launch_down<WT, NCT>(a, a.S, st);
+  launch_down<WT, NCT, -1>(a, a.S, st);
 }
 
 template <int WT, int XT>
@@ -75,7 +85,7 @@ static void launch_shared_x(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
-  if (a.n_routed_slots != 0) return hipErrorInvalidValue;
+  if (a.n_routed_slots != 0 || a.dn_count) return hipErrorInvalidValue;
   if (wdt == DT_F32) {
     if (xdt == DT_F32) launch_shared_x<DT_F32, DT_F32>(a, st);
     else launch_shared_x<DT_F32, DT_BF16>(a, st);

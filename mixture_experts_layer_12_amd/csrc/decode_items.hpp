@@ -587,7 +587,9 @@ struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 // expert outputs; they go to `partials` at the same row the activations use
 // (one row per routed assignment, then the shared tokens).  `red` holds
 // [4 waves][RPW * NCT][64] accumulators.
-template <int WT, int NCT, bool COH, int RPW = 1>
+// CST: the partial rows are stored with device-scope stores (read by another
+// work-group of the same launch); COH implies it.
+template <int WT, int NCT, bool COH, int RPW = 1, bool CST = COH>
 __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
@@ -677,7 +679,7 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
       const int c = ct * 16 + (lane & 15);
       if (c >= n_e) continue;
       // lane holds rows 4*(lane/16) + 0..3 of row tile r for token column c
-      st_f32x4<COH>(a.partials + size_t(hrow0 + c) * H + row0 + r * 16 + (lane >> 4) * 4, v * sd_rows[r]);
+      st_f32x4<COH || CST>(a.partials + size_t(hrow0 + c) * H + row0 + r * 16 + (lane >> 4) * 4, v * sd_rows[r]);
     }
 }
 
@@ -694,6 +696,41 @@ __device__ __forceinline__ void combine_item(const DecodeArgs a, long i4) {
   for (int s = 0; s < a.S; ++s) v += p[size_t(a.T * a.k + s * a.T + t) * H4 + h4];
   if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
   else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+
+// Combine epilogue of the down projection.  The work-groups writing partial
+// rows into output row group rt (`rows` outputs wide) are the A active
+// routed slots and the S shared ones; each counts in once its device-scope
+// stores of the partials have completed, and the last to count in sums, for
+// every token, the k routed rows and the S shared rows in the order of
+// combine_item (same bits) and writes the outputs.  Ordinary loads read the
+// current rows: the writers stored them with device-scope stores, and each
+// 128-byte line of a row group is written by one work-group only, so no
+// cache on the reader's side can hold an older copy.  dn_count[rt] is zeroed
+// by the router launch of the same pass.
+template <int OT>
+__device__ __forceinline__ void down_combine(const DecodeArgs a, int rt, int slot, int rows) {
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int A = ld_i32<false>(a.active);                    // written by an earlier launch
+  if (slot < a.n_routed_slots && slot >= A) return;          // this work-group wrote nothing
+  if (tid < 64) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // wave 0 stored the partials
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(a.dn_count + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           unsigned(A + a.S - 1);
+  __syncthreads();
+  if (!last) return;
+  const int H = a.H, r4 = rows / 4;
+  for (int i = tid; i < a.T * r4; i += blockDim.x) {
+    const int t = i / r4, h = rt * rows + 4 * (i - t * r4);
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) v += ld_f32x4<false>(a.partials + size_t(a.inv[t * a.k + j]) * H + h);
+    for (int s = 0; s < a.S; ++s) v += ld_f32x4<false>(a.partials + size_t(a.T * a.k + s * a.T + t) * H + h);
+    const long o = (long(t) * H + h) / 4;
+    if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[o] = v;
+    else reinterpret_cast<u32x2_t*>(a.out)[o] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  }
 }
 
 }  // namespace moe
