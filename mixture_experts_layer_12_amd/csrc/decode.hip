@@ -6,18 +6,31 @@ namespace moe {
 
 // ------------------------------------------------------------- kernels --
 
-template <int WT, int XT, int NCT>
+// PASSES: slots with more tokens than the NCT column tiles take further
+// passes over the same weight rows (served from cache); without, one pass
+// (every slot fits: the loop would only cost registers).
+template <int WT, int XT, int NCT, bool PASSES>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
-  gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
+  if constexpr (PASSES) {
+    for (int c0 = 0; gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red, c0); c0 += 16 * NCT)
+      __syncthreads();
+  } else {
+    gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
+  }
 }
 
 // OT >= 0: with the combine epilogue, outputs of dtype OT (partials stored
 // with device-scope stores); OT < 0: partials only.
-template <int WT, int NCT, int RPW, int OT>
+template <int WT, int NCT, int RPW, int OT, bool PASSES>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][RPW * NCT][64];
-  down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red);
+  if constexpr (PASSES) {
+    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red, c0); c0 += 16 * NCT)
+      __syncthreads();
+  } else {
+    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red);
+  }
   if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, blockIdx.y, RPW * 16);
 }
 
@@ -27,16 +40,16 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
 #ifndef MOE_DN_RPW
 #define MOE_DN_RPW 2
 #endif
-template <int WT, int NCT, int OT>
+template <int WT, int NCT, int OT, bool PASSES>
 static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
   constexpr int R = NCT == 1 ? MOE_DN_RPW : 1;
   if (R >= 4 && a.H % 64 == 0)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R, OT>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R, OT, PASSES>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
   else if (R >= 2 && a.H % 32 == 0)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1), OT>), dim3(a.H / 32, n_slots), dim3(256), 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1), OT, PASSES>), dim3(a.H / 32, n_slots), dim3(256),
+                       0, st, a);
   else
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT, PASSES>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
 }
 
 template <int OT>
@@ -48,33 +61,37 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 
 // With a.dn_count the combine runs in the down launch's epilogue; without,
 // in a launch of its own.
-template <int WT, int XT, int NCT>
+template <int WT, int XT, int NCT, bool PASSES>
 static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
-  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), g1, b, 0, st, a);
+  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, PASSES>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
   if (a.dn_count) {
-    launch_down<WT, NCT, XT>(a, a.n_routed_slots + a.S, st);
+    launch_down<WT, NCT, XT, PASSES>(a, a.n_routed_slots + a.S, st);
   } else {
-    launch_down<WT, NCT, -1>(a, a.n_routed_slots + a.S, st);
+    launch_down<WT, NCT, -1, PASSES>(a, a.n_routed_slots + a.S, st);
     const long n4 = long(a.T) * a.H / 4;
     hipLaunchKernelGGL((decode_combine_kernel<XT>), dim3(int((n4 + 255) / 256)), b, 0, st, a);
   }
   if (mark) mark->mark(st);
 }
 
+// One 16-token column tile per pass unless the routed slots average more than
+// 8 tokens: the one-tile kernels keep more weight bytes in flight per wave,
+// and the rare slot with more tokens takes another pass.
 template <int WT, int XT>
 static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
-  if (a.T <= 16) launch_decode_t<WT, XT, 1>(a, n_gu_row_tiles, st, mark);
-  else launch_decode_t<WT, XT, 4>(a, n_gu_row_tiles, st, mark);
+  if (a.T <= 16) launch_decode_t<WT, XT, 1, false>(a, n_gu_row_tiles, st, mark);
+  else if (a.T * a.k <= 8 * a.E) launch_decode_t<WT, XT, 1, true>(a, n_gu_row_tiles, st, mark);
+  else launch_decode_t<WT, XT, 4, false>(a, n_gu_row_tiles, st, mark);
 }
 
 // Gate/up and down of the shared experts only (a.n_routed_slots must be 0):
 // rows T*k + s*T + t of h and of the partials, as in the full decode pass.
 template <int WT, int XT, int NCT>
 static void launch_shared_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
-  launch_down<WT, NCT, -1>(a, a.S, st);
+  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, false>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
+  launch_down<WT, NCT, -1, false>(a, a.S, st);
 }
 
 template <int WT, int XT>

@@ -375,16 +375,20 @@ struct GUStep { AFrag<WT> g, u; XRaw<Fam<WT>::v, XT> x[NCT]; };
 // ------------------------------------------------------------- gate/up --
 
 // One work-group: 16 intermediate rows (gate and up) of one expert slot, for
-// every token of that slot; `red` is LDS for the cross-wave sums.
+// the slot's token columns [c0, c0 + 16 * NCT); `red` is LDS for the
+// cross-wave sums.  Returns whether the slot has columns past these (the
+// caller then runs another pass after a barrier); every thread returns the
+// same value.
 template <int WT, int XT, int NCT, bool COH>
-__device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[2 * NCT][64]) {
+__device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[2 * NCT][64],
+                                            int c0 = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   int e, n_e, hrow0, N, seg = 0;
   long n_mat;
   const uint8_t *bg, *bu;
   if (routed) {
-    if (slot >= ld_i32<COH>(a.active)) return;
+    if (slot >= ld_i32<COH>(a.active)) return false;
     e = ld_i32<COH>(a.active + 1 + slot);
     n_e = ld_i32<COH>(a.counts + e);
     seg = ld_i32<COH>(a.offsets + e);
@@ -396,7 +400,7 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
     hrow0 = a.T * a.k + e * a.T;
     N = a.Is; bg = a.sg; bu = a.su; n_mat = a.S;
   }
-  if (rt * 16 >= N) return;
+  if (rt * 16 >= N) return false;
   constexpr int F = Fam<WT>::v;
   const int K = a.H, g = lane >> 4;
   RowPtr<WT> rg, ru;
@@ -416,13 +420,13 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
   bool xok[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
+    const int c = c0 + ct * 16 + (lane & 15);
     xok[ct] = c < n_e;
     int tok = 0;
     if (xok[ct]) tok = routed ? ld_i32<COH>(a.sorted_ids + seg + c) / a.k : c;
     xrow[ct] = reinterpret_cast<const uint8_t*>(a.x) + size_t(tok) * K * xb;
   }
-  const int nct = (n_e + 15) >> 4;
+  const int nct = (n_e - c0 + 15) >> 4;
 
   const int nsteps = n_steps<WT>(K);
   const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
@@ -461,7 +465,8 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
     red[wave][NCT + ct][lane] = accu[ct];
   }
   __syncthreads();
-  if (wave != 0) return;
+  const bool more = c0 + 16 * NCT < n_e;
+  if (wave != 0) return more;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     if (!(NCT == 1 || ct < nct)) continue;
@@ -471,7 +476,7 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
       gs += red[w][ct][lane];
       us += red[w][NCT + ct][lane];
     }
-    const int c = ct * 16 + (lane & 15);
+    const int c = c0 + ct * 16 + (lane & 15);
     if (c >= n_e) continue;
     const float wr = routed ? ld_f32<COH>(a.topk_w + ld_i32<COH>(a.sorted_ids + seg + c)) : 1.0f;
     float hv[4];
@@ -492,6 +497,7 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs a, int rt, int slot
       st_u32x2<COH>(hp + off, u32x2_t{pack_f16(hv[0], hv[1]), pack_f16(hv[2], hv[3])});
     }
   }
+  return more;
 }
 
 // ---------------------------------------------------------------- down --
@@ -579,7 +585,8 @@ template <int WT, int NCT, int RPW>
 struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 
 // One work-group: RPW x 16 hidden outputs (rows of the down projection) of
-// one expert slot, for every token of that slot.  Its 4 waves split the
+// one expert slot, for the slot's token columns [c0, c0 + 16 * NCT) (returns
+// whether more follow, as gateup_item).  Its 4 waves split the
 // slot's intermediate dimension; partial sums meet in LDS.  A wave's RPW row
 // tiles share each activation fragment it loads, which cuts the activation
 // loads per weight byte by RPW (they otherwise add a fifth of the weight
@@ -590,14 +597,15 @@ struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 // CST: the partial rows are stored with device-scope stores (read by another
 // work-group of the same launch); COH implies it.
 template <int WT, int NCT, bool COH, int RPW = 1, bool CST = COH>
-__device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64]) {
+__device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64],
+                                          int c0 = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   int e, n_e, hrow0, K;
   long n_mat;
   const uint8_t* base;
   if (routed) {
-    if (slot >= ld_i32<COH>(a.active)) return;
+    if (slot >= ld_i32<COH>(a.active)) return false;
     e = ld_i32<COH>(a.active + 1 + slot);
     n_e = ld_i32<COH>(a.counts + e);
     hrow0 = ld_i32<COH>(a.cprefix + e);
@@ -625,11 +633,11 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
   bool hok[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
+    const int c = c0 + ct * 16 + (lane & 15);
     hok[ct] = c < n_e;
     hoff[ct] = size_t(hrow0 + (hok[ct] ? c : 0)) * a.h_stride;
   }
-  const int nct = (n_e + 15) >> 4;
+  const int nct = (n_e - c0 + 15) >> 4;
   const int nsteps = n_steps<WT>(K);
   const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
   f32x4_t acc[RPW][NCT];
@@ -667,7 +675,8 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) red[wave][r * NCT + ct][lane] = acc[r][ct];
   __syncthreads();
-  if (wave != 0) return;
+  const bool more = c0 + 16 * NCT < n_e;
+  if (wave != 0) return more;
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -676,11 +685,12 @@ __device__ __forceinline__ void down_item(const DecodeArgs a, int rt, int slot, 
       f32x4_t v = red[0][r * NCT + ct][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) v += red[w][r * NCT + ct][lane];
-      const int c = ct * 16 + (lane & 15);
+      const int c = c0 + ct * 16 + (lane & 15);
       if (c >= n_e) continue;
       // lane holds rows 4*(lane/16) + 0..3 of row tile r for token column c
       st_f32x4<COH || CST>(a.partials + size_t(hrow0 + c) * H + row0 + r * 16 + (lane >> 4) * 4, v * sd_rows[r]);
     }
+  return more;
 }
 
 // out[t] = sum over j of the partial row of assignment t*k + j (found through

@@ -48,6 +48,9 @@ SMALL = {
     # exactly 64 assignments over 32 experts
     "e256_t1_k8": W("e256_t1_k8", T=1, H=64, E=256, k=8, I=32),
     "n64_e32": W("n64_e32", T=8, H=64, E=32, k=8, I=32, S=1, Is=32),
+    # more than 16 tokens with few per expert: one-column-tile kernels with extra passes (the shared
+    # slot takes three)
+    "e32_t40_passes": W("e32_t40_passes", T=40, H=160, E=32, k=2, I=96, S=1, Is=64),
     # 8-bit expert weights: Q8_0 blocks with a partly filled last step (9 and 5 blocks per row),
     # fp8 rows whose length is 32 past a multiple of 64 (a half-filled last step)
     "q8_small_t5": W("q8_small_t5", T=5, H=288, E=64, k=8, I=160, S=1, Is=96,
