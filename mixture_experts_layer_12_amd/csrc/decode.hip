@@ -6,17 +6,25 @@ namespace moe {
 
 // ------------------------------------------------------------- kernels --
 
+// Slot of a work-group row: the shared experts' rows of the grid come first,
+// so that their work-groups (every token, hence the most columns) start with
+// the first wave of the grid instead of forming its tail.
+__device__ __forceinline__ int grid_slot(const DecodeArgs& a) {
+  const int y = blockIdx.y;
+  return y < a.S ? a.n_routed_slots + y : y - a.S;
+}
+
 // PASSES: slots with more tokens than the NCT column tiles take further
 // passes over the same weight rows (served from cache); without, one pass
 // (every slot fits: the loop would only cost registers).
 template <int WT, int XT, int NCT, bool PASSES>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
+  const int slot = grid_slot(a);
   if constexpr (PASSES) {
-    for (int c0 = 0; gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red, c0); c0 += 16 * NCT)
-      __syncthreads();
+    for (int c0 = 0; gateup_item<WT, XT, NCT, false>(a, blockIdx.x, slot, red, c0); c0 += 16 * NCT) __syncthreads();
   } else {
-    gateup_item<WT, XT, NCT, false>(a, blockIdx.x, blockIdx.y, red);
+    gateup_item<WT, XT, NCT, false>(a, blockIdx.x, slot, red);
   }
 }
 
@@ -25,13 +33,14 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
 template <int WT, int NCT, int RPW, int OT, bool PASSES>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][RPW * NCT][64];
+  const int slot = grid_slot(a);
   if constexpr (PASSES) {
-    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red, c0); c0 += 16 * NCT)
+    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, slot, red, c0); c0 += 16 * NCT)
       __syncthreads();
   } else {
-    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, blockIdx.y, red);
+    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, slot, red);
   }
-  if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, blockIdx.y, RPW * 16);
+  if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, slot, RPW * 16);
 }
 
 // Row tiles of 16 outputs per down-projection work-group: two when the
