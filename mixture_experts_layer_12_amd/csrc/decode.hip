@@ -43,16 +43,17 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, slot, RPW * 16);
 }
 
-// Row tiles of 16 outputs per down-projection work-group: two when the
-// token columns fit one MFMA tile (they share every activation load).  Four
-// measured slower: too few work-groups for the memory stream.
+// Row tiles of 16 outputs per down-projection work-group when the token
+// columns fit one MFMA tile (the tiles share every activation load): four
+// while that still leaves at least 2048 work-groups, else two (fewer
+// work-groups starve the memory stream).
 #ifndef MOE_DN_RPW
-#define MOE_DN_RPW 2
+#define MOE_DN_RPW 4
 #endif
 template <int WT, int NCT, int OT, bool PASSES>
 static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
   constexpr int R = NCT == 1 ? MOE_DN_RPW : 1;
-  if (R >= 4 && a.H % 64 == 0)
+  if (R >= 4 && a.H % 64 == 0 && (a.H / 64) * n_slots >= 2048)
     hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R, OT, PASSES>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
   else if (R >= 2 && a.H % 32 == 0)
     hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1), OT, PASSES>), dim3(a.H / 32, n_slots), dim3(256),

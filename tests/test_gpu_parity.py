@@ -51,6 +51,9 @@ SMALL = {
     # more than 16 tokens with few per expert: one-column-tile kernels with extra passes (the shared
     # slot takes three)
     "e32_t40_passes": W("e32_t40_passes", T=40, H=160, E=32, k=2, I=96, S=1, Is=64),
+    # down work-groups of four row tiles (the grid keeps >= 2048 of them), with and without passes
+    "rpw4_t16": W("rpw4_t16", T=16, H=1024, E=128, k=8, I=64),
+    "rpw4_t24_passes": W("rpw4_t24_passes", T=24, H=2048, E=128, k=4, I=64, S=1, Is=64),
     # 8-bit expert weights: Q8_0 blocks with a partly filled last step (9 and 5 blocks per row),
     # fp8 rows whose length is 32 past a multiple of 64 (a half-filled last step)
     "q8_small_t5": W("q8_small_t5", T=5, H=288, E=64, k=8, I=160, S=1, Is=96,
