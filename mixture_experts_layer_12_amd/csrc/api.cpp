@@ -106,7 +106,7 @@ moe::FusedArgs fused_plan(const moe_shape_t* s, int Tc) {
   f.end_shared_gu = f.n_logit + S * f.gu_rt_shared;
   f.end_select = f.end_shared_gu + 1;
   f.end_gu = f.end_select + n_slots * f.gu_rt_routed;
-  f.end_down = f.end_gu + (n_slots + S) * (s->H / 16);
+  f.end_down = f.end_gu + (n_slots + S) * (s->H / (Tc <= 16 ? moe::kFusedDownRows<1> : moe::kFusedDownRows<4>));
   f.n_items = f.end_down + int((long(Tc) * s->H / 4 + 255) / 256);
   return f;
 }

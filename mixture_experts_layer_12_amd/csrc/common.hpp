@@ -302,6 +302,11 @@ struct DecodeArgs {
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
 };
 
+// Output rows per down item of the single-launch decode: two row tiles when
+// the tokens fit one column tile (H is a multiple of 32), else one.
+template <int NCT>
+constexpr int kFusedDownRows = NCT == 1 ? 32 : 16;
+
 // Single-launch decode: one work list of items in a fixed order, taken
 // round-robin by a co-resident grid; an item waits only on items of lower
 // index (completion flags carry the call's epoch).
@@ -312,7 +317,7 @@ struct FusedArgs {
   int end_shared_gu;    // [n_logit, end_shared_gu): shared-expert gate/up row tiles
   int end_select;       // end_shared_gu: top-k and dispatch (one item)
   int end_gu;           // [end_select, end_gu): routed gate/up row tiles, slot-major
-  int end_down;         // [end_gu, end_down): down row tiles, slot-major, routed then shared
+  int end_down;         // [end_gu, end_down): down row groups (kFusedDownRows), slot-major, routed then shared
   int n_items;          // [end_down, n_items): combine blocks of 1024 outputs
   int gu_rt_routed, gu_rt_shared;   // gate/up row tiles per routed / shared slot
   unsigned long long epoch;

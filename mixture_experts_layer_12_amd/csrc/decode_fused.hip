@@ -20,7 +20,7 @@
 //   [n_logit, end_shared_gu)     shared-expert gate/up row tiles
 //   end_shared_gu                top-k, renormalisation, dispatch (one item)
 //   [end_select, end_gu)         routed gate/up row tiles, slot-major
-//   [end_gu, end_down)           down row tiles, slot-major (routed, then shared)
+//   [end_gu, end_down)           down row groups of kFusedDownRows outputs, slot-major (routed, then shared)
 //   [end_down, n_items)          combine, 1024 outputs per item
 // An item waits only on items of lower index, and every work-group takes its
 // items in increasing order, so the lowest unfinished item can always run.
@@ -80,8 +80,9 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
   extern __shared__ __attribute__((aligned(16))) int smem[];
   const DecodeArgs a = f.d;
   auto* red_gu = reinterpret_cast<f32x4_t(*)[2 * NCT][64]>(smem);
-  auto* red_dn = reinterpret_cast<f32x4_t(*)[NCT][64]>(smem);
-  const int nrt_down = a.H / 16;
+  constexpr int RPW = kFusedDownRows<NCT> / 16;
+  auto* red_dn = reinterpret_cast<f32x4_t(*)[RPW * NCT][64]>(smem);
+  const int nrt_down = a.H / (16 * RPW);
   for (int i = blockIdx.x; i < f.n_items; i += gridDim.x) {
     if (i < f.n_logit) {      // one group of 4 chunks of one tile -> its partial plane
       const int tile = i >> 2, q = i & 3;
@@ -113,7 +114,7 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
         const int b = f.n_logit + (slot - a.n_routed_slots) * f.gu_rt_shared;
         wait_items(f, b, b + f.gu_rt_shared);
       }
-      down_item<WT, NCT, true>(a, rt, slot, red_dn);
+      down_item<WT, NCT, true, RPW>(a, rt, slot, red_dn);
     } else {
       wait_items(f, f.end_gu, f.end_down);
       const long i4 = long(i - f.end_down) * kFusedThreads + threadIdx.x;

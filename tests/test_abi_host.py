@@ -110,8 +110,9 @@ def test_single_launch_decode_workspace(m):
     fused = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE_FUSED))
     multi = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE))
 
-    # work list: 1 logits tile, 1 selection, 8 x 896 gate/up tiles, 8 x 256 down tiles, 32 combine blocks
-    n_items = 1 + 1 + 8 * 896 + 8 * 256 + 32
+    # work list: 4 logits planes, 1 selection, 8 x 896 gate/up tiles, 8 x 128 down row groups (32 outputs
+    # each), 32 combine blocks
+    n_items = 4 + 1 + 8 * 896 + 8 * 128 + 32
     assert fused - multi >= n_items * 8
 
 
