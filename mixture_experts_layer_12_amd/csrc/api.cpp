@@ -15,7 +15,7 @@
 #include "common.hpp"
 
 namespace moe {
-hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st);
+hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st, bool logits_only = false);
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark);
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
@@ -26,6 +26,7 @@ hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, 
 namespace {
 
 constexpr int kEpilogueMaxSlots = 16;   // decode: expert slots per output row group for the combine epilogue
+constexpr long kRouteInGateUpMaxGroups = 1024;   // decode: gate/up grids that select in their own prologue
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
 constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
@@ -408,13 +409,23 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       continue;
     }
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
+    // Few assignments and a small gate/up grid: the router launch computes the logits only, and
+    // every routed gate/up work-group selects and dispatches in its prologue (one launch fewer
+    // on the critical path of a latency-bound layer; larger grids would repeat it too often).
+    const bool pro = Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
+                     long(n_gu_rt) * (d.n_routed_slots + d.S) <= kRouteInGateUpMaxGroups;
     // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
-    ra.logit_parts = (nblocks > 1 && nblocks < 64) ? 4 : 1;
+    ra.logit_parts = (nblocks < 64 && (pro || nblocks > 1)) ? 4 : 1;
     if (d.dn_count) {             // the router launch clears the down launch's arrival counters
       ra.zero_f32 = reinterpret_cast<float*>(d.dn_count);
       ra.zero_n = roundup(s->H / 16, 4);
     }
-    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
+    if (pro) {
+      d.route_in_gu = 1;
+      d.route = ra;
+    }
+    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st, pro)))
+      return e;
     sev.mark(st);
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))
       return e;

@@ -256,6 +256,16 @@ struct StageMarker {
   virtual ~StageMarker() = default;
 };
 
+// Few assignments (decode): at most kSmallN of them (T * k), T * E <= 1024 and
+// T * E * E <= kRankWork take the few-assignment route (route_small).
+constexpr int kSmallN = 64;
+constexpr int kRankWork = 65536;
+constexpr int kSmallDispInts = 3 * 64 + 2 * 65 + 1;    // slot tables of the one-wave dispatch
+
+__host__ __device__ inline bool small_route(int T, int E, int k) {
+  return T * k <= kSmallN && T * E <= 1024 && long(T) * E * E <= kRankWork;
+}
+
 // ------------------------------------------------------ kernel arguments --
 
 // Routing state inside the workspace (or caller buffers for moe_route).
@@ -300,6 +310,8 @@ struct DecodeArgs {
   float* partials;      // down: [T*k + S*T][H] weighted expert output rows
   void* out;            // [T, H]
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
+  int route_in_gu;      // 1: the routed gate/up work-groups select and dispatch from the logits themselves
+  RouterArgs route;     // ... with these arguments (logits in route.rb.logits)
 };
 
 // Output rows per down item of the single-launch decode: two row tiles when

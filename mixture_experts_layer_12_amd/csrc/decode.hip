@@ -17,10 +17,27 @@ __device__ __forceinline__ int grid_slot(const DecodeArgs& a) {
 // PASSES: slots with more tokens than the NCT column tiles take further
 // passes over the same weight rows (served from cache); without, one pass
 // (every slot fits: the loop would only cost registers).
-template <int WT, int XT, int NCT, bool PASSES>
+// PRO: a.route_in_gu; every routed work-group first selects and dispatches
+// from the logits in LDS (dynamic LDS of small_route_ints(256, ...) ints) and
+// takes its slot's routing from there; the one of slot 0, row tile 0 also
+// writes the routing tables for the down launch.  One pass.
+template <int WT, int XT, int NCT, bool PASSES, bool PRO>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
   const int slot = grid_slot(a);
+  if constexpr (PRO) {
+    extern __shared__ __attribute__((aligned(16))) int lds[];
+    if (slot < a.n_routed_slots) {
+      const SmallRoute R(lds, a.route.T, a.route.E, a.route.k);
+      const bool writer = blockIdx.x == 0 && slot == 0;
+      int rk, fslot;
+      small_select<false>(a.route, a.route.rb.logits, false, R);
+      small_place<false>(a.route, R, writer, rk, fslot);
+      if (writer) small_tables<false>(a.route, R, rk, fslot);
+      gateup_item<WT, XT, NCT, false, true>(a, blockIdx.x, slot, red, 0, &R);
+      return;
+    }
+  }
   if constexpr (PASSES) {
     for (int c0 = 0; gateup_item<WT, XT, NCT, false>(a, blockIdx.x, slot, red, c0); c0 += 16 * NCT) __syncthreads();
   } else {
@@ -74,7 +91,11 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 template <int WT, int XT, int NCT, bool PASSES>
 static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
-  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, PASSES>), g1, b, 0, st, a);
+  if (NCT == 1 && !PASSES && a.route_in_gu)
+    hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, 1, false, true>), g1, b,
+                       size_t(small_route_ints(256, a.T, a.E, a.k)) * 4, st, a);
+  else
+    hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, PASSES, false>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
   if (a.dn_count) {
     launch_down<WT, NCT, XT, PASSES>(a, a.n_routed_slots + a.S, st);
@@ -100,7 +121,7 @@ static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
 // rows T*k + s*T + t of h and of the partials, as in the full decode pass.
 template <int WT, int XT, int NCT>
 static void launch_shared_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, false>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, false, false>), dim3(a.n_row_tiles, a.S), dim3(256), 0, st, a);
   launch_down<WT, NCT, -1, false>(a, a.S, st);
 }
 
@@ -112,7 +133,7 @@ static void launch_shared_x(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
-  if (a.n_routed_slots != 0 || a.dn_count) return hipErrorInvalidValue;
+  if (a.n_routed_slots != 0 || a.dn_count || a.route_in_gu) return hipErrorInvalidValue;
   if (wdt == DT_F32) {
     if (xdt == DT_F32) launch_shared_x<DT_F32, DT_F32>(a, st);
     else launch_shared_x<DT_F32, DT_BF16>(a, st);
@@ -127,6 +148,7 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
 
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
+  if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
   if (wdt == DT_F32) {
     if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, n_gu_row_tiles, st, mark);
     else launch_decode_x<DT_F32, DT_BF16>(a, n_gu_row_tiles, st, mark);

@@ -37,6 +37,7 @@
 // activations; fp32 weights use the fp32 MFMA.
 #pragma once
 #include "common.hpp"
+#include "router_items.hpp"
 
 namespace moe {
 
@@ -379,20 +380,29 @@ struct GUStep { AFrag<WT> g, u; XRaw<Fam<WT>::v, XT> x[NCT]; };
 // cross-wave sums.  Returns whether the slot has columns past these (the
 // caller then runs another pass after a barrier); every thread returns the
 // same value.
-template <int WT, int XT, int NCT, bool COH>
+// PRO: the routing of routed slots comes from the work-group's own selection
+// in LDS (`R`, tile_m 1) instead of the tables in memory.
+template <int WT, int XT, int NCT, bool COH, bool PRO = false>
 __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[2 * NCT][64],
-                                            int c0 = 0) {
+                                            int c0 = 0, const SmallRoute* R = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   int e, n_e, hrow0, N, seg = 0;
   long n_mat;
   const uint8_t *bg, *bu;
   if (routed) {
-    if (slot >= ld_i32<COH>(a.active)) return false;
-    e = ld_i32<COH>(a.active + 1 + slot);
-    n_e = ld_i32<COH>(a.counts + e);
-    seg = ld_i32<COH>(a.offsets + e);
-    hrow0 = ld_i32<COH>(a.cprefix + e);
+    if constexpr (PRO) {
+      if (slot >= R->s_na[0]) return false;
+      e = R->s_e[slot];
+      n_e = R->s_cnt[slot];
+      seg = hrow0 = R->s_cpre[slot];
+    } else {
+      if (slot >= ld_i32<COH>(a.active)) return false;
+      e = ld_i32<COH>(a.active + 1 + slot);
+      n_e = ld_i32<COH>(a.counts + e);
+      seg = ld_i32<COH>(a.offsets + e);
+      hrow0 = ld_i32<COH>(a.cprefix + e);
+    }
     N = a.I; bg = a.wg; bu = a.wu; n_mat = a.E;
   } else {
     e = slot - a.n_routed_slots;
@@ -423,7 +433,10 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
     const int c = c0 + ct * 16 + (lane & 15);
     xok[ct] = c < n_e;
     int tok = 0;
-    if (xok[ct]) tok = routed ? ld_i32<COH>(a.sorted_ids + seg + c) / a.k : c;
+    if (xok[ct]) {
+      if constexpr (PRO) tok = routed ? R->sorted[seg + c] / a.k : c;
+      else tok = routed ? ld_i32<COH>(a.sorted_ids + seg + c) / a.k : c;
+    }
     xrow[ct] = reinterpret_cast<const uint8_t*>(a.x) + size_t(tok) * K * xb;
   }
   const int nct = (n_e - c0 + 15) >> 4;
@@ -478,7 +491,12 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
     }
     const int c = c0 + ct * 16 + (lane & 15);
     if (c >= n_e) continue;
-    const float wr = routed ? ld_f32<COH>(a.topk_w + ld_i32<COH>(a.sorted_ids + seg + c)) : 1.0f;
+    float wr = 1.0f;
+    if constexpr (PRO) {
+      if (routed) wr = R->wts[R->sorted[seg + c]];
+    } else {
+      if (routed) wr = ld_f32<COH>(a.topk_w + ld_i32<COH>(a.sorted_ids + seg + c));
+    }
     float hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = silu_f(gs[i] * sg_rows[i]) * (us[i] * su_rows[i]) * wr;
@@ -486,6 +504,10 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
     if constexpr (F == DT_F32) {
       st_f32x4<COH>(reinterpret_cast<float*>(a.h) + off, f32x4_t{hv[0], hv[1], hv[2], hv[3]});
     } else if constexpr (F == DT_BF16) {
+      // lo = hv - hi exactly as written: a contraction with the product that formed hv would
+      // depend on how the item was inlined (a constant routing weight folds away), and the
+      // single- and multi-launch decodes must agree bit for bit
+#pragma clang fp contract(off)
       uint32_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]), h2 = f32_to_bf16(hv[2]), h3 = f32_to_bf16(hv[3]);
       float r0 = hv[0] - __uint_as_float(h0 << 16), r1 = hv[1] - __uint_as_float(h1 << 16);
       float r2 = hv[2] - __uint_as_float(h2 << 16), r3 = hv[3] - __uint_as_float(h3 << 16);

@@ -82,10 +82,15 @@ static void launch_logits(const RouterArgs& a, int grid, int NW, hipStream_t st)
 }
 
 template <int RT, int XT>
-static void launch_router_t(const RouterArgs& a, int NW, hipStream_t st) {
+static void launch_router_t(const RouterArgs& a, int NW, bool logits_only, hipStream_t st) {
   const int nblocks = a.n_row_tiles * a.n_col_tiles;
   const int mode = topk_mode(a.E, a.k);
-  if (nblocks == 1) {
+  if (logits_only) {
+    if (a.logit_parts == 4) launch_logits<RT, XT, 1>(a, 4 * nblocks, 4, st);
+    else if (NW == 16) launch_logits<RT, XT, 1>(a, nblocks, 16, st);
+    else if (NW == 8) launch_logits<RT, XT, 2>(a, nblocks, 8, st);
+    else launch_logits<RT, XT, 4>(a, nblocks, 4, st);
+  } else if (nblocks == 1) {
     // E <= 16: a thread per token, or a 16-lane row when k > 8
     const size_t lds = router_lds_bytes(16, a.E, a.T * a.k, false);
     if (mode == kTopkT8) hipLaunchKernelGGL((router_fused_kernel<RT, XT, kTopkT8>), dim3(1), dim3(1024), lds, st, a);
@@ -106,11 +111,11 @@ static void launch_router_t(const RouterArgs& a, int NW, hipStream_t st) {
   }
 }
 
-hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st) {
-  if (rdt == DT_F32 && xdt == DT_F32) launch_router_t<DT_F32, DT_F32>(a, NW, st);
-  else if (rdt == DT_F32) launch_router_t<DT_F32, DT_BF16>(a, NW, st);
-  else if (xdt == DT_F32) launch_router_t<DT_BF16, DT_F32>(a, NW, st);
-  else launch_router_t<DT_BF16, DT_BF16>(a, NW, st);
+hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st, bool logits_only) {
+  if (rdt == DT_F32 && xdt == DT_F32) launch_router_t<DT_F32, DT_F32>(a, NW, logits_only, st);
+  else if (rdt == DT_F32) launch_router_t<DT_F32, DT_BF16>(a, NW, logits_only, st);
+  else if (xdt == DT_F32) launch_router_t<DT_BF16, DT_F32>(a, NW, logits_only, st);
+  else launch_router_t<DT_BF16, DT_BF16>(a, NW, logits_only, st);
   return hipGetLastError();
 }
 

@@ -473,16 +473,6 @@ __device__ __forceinline__ void logits_tile(const RouterArgs a, int rtile, int c
   }
 }
 
-// Few assignments (decode): at most kSmallN of them (T * k), T * E <= 1024 and
-// T * E * E <= kRankWork take route_small below.
-constexpr int kSmallN = 64;
-constexpr int kRankWork = 65536;
-constexpr int kSmallDispInts = 3 * 64 + 2 * 65 + 1;    // slot tables of the one-wave dispatch
-
-__host__ __device__ inline bool small_route(int T, int E, int k) {
-  return T * k <= kSmallN && T * E <= 1024 && long(T) * E * E <= kRankWork;
-}
-
 // LDS of the selection and dispatch, in ints: dispatch scratch, then the flat
 // ids (when T*k fits), then the logits staging area (select kernel only).
 // A multiple of 4 ints, so that what follows stays 16-byte aligned.
@@ -596,22 +586,50 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 //     order, each padded to a multiple of tile_m;
 //  5. the work-group writes the per-expert tables, the padding and the tile
 //     table.  The results are those of dispatch_wg.
+// Phases 1-3 are small_select, 4 small_place and 5 small_tables, so that a
+// consumer can keep the routing in LDS (see the decode gate/up launch).
+// The phases share one LDS region (16-byte aligned), laid out here.
+struct SmallRoute {
+  int* s_e;                        // [64]: expert of active slot j (slots in expert order)
+  int* s_cnt;                      // [64]: its assignments
+  int* s_pad;                      // [64]: its padded length
+  int* s_off;                      // [65]: start of its segment; [A]: end of the last segment
+  int* s_cpre;                     // [65]: assignments with a smaller expert; [A]: n
+  int* s_na;                       // [1]: A, the number of active experts
+  int32_t* ids;                    // [n]: selected experts, flat order
+  float* wts;                      // [n]: their weights
+  int* sorted;                     // [n]: flat ids in expert-sorted order (tile_m 1)
+  float* selv;                     // [n]: selected logits, flat order
+  uint64_t* keys;                  // [T][E4]
+  int* part;                       // [Q][T][E4]: partial ranks
+  __device__ __forceinline__ SmallRoute(int* lds, int T, int E, int k) {
+    const int n = T * k, E4 = (E + 3) & ~3;
+    s_e = lds; s_cnt = s_e + 64; s_pad = s_cnt + 64; s_off = s_pad + 64; s_cpre = s_off + 65; s_na = s_cpre + 65;
+    ids = lds + ((kSmallDispInts + 3) & ~3);
+    wts = reinterpret_cast<float*>(ids + n);
+    sorted = reinterpret_cast<int*>(wts + n);
+    selv = reinterpret_cast<float*>(sorted + n);
+    keys = reinterpret_cast<uint64_t*>(ids + ((4 * n + 3) & ~3));
+    part = reinterpret_cast<int*>(keys + T * E4);
+  }
+};
+
+// Ints of the region for a work-group of NT threads (at most: the partial
+// ranks take Q * T * E4 <= 4 * NT).
+__host__ __device__ inline int small_route_ints(int NT, int T, int E, int k) {
+  return ((kSmallDispInts + 3) & ~3) + ((4 * T * k + 3) & ~3) + 2 * T * ((E + 3) & ~3) + 4 * NT;
+}
+
+// Phases 1-3: the selection into R.ids and R.selv (ends with a barrier).
 template <bool COH>
-__device__ __forceinline__ void route_small(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
-  const RouteBufs& rb = a.rb;
-  const int tid = threadIdx.x, NT = blockDim.x, lane = tid & 63, NW = NT >> 6;
-  const int T = a.T, E = a.E, k = a.k, n = T * k, M = a.tile_m;
+__device__ __forceinline__ void small_select(const RouterArgs a, const float* l, bool l_in_lds, const SmallRoute& R) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int T = a.T, E = a.E, k = a.k;
   const int E4 = (E + 3) & ~3, G = E4 >> 2;
-  int* s_e = lds;                  // [64]: expert of active slot j (slots in expert order)
-  int* s_cnt = s_e + 64;           // [64]: its assignments
-  int* s_pad = s_cnt + 64;         // [64]: its padded length
-  int* s_off = s_pad + 64;         // [65]: start of its segment; [A]: end of the last segment
-  int* s_cpre = s_off + 65;        // [65]: assignments with a smaller expert; [A]: n
-  int* s_na = s_cpre + 65;         // [1]: A, the number of active experts
-  int32_t* ids_lds = lds + router_disp_ints(NW, E);                       // [n]
-  float* selv = reinterpret_cast<float*>(ids_lds + n);                     // [n]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(ids_lds + ((2 * n + 3) & ~3));       // [T][E4], 16-byte aligned
-  int* part = reinterpret_cast<int*>(keys + T * E4);                        // [Q][T][E4]
+  int32_t* ids_lds = R.ids;
+  float* selv = R.selv;
+  uint64_t* keys = R.keys;
+  int* part = R.part;
 
   // 1. keys
   const size_t plane = size_t(T) * E;
@@ -684,9 +702,23 @@ __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, 
     }
   }
   __syncthreads();
+}
 
-  // 4. weights and the assignments' places (wave 0)
-  int rk = 0, slot = 0;
+// Phase 4 (wave 0): weights into R.wts (and the top-k outputs when `store`),
+// the slot tables, and for tile_m 1 the expert-sorted flat ids into
+// R.sorted; returns each assignment's rank in its group and its slot (lanes
+// of wave 0).  Ends with a barrier.
+template <bool COH>
+__device__ __forceinline__ void small_place(const RouterArgs a, const SmallRoute& R, bool store, int& rk, int& slot) {
+  const RouteBufs& rb = a.rb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int T = a.T, k = a.k, n = T * k, M = a.tile_m;
+  int* s_e = R.s_e; int* s_cnt = R.s_cnt; int* s_pad = R.s_pad; int* s_off = R.s_off; int* s_cpre = R.s_cpre;
+  int* s_na = R.s_na;
+  const int32_t* ids_lds = R.ids;
+  const float* selv = R.selv;
+  rk = 0;
+  slot = 0;
   if (tid < 64) {
     const bool valid = lane < n;
     const int f = valid ? lane : 0;
@@ -700,9 +732,13 @@ __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, 
       if (j == f - i * k) zf = z;
     }
     const int e = valid ? ids_lds[f] : 0;
+    const float wf = denom > 0.f ? zf * (1.0f / denom) : 1.0f / float(k);   // see topk_thread
     if (valid) {
-      st_i32<COH>(rb.topk_ids + f, e);
-      st_f32<COH>(rb.topk_w + f, denom > 0.f ? zf * (1.0f / denom) : 1.0f / float(k));   // see topk_thread
+      R.wts[f] = wf;
+      if (store) {
+        st_i32<COH>(rb.topk_ids + f, e);
+        st_f32<COH>(rb.topk_w + f, wf);
+      }
     }
     uint64_t same = __ballot(valid), lt = 0;     // same expert / smaller expert (valid lanes)
 #pragma unroll
@@ -718,6 +754,7 @@ __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, 
     const int A = __popcll(lead);
     rk = __popcll(same & below);
     slot = __popcll(lt & lead);
+    if (M == 1 && valid) R.sorted[__popcll(lt) + rk] = f;
     if (leader) {
       const int c = __popcll(same);
       s_e[slot] = e;
@@ -748,9 +785,16 @@ __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, 
     }
   }
   __syncthreads();
+}
 
-  // 5. tables
-  const int A = s_na[0];
+// Phase 5: the routing tables in memory.
+template <bool COH>
+__device__ __forceinline__ void small_tables(const RouterArgs a, const SmallRoute& R, int rk, int slot) {
+  const RouteBufs& rb = a.rb;
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int E = a.E, n = a.T * a.k, M = a.tile_m;
+  const int* s_e = R.s_e; const int* s_cnt = R.s_cnt; const int* s_off = R.s_off; const int* s_cpre = R.s_cpre;
+  const int A = R.s_na[0];
   const int total = s_off[A];
   if (tid < n) {
     const int pos = s_off[slot] + rk;
@@ -794,6 +838,15 @@ __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, 
     }
     st_i32<COH>(rb.tile_expert + i, e);
   }
+}
+
+template <bool COH>
+__device__ __forceinline__ void route_small(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
+  const SmallRoute R(lds, a.T, a.E, a.k);
+  int rk, slot;
+  small_select<COH>(a, l, l_in_lds, R);
+  small_place<COH>(a, R, true, rk, slot);
+  small_tables<COH>(a, R, rk, slot);
 }
 
 // Top-k of every token, then the dispatch; one work-group.  Few assignments
