@@ -23,6 +23,10 @@ def hipcc() -> str:
 
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+         # no implicit multiply-add contraction: whether a product and a sum fuse would otherwise
+         # depend on how a work item was inlined, and the single- and multi-launch decodes, which
+         # share the items, must produce the same bits (explicit fmaf calls are unaffected)
+         "-ffp-contract=off",
          # packed fp32 ops are kept out of the generated code on purpose
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

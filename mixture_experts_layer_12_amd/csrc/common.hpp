@@ -183,12 +183,14 @@ __host__ __device__ __forceinline__ size_t q4_scale_offset(long n_mat, long N, l
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-__device__ __forceinline__ u32x4_t ldg16(const void* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
-__device__ __forceinline__ u32x2_t ldg8(const void* p) {
-  return *reinterpret_cast<const u32x2_t*>(p);
-}
+// Loads from global memory, stated as such: the pointer may reach here
+// through a path the compiler cannot see into (a base picked among several
+// at run time can end up in a private lookup table), and a generic load
+// would also wait on LDS traffic.
+typedef const __attribute__((address_space(1))) u32x4_t g_u32x4_t;
+typedef const __attribute__((address_space(1))) u32x2_t g_u32x2_t;
+__device__ __forceinline__ u32x4_t ldg16(const void* p) { return *(g_u32x4_t*)(p); }
+__device__ __forceinline__ u32x2_t ldg8(const void* p) { return *(g_u32x2_t*)(p); }
 
 // Handoffs between work-groups of one launch (the single-launch decode).  The
 // L2 of each XCD is not coherent with the others, so data that another

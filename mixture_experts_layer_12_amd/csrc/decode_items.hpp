@@ -81,7 +81,8 @@ struct RowPtr {
 
 // fp8 row scales of output rows r0 .. r0+3 of matrix e (one 16-byte load).
 __device__ __forceinline__ f32x4_t fp8_row_scales(const uint8_t* base, long n_mat, long N, long K, long e, long r0) {
-  return *reinterpret_cast<const f32x4_t*>(base + byte_code_scale_offset(n_mat, N, K) + (size_t(e) * N + r0) * 4);
+  return *(const __attribute__((address_space(1))) f32x4_t*)(base + byte_code_scale_offset(n_mat, N, K) +
+                                                             (size_t(e) * N + r0) * 4);
 }
 
 // A operand fragments of one step, as loaded.
@@ -112,7 +113,7 @@ __device__ __forceinline__ AFrag<WT> load_a(const RowPtr<WT>& r, int s, int g, i
       f.raw0 = ldg16(r.p + size_t(blk) * 32);
       f.raw1 = ldg16(r.p + size_t(blk) * 32 + 16);
     }
-    f.d = ok ? r.sc[blk] : uint16_t(0);
+    f.d = ok ? *(const __attribute__((address_space(1))) uint16_t*)(r.sc + blk) : uint16_t(0);
   }
   return f;
 }
@@ -387,9 +388,13 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
                                             int c0 = 0, const SmallRoute* R = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
-  int e, n_e, hrow0, N, seg = 0;
-  long n_mat;
-  const uint8_t *bg, *bu;
+  // the matrices of the slot's family: selects on a uniform flag (a branch per field lets the
+  // compiler turn the pointers into a private lookup table)
+  const uint8_t* bg = routed ? a.wg : a.sg;
+  const uint8_t* bu = routed ? a.wu : a.su;
+  const int N = routed ? a.I : a.Is;
+  const long n_mat = routed ? a.E : a.S;
+  int e, n_e, hrow0, seg = 0;
   if (routed) {
     if constexpr (PRO) {
       if (slot >= R->s_na[0]) return false;
@@ -403,12 +408,10 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
       seg = ld_i32<COH>(a.offsets + e);
       hrow0 = ld_i32<COH>(a.cprefix + e);
     }
-    N = a.I; bg = a.wg; bu = a.wu; n_mat = a.E;
   } else {
     e = slot - a.n_routed_slots;
     n_e = a.T;
     hrow0 = a.T * a.k + e * a.T;
-    N = a.Is; bg = a.sg; bu = a.su; n_mat = a.S;
   }
   if (rt * 16 >= N) return false;
   constexpr int F = Fam<WT>::v;
@@ -504,10 +507,6 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
     if constexpr (F == DT_F32) {
       st_f32x4<COH>(reinterpret_cast<float*>(a.h) + off, f32x4_t{hv[0], hv[1], hv[2], hv[3]});
     } else if constexpr (F == DT_BF16) {
-      // lo = hv - hi exactly as written: a contraction with the product that formed hv would
-      // depend on how the item was inlined (a constant routing weight folds away), and the
-      // single- and multi-launch decodes must agree bit for bit
-#pragma clang fp contract(off)
       uint32_t h0 = f32_to_bf16(hv[0]), h1 = f32_to_bf16(hv[1]), h2 = f32_to_bf16(hv[2]), h3 = f32_to_bf16(hv[3]);
       float r0 = hv[0] - __uint_as_float(h0 << 16), r1 = hv[1] - __uint_as_float(h1 << 16);
       float r2 = hv[2] - __uint_as_float(h2 << 16), r3 = hv[3] - __uint_as_float(h3 << 16);
@@ -623,20 +622,19 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
                                           int c0 = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
-  int e, n_e, hrow0, K;
-  long n_mat;
-  const uint8_t* base;
+  const uint8_t* base = routed ? a.wd : a.sd;     // selects, as in gateup_item
+  const int K = routed ? a.I : a.Is;
+  const long n_mat = routed ? a.E : a.S;
+  int e, n_e, hrow0;
   if (routed) {
     if (slot >= ld_i32<COH>(a.active)) return false;
     e = ld_i32<COH>(a.active + 1 + slot);
     n_e = ld_i32<COH>(a.counts + e);
     hrow0 = ld_i32<COH>(a.cprefix + e);
-    K = a.I; base = a.wd; n_mat = a.E;
   } else {
     e = slot - a.n_routed_slots;
     n_e = a.T;
     hrow0 = a.T * a.k + e * a.T;
-    K = a.Is; base = a.sd; n_mat = a.S;
   }
   constexpr int F = Fam<WT>::v;
   const int H = a.H, g = lane >> 4;
