@@ -572,11 +572,12 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 // Selection and dispatch of few assignments (small_route), in five phases:
 //  1. the logits of every token become candidate keys in LDS (rows padded to
 //     E4 = E rounded up to 4 with key 0, which precedes nothing);
-//  2. the rank of each expert of each token, the number of keys above its
-//     own, is counted in parts: a work item takes 4 experts and one part of
-//     the row, loads each key pair once and compares it with all 4;
-//  3. the parts are summed; experts of rank < k are the selection, in rank
-//     order (the list the round-by-round selections produce);
+//  2. the rank of an expert is the number of keys above its own; experts of
+//     rank < k are the selection, in rank order (the list the round-by-round
+//     selections produce).  Ranks are counted inside groups of 64 experts
+//     (a wave per group, a lane per expert);
+//  3. with more than one group per token, the keys ranked below k in their
+//     group are ranked again among themselves;
 //  4. wave 0, lane f = flat id t * k + j: the weight of selection j (softmax
 //     over the selected logits, the denominator summed in selection order, as
 //     in the other strategies) and, with ballots over the 8 bits of the
@@ -601,7 +602,7 @@ struct SmallRoute {
   int* sorted;                     // [n]: flat ids in expert-sorted order (tile_m 1)
   float* selv;                     // [n]: selected logits, flat order
   uint64_t* keys;                  // [T][E4]
-  int* part;                       // [Q][T][E4]: partial ranks
+  int* part;                       // survivors of the group ranks: [T][ceil(E / 64) * k] 64-bit keys
   __device__ __forceinline__ SmallRoute(int* lds, int T, int E, int k) {
     const int n = T * k, E4 = (E + 3) & ~3;
     s_e = lds; s_cnt = s_e + 64; s_pad = s_cnt + 64; s_off = s_pad + 64; s_cpre = s_off + 65; s_na = s_cpre + 65;
@@ -614,8 +615,8 @@ struct SmallRoute {
   }
 };
 
-// Ints of the region for a work-group of NT threads (at most: the partial
-// ranks take Q * T * E4 <= 4 * NT).
+// Ints of the region for a work-group of NT threads (at most: the survivors
+// take 2 * T * ceil(E / 64) * k <= 512 <= 4 * NT ints).
 __host__ __device__ inline int small_route_ints(int NT, int T, int E, int k) {
   return ((kSmallDispInts + 3) & ~3) + ((4 * T * k + 3) & ~3) + 2 * T * ((E + 3) & ~3) + 4 * NT;
 }
@@ -625,13 +626,14 @@ template <bool COH>
 __device__ __forceinline__ void small_select(const RouterArgs a, const float* l, bool l_in_lds, const SmallRoute& R) {
   const int tid = threadIdx.x, NT = blockDim.x;
   const int T = a.T, E = a.E, k = a.k;
-  const int E4 = (E + 3) & ~3, G = E4 >> 2;
+  const int E4 = (E + 3) & ~3;
   int32_t* ids_lds = R.ids;
   float* selv = R.selv;
   uint64_t* keys = R.keys;
-  int* part = R.part;
 
-  // 1. keys
+  // 1. keys (and the survivor slots of step 2 cleared)
+  if (E > 64)
+    for (int p = tid; p < T * ((E + 63) >> 6) * k; p += NT) reinterpret_cast<uint64_t*>(R.part)[p] = 0ull;
   const size_t plane = size_t(T) * E;
   for (int b = 0; b < T * E4; b += 4 * NT) {
     float v[4];
@@ -663,45 +665,55 @@ __device__ __forceinline__ void small_select(const RouterArgs a, const float* l,
   }
   __syncthreads();
 
-  // 2. partial ranks: item (part q, token i, group g of 4 experts)
-  const int W = T * G;
-  int Q = 1;
-  while (2 * Q <= G && 2 * Q * W <= NT) Q *= 2;
-  const int span = ((E4 + Q - 1) / Q + 1) & ~1;
-  for (int w = tid; w < Q * W; w += NT) {
-    const int q = w / W, r = w - q * W, i = r / G, g = r - i * G;
-    const uint64_t* row = keys + i * E4;
-    const u32x4_t o01 = *reinterpret_cast<const u32x4_t*>(row + 4 * g);
-    const u32x4_t o23 = *reinterpret_cast<const u32x4_t*>(row + 4 * g + 2);
-    const uint64_t k0 = uint64_t(o01[0]) | (uint64_t(o01[1]) << 32), k1 = uint64_t(o01[2]) | (uint64_t(o01[3]) << 32);
-    const uint64_t k2 = uint64_t(o23[0]) | (uint64_t(o23[1]) << 32), k3 = uint64_t(o23[2]) | (uint64_t(o23[3]) << 32);
-    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-    const int j1 = min(E4, (q + 1) * span);
+  // 2. rank of each key inside its group of 64 experts (a wave per token and
+  //    group, a lane per expert, every lane reading the group's keys in the
+  //    same order).  A key with k or more larger keys in its own group is out;
+  //    the selection is among the rest: for one group the local rank is the
+  //    rank, else the survivors (at most k per group) go to `cand` and
+  //    3. each survivor's rank among the survivors of its token is its rank:
+  //    every key above a selected key is itself a survivor, and a survivor
+  //    outside the selection has the k selected keys above it.
+  const int lane = tid & 63, wave = tid >> 6, NW = NT >> 6;
+  const int GP = (E + 63) >> 6, C = GP * k;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(R.part);    // [T][GP * k] survivors (0: none)
+  for (int w = wave; w < T * GP; w += NW) {                // wave-uniform loop
+    const int i = w / GP, g = w - i * GP;
+    const uint64_t* row = keys + i * E4 + 64 * g;
+    const int len = min(64, E4 - 64 * g);                 // keys of the group, padding (key 0) included
+    const bool valid = 64 * g + lane < E;
+    const uint64_t mine = valid ? row[lane] : 0ull;
+    int c0 = 0, c1 = 0;
 #pragma unroll 8
-    for (int j = q * span; j < j1; j += 2) {
+    for (int j = 0; j < len; j += 2) {
       const u32x4_t t = *reinterpret_cast<const u32x4_t*>(row + j);
-      const uint64_t x0 = uint64_t(t[0]) | (uint64_t(t[1]) << 32), x1 = uint64_t(t[2]) | (uint64_t(t[3]) << 32);
-      c0 += (x0 > k0) + (x1 > k0);
-      c1 += (x0 > k1) + (x1 > k1);
-      c2 += (x0 > k2) + (x1 > k2);
-      c3 += (x0 > k3) + (x1 > k3);
+      c0 += (uint64_t(t[0]) | (uint64_t(t[1]) << 32)) > mine;
+      c1 += (uint64_t(t[2]) | (uint64_t(t[3]) << 32)) > mine;
     }
-    *reinterpret_cast<u32x4_t*>(part + (q * T + i) * E4 + 4 * g) =
-        u32x4_t{uint32_t(c0), uint32_t(c1), uint32_t(c2), uint32_t(c3)};
-  }
-  __syncthreads();
-
-  // 3. ranks -> selection
-  for (int p = tid; p < T * E; p += NT) {
-    const int i = p / E, e = p - i * E;
-    int rnk = 0;
-    for (int q = 0; q < Q; ++q) rnk += part[(q * T + i) * E4 + e];
-    if (rnk < k) {
-      ids_lds[i * k + rnk] = e;
-      selv[i * k + rnk] = key_value(keys[i * E4 + e]);
+    const int r = c0 + c1;
+    if (valid && r < k) {
+      if (GP == 1) {
+        ids_lds[i * k + r] = 64 * g + lane;
+        selv[i * k + r] = key_value(mine);
+      } else {
+        cand[i * C + g * k + r] = mine;
+      }
     }
   }
   __syncthreads();
+  if (GP > 1) {
+    for (int p = tid; p < T * C; p += NT) {
+      const int i = p / C;
+      const uint64_t* ci = cand + i * C;
+      const uint64_t mine = ci[p - i * C];
+      int r = 0;
+      for (int j = 0; j < C; ++j) r += ci[j] > mine;
+      if (mine != 0ull && r < k) {
+        ids_lds[i * k + r] = int(~uint32_t(mine));
+        selv[i * k + r] = key_value(mine);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Phase 4 (wave 0): weights into R.wts (and the top-k outputs when `store`),
