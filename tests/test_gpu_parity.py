@@ -48,6 +48,8 @@ SMALL = {
     # exactly 64 assignments over 32 experts
     "e256_t1_k8": W("e256_t1_k8", T=1, H=64, E=256, k=8, I=32),
     "n64_e32": W("n64_e32", T=8, H=64, E=32, k=8, I=32, S=1, Is=32),
+    # two groups of experts per token, the second holding 8 (survivor slots left empty)
+    "e72_t3_k6": W("e72_t3_k6", T=3, H=96, E=72, k=6, I=32, S=1, Is=32),
     # more than 16 tokens with few per expert: one-column-tile kernels with extra passes (the shared
     # slot takes three)
     "e32_t40_passes": W("e32_t40_passes", T=40, H=160, E=32, k=2, I=96, S=1, Is=64),
@@ -171,7 +173,7 @@ def test_empty_batch_is_noop(m):
 @pytest.mark.parametrize("name", ["mixtral_small_bf16", "qwen_small_q4_t5", "deepseek_small_t40",
                                   "prefill_small_zipf", "k_equals_E", "tiny_f32", "e20_k12", "e256_k70",
                                   "n10k_prefill", "e40_k10", "e256_t1_k8", "n64_e32", "qwen_small_q4_t1",
-                                  "t1_k1"])
+                                  "t1_k1", "e72_t3_k6"])
 def test_route_bit_exact(m, name):
     wl = SMALL[name]
     inp = _inputs(wl, 4)
@@ -189,7 +191,7 @@ def test_route_bit_exact(m, name):
     assert act[0] == len(d["active"]) and np.array_equal(act[1:1 + act[0]], d["active"])
 
 
-@pytest.mark.parametrize("T, E, k", [(1, 256, 8), (3, 64, 8), (4, 8, 2), (40, 16, 6), (5, 256, 70)])
+@pytest.mark.parametrize("T, E, k", [(1, 256, 8), (3, 64, 8), (4, 8, 2), (40, 16, 6), (5, 256, 70), (2, 100, 12)])
 def test_equal_logits_pick_lowest_indices(m, T, E, k):
     """All logits equal (zero router weights, no bias): every token takes experts
     0..k-1 in index order with weight 1/k, on each selection strategy."""
