@@ -61,7 +61,7 @@ enum {
                            (roundup(T*top_k + E*255, 256) + n_shared*roundup(T, 256)) *
                            max(I, I_shared) all below 2^31; its expert segments are padded
                            to multiples of 256 rows */
-  MOE_PATH_DECODE_FUSED = 3  /* the decode kernels as one cooperative launch per pass of
+  MOE_PATH_DECODE_FUSED = 3  /* the decode kernels as one launch (a resident grid) per pass of
                            at most 64 tokens; needs router_dtype == x_dtype and
                            top_k <= 16.  While `stream` is being captured into a
                            graph the call runs path 1 instead (a captured launch

@@ -722,7 +722,14 @@ __device__ __forceinline__ void combine_item(const DecodeArgs a, long i4) {
   const int t = int(i4 / H4), h4 = int(i4 % H4);
   const f32x4_t* p = reinterpret_cast<const f32x4_t*>(a.partials);
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) v += p[size_t(ld_i32<COH>(a.inv + t * a.k + j)) * H4 + h4];
+  for (int j0 = 0; j0 < a.k; j0 += 8) {     // the rows of 8 assignments located first, then added in order
+    int row[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) row[u] = j0 + u < a.k ? ld_i32<COH>(a.inv + t * a.k + j0 + u) : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < a.k) v += p[size_t(row[u]) * H4 + h4];
+  }
   for (int s = 0; s < a.S; ++s) v += p[size_t(a.T * a.k + s * a.T + t) * H4 + h4];
   if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
   else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};

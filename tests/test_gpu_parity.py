@@ -135,7 +135,7 @@ def test_forward_multi_launch_decode(m, name):
 
 @pytest.mark.parametrize("name", sorted(n for n in SMALL if _fused_ok(SMALL[n])))
 def test_single_launch_decode_equals_multi_launch(m, name):
-    """The single-launch decode runs the same work items in one cooperative
+    """The single-launch decode runs the same work items in one resident-grid
     launch, with handoffs through device-scope stores and flags: its output
     must be bit-identical to the multi-launch decode, and within the oracle's
     tolerance."""
