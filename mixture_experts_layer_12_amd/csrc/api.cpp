@@ -105,7 +105,9 @@ moe::FusedArgs fused_plan(const moe_shape_t* s, int Tc) {
   f.gu_rt_shared = Is / 16;
   f.n_logit = 4 * ((s->E + 15) / 16) * ((Tc + 15) / 16);   // 4 partial planes per tile
   f.end_shared_gu = f.n_logit + S * f.gu_rt_shared;
-  f.end_select = f.end_shared_gu + 1;
+  // routing in the routed gate/up items: few assignments and few such items (each repeats it)
+  f.route_in_gu = moe::small_route(Tc, s->E, s->top_k) && long(n_slots) * f.gu_rt_routed <= 512 ? 1 : 0;
+  f.end_select = f.end_shared_gu + (f.route_in_gu ? 0 : 1);
   f.end_gu = f.end_select + n_slots * f.gu_rt_routed;
   f.end_down = f.end_gu + (n_slots + S) * (s->H / (Tc <= 16 ? moe::kFusedDownRows<1> : moe::kFusedDownRows<4>));
   f.n_items = f.end_down + int((long(Tc) * s->H / 4 + 255) / 256);

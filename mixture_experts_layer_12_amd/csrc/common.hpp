@@ -329,7 +329,8 @@ struct FusedArgs {
   DecodeArgs d;
   int n_logit;          // [0, n_logit): router logit tiles
   int end_shared_gu;    // [n_logit, end_shared_gu): shared-expert gate/up row tiles
-  int end_select;       // end_shared_gu: top-k and dispatch (one item)
+  int end_select;       // end_shared_gu: top-k and dispatch (one item; none with route_in_gu)
+  int route_in_gu;      // 1: every routed gate/up item selects and dispatches from the logits itself
   int end_gu;           // [end_select, end_gu): routed gate/up row tiles, slot-major
   int end_down;         // [end_gu, end_down): down row groups (kFusedDownRows), slot-major, routed then shared
   int n_items;          // [end_down, n_items): combine blocks of 1024 outputs

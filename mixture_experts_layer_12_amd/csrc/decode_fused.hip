@@ -20,6 +20,11 @@
 //   [n_logit, end_shared_gu)     shared-expert gate/up row tiles
 //   end_shared_gu                top-k, renormalisation, dispatch (one item)
 //   [end_select, end_gu)         routed gate/up row tiles, slot-major
+// With few assignments (route_in_gu) there is no selection item: each routed
+// gate/up item waits for the logits and runs the few-assignment route itself
+// (the first one also writes the routing tables, on which the routed down
+// items then wait), so the routing latency is paid in parallel, not in
+// series with one item's handoff.
 //   [end_gu, end_down)           down row groups of kFusedDownRows outputs, slot-major (routed, then shared)
 //   [end_down, n_items)          combine, 1024 outputs per item
 // An item waits only on items of lower index, and every work-group takes its
@@ -75,6 +80,11 @@ __device__ __forceinline__ void signal_item(const FusedArgs& f, int i) {
   if (threadIdx.x == 0) __hip_atomic_store(f.flags + i, f.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Ints of the gate/up cross-wave sums (the few-assignment route of a routed
+// gate/up item lives past them).
+template <int NCT>
+constexpr int kFusedGuInts = (kFusedThreads / 64) * 2 * NCT * 64 * 4;
+
 template <int WT, int XT, int NCT>
 __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f) {
   extern __shared__ __attribute__((aligned(16))) int smem[];
@@ -102,13 +112,26 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
       }
     } else if (i < f.end_gu) {
       const int j = i - f.end_select;
-      wait_items(f, f.end_shared_gu, f.end_select);
-      gateup_item<WT, XT, NCT, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu);
+      if (f.route_in_gu) {
+        // the item selects and dispatches from the logits into LDS past the cross-wave sums; the
+        // first one (slot 0, row tile 0) also publishes the routing tables for the down items
+        wait_items(f, 0, f.n_logit);
+        const SmallRoute R(smem + kFusedGuInts<NCT>, a.T, a.E, a.k);
+        int rk, fs;
+        small_select<false>(f.r, f.r.rb.logits, false, R);
+        small_place<true>(f.r, R, j == 0, rk, fs);
+        if (j == 0) small_tables<true>(f.r, R, rk, fs);
+        gateup_item<WT, XT, NCT, true, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu, 0, &R);
+      } else {
+        wait_items(f, f.end_shared_gu, f.end_select);
+        gateup_item<WT, XT, NCT, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu);
+      }
     } else if (i < f.end_down) {
       const int j = i - f.end_gu;
       const int slot = j / nrt_down, rt = j % nrt_down;
       if (slot < a.n_routed_slots) {
         const int b = f.end_select + slot * f.gu_rt_routed;
+        if (f.route_in_gu) wait_items(f, f.end_select, f.end_select + 1);   // the routing tables
         wait_items(f, b, b + f.gu_rt_routed);
       } else {
         const int b = f.n_logit + (slot - a.n_routed_slots) * f.gu_rt_shared;
@@ -142,7 +165,8 @@ size_t fused_lds_bytes(int E, int T, int k, int nct) {
   const size_t select = (size_t(router_disp_ints(NW, E)) + (n <= kRouterIdsLds ? n : 0) + size_t(std::min(T, ch)) * E) *
                         sizeof(int);
   const size_t gu = size_t(NW) * 2 * nct * 64 * sizeof(f32x4_t);
-  return std::max(std::max(logits, select), gu);
+  const size_t route = gu + size_t(small_route_max_ints(kFusedThreads)) * sizeof(int);   // route_in_gu items
+  return std::max(std::max(logits, select), route);
 }
 
 template <int WT, int XT, int NCT>

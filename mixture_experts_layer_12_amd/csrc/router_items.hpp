@@ -621,6 +621,11 @@ __host__ __device__ inline int small_route_ints(int NT, int T, int E, int k) {
   return ((kSmallDispInts + 3) & ~3) + ((4 * T * k + 3) & ~3) + 2 * T * ((E + 3) & ~3) + 4 * NT;
 }
 
+// Upper bound of small_route_ints over every shape small_route admits.
+__host__ __device__ constexpr int small_route_max_ints(int NT) {
+  return ((kSmallDispInts + 3) & ~3) + 4 * kSmallN + 2 * (1024 + 3 * kSmallN) + 4 * NT;
+}
+
 // Phases 1-3: the selection into R.ids and R.selv (ends with a barrier).
 template <bool COH>
 __device__ __forceinline__ void small_select(const RouterArgs a, const float* l, bool l_in_lds, const SmallRoute& R) {
