@@ -67,6 +67,11 @@ constexpr int MM_NP = MM_KS - 1;              // k-steps that carry a refill par
 constexpr int MM_PQ = (MM_DMA + MM_NP - 1) / MM_NP;   // loads per part
 static_assert(MM_PQ <= 8, "one load per MFMA pair");
 constexpr size_t MM_LDS = size_t(MM_S) * MM_STAGE * sizeof(uint16_t);   // 128 KiB
+// The deep ring: three slots for the A operand (the one that streams from
+// HBM) and two for B, 5 x 32 KiB, the whole LDS of a CU.
+constexpr int MM_HALF = MM_TM * MM_BK;        // bf16 elements of one operand's slot
+constexpr int MM_DMA_A = MM_TN / MM_RPI / MM_WAVES;   // A load instructions per wave per stage (q < 8)
+constexpr size_t MM_LDS_DEEP = size_t(5) * MM_HALF * sizeof(uint16_t);   // 160 KiB
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (expcnt and lgkmcnt left unconstrained).
@@ -93,28 +98,55 @@ __device__ __forceinline__ void ring_barrier() {
 // index within any block that starts at a multiple of 16 rows.
 __device__ __forceinline__ int mm_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Tile order.  Each XCD (hardware places work-group b on XCD b % 8) owns a
-// contiguous range of row tiles, so its resident work-groups mostly serve
-// one expert and share that expert's weight tiles in its L2.  All XCDs walk
-// the output columns in the same order, in groups of MM_CG column tiles
-// (outer) over their row tiles (inner), so the XCDs that serve one expert
-// read the same weight columns at about the same time.  Returns false for
-// the padding work-groups of a grid of 8 * ceil(n_rt / 8) * n_ct.
+// Tile order.  The work is the list of (k range, column group, row tile,
+// column) items over the row tiles in use only: the routed tiles up to the
+// dispatch's padded total (the capacity's worst case leaves several unused)
+// and the shared experts' tiles.  Column groups are MM_CG column tiles; in
+// a group the row tiles go in order and the columns inner, so consecutive
+// items share a weight tile (same columns, same expert) or a token tile.
+// Each XCD (hardware places work-group b on XCD b % 8) takes one contiguous
+// eighth of the list, in order: the XCDs get equal work whatever the number
+// of row tiles, the work-groups resident on one XCD at a time cover a block
+// of about 32 / MM_CG row tiles by MM_CG columns and share its operands in
+// that XCD's L2, and each weight column is read by one or two XCDs only.
 #ifndef MOE_PF_CG
 #define MOE_PF_CG 4
 #endif
 constexpr int MM_CG = MOE_PF_CG;
-__device__ __forceinline__ bool tile_colgroups(int bid, int n_rt, int n_ct, int& rt, int& ct) {
-  const int x = bid & 7, local = bid >> 3;
-  const int r8 = (n_rt + 7) >> 3;
-  const int g = local / (r8 * MM_CG);
-  const int in = local - g * r8 * MM_CG;
-  const int ncg = min(MM_CG, n_ct - g * MM_CG);
-  ct = g * MM_CG + in % ncg;
-  rt = x * r8 + in / ncg;
-  return rt < n_rt && ct < n_ct;
+struct TileList {
+  int n_real;      // routed row tiles in use
+  int n_routed;    // routed row tiles of the capacity
+  int n_rows;      // row tiles in the list: n_real + the shared experts' tiles
+  int n_ct;        // column tiles
+  long n_items;    // k ranges x n_rows x n_ct
+};
+__device__ __forceinline__ TileList tile_list(const PrefillArgs& a, int n_ct, int k_ranges) {
+  TileList L;
+  L.n_routed = a.capacity / MM_TM;
+  L.n_real = min(max(a.offsets[a.E], 0) / MM_TM, L.n_routed);
+  L.n_rows = L.n_real + (a.n_row_tiles - L.n_routed);
+  L.n_ct = n_ct;
+  L.n_items = long(k_ranges) * L.n_rows * n_ct;
+  return L;
 }
-__host__ __device__ inline int tile_grid(int n_rt, int n_ct) { return 8 * ((n_rt + 7) / 8) * n_ct; }
+// Item of work-group `bid`: false past the end of its XCD's share.
+__device__ __forceinline__ bool tile_item(int bid, const TileList& L, int& kr, int& rt, int& ct) {
+  const int x = bid & 7;
+  const long item = x * L.n_items / 8 + (bid >> 3);
+  if (item >= (x + 1) * L.n_items / 8) return false;
+  const long per_k = long(L.n_rows) * L.n_ct;
+  kr = int(item / per_k);
+  const int in_k = int(item - kr * per_k);
+  const int g = in_k / (L.n_rows * MM_CG);
+  const int in_g = in_k - g * L.n_rows * MM_CG;
+  const int ncg = min(MM_CG, L.n_ct - g * MM_CG);
+  const int j = in_g / ncg;
+  ct = g * MM_CG + in_g % ncg;
+  rt = j < L.n_real ? j : L.n_routed + (j - L.n_real);
+  return true;
+}
+// Work-groups for up to n_items items: every XCD's share fits.
+__host__ __device__ inline int tile_grid(long n_items) { return int(8 * ((n_items + 7) / 8)); }
 
 // What one wave stages per k stage: load instruction q (8 rows x 128 bytes)
 // reads matrix base[q] (wave-uniform) at this lane's element offset off[q]
@@ -147,22 +179,43 @@ struct MMFrags { u32x4_t a[2][4], b[2][4]; };   // [k-step parity][32-row block]
 // blocks (32 rows each) start at a0 + (i & 1) * 32 + (i >> 1) * a_step, its B
 // blocks at 256 + b0 + 32 j; acc[i][j] accumulates A block i x B block j:
 // register q of lane l holds row 8 (q / 4) + 4 (l / 32) + q % 4 of A block i
-// and row l % 32 of B block j.  The LDS ring is `smem` (MM_LDS bytes).
+// and row l % 32 of B block j.
+//
+// DEEP = 0: a ring of two stages (`smem`, MM_LDS bytes); the refill of a
+// freed slot is spread over the next three k-steps and must land within
+// about one stage.  DEEP = 1 (A) or 2 (B): that operand, the one that
+// streams from HBM, has three slots and the other two (`smem`, MM_LDS_DEEP
+// bytes); its rows are load instructions q < 8 of `ld`, the other
+// operand's q >= 8.  After the barrier of stage kt the fast operand of
+// stage kt + 2 is issued first (k-steps 3 and 0) and then the slow operand
+// of stage kt + 3 (k-steps 1 and 2 of the next stage), so the barrier of
+// stage kt + 1 waits for everything but those last loads (loads complete in
+// issue order): slow loads get about two stages to arrive, fast loads one.
+template <int DEEP>
 __device__ __forceinline__ void mm_tile(uint16_t* smem, const TileLoads& ld, int K, int a0, int a_step, int b0,
                                         f32x16_t (&acc)[4][4]) {
   const int lane = threadIdx.x & 63;
   const int nk = (K + MM_BK - 1) / MM_BK;     // stages; K % 64 == 32 leaves a half-full last one
   const int nk_full = K / MM_BK;
+  // Element offsets of stage kt's A and B slots; a staged row r is at
+  // offset + r * MM_BK (B rows are r = 256 .. 511).
+  auto slow = [](int kt) { return (kt % 3) * MM_HALF; };        // slots 0 .. 2
+  auto fast = [](int kt) { return (3 + kt % 2) * MM_HALF; };    // slots 3, 4
+  auto a_slot = [&](int kt) { return DEEP == 1 ? slow(kt) : DEEP == 2 ? fast(kt) : (kt % MM_S) * MM_STAGE; };
+  auto b_slot = [&](int kt) {
+    return DEEP == 1 ? fast(kt) - MM_HALF : DEEP == 2 ? slow(kt) - MM_HALF : (kt % MM_S) * MM_STAGE;
+  };
   // In a half-full last stage, lanes whose chunk lies past K load the chunk
   // 32 values lower instead (in bounds), and the k-steps past K multiply a
   // zero B operand.
   auto issue = [&](int kt, auto q0, auto q1) {   // load instructions q0 .. q1 - 1 of stage kt
-    uint16_t* d = smem + (kt % MM_S) * MM_STAGE;
     const int k0 = kt * MM_BK;
     const bool part = k0 + MM_BK > K;
+    const int oa = a_slot(kt), ob = b_slot(kt);
     static_for<decltype(q0)::value, decltype(q1)::value>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       const int back = (part && ((ld.upper >> q) & 1)) ? 32 : 0;
+      uint16_t* d = smem + ((q < MM_DMA_A) == (DEEP != 2) ? oa : ob);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(ld.base[q] + (ld.off[q] + uint32_t(k0 - back))),
                                        (lds_void_t*)(d + ld.row[q] * MM_BK), 16, 0, 0);
     });
@@ -175,12 +228,14 @@ __device__ __forceinline__ void mm_tile(uint16_t* smem, const TileLoads& ld, int
   const int l32 = lane & 31, hi = lane >> 5;
   auto read_step = [&](int kt, int ks, MMFrags& f, auto steady) {   // the operands of one MFMA k-step
     const int h = ks & 1;
-    const uint16_t* sh = smem + (kt % MM_S) * MM_STAGE + l32 * MM_BK + (((2 * ks + hi) ^ mm_swz(l32)) << 3);
+    const uint16_t* sh = smem + l32 * MM_BK + (((2 * ks + hi) ^ mm_swz(l32)) << 3);
+    const uint16_t* sa = sh + a_slot(kt);
+    const uint16_t* sb = sh + b_slot(kt);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      f.a[h][i] = *reinterpret_cast<const u32x4_t*>(sh + (a0 + (i & 1) * 32 + (i >> 1) * a_step) * MM_BK);
+      f.a[h][i] = *reinterpret_cast<const u32x4_t*>(sa + (a0 + (i & 1) * 32 + (i >> 1) * a_step) * MM_BK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[h][j] = *reinterpret_cast<const u32x4_t*>(sh + (MM_TM + b0 + j * 32) * MM_BK);
+    for (int j = 0; j < 4; ++j) f.b[h][j] = *reinterpret_cast<const u32x4_t*>(sb + (MM_TM + b0 + j * 32) * MM_BK);
     if (!steady && kt * MM_BK + ks * 16 >= K) {     // past K in a half-full last stage
 #pragma unroll
       for (int j = 0; j < 4; ++j) f.b[h][j] = u32x4_t{0, 0, 0, 0};
@@ -267,6 +322,80 @@ __device__ __forceinline__ void mm_tile(uint16_t* smem, const TileLoads& ld, int
     }
   };
 
+  if constexpr (DEEP != 0) {
+    using QA = std::integral_constant<int, MM_DMA_A>;
+    using QA2 = std::integral_constant<int, MM_DMA_A / 2>;
+    using QB2 = std::integral_constant<int, MM_DMA_A + (MM_DMA - MM_DMA_A) / 2>;
+    using half_loads = std::integral_constant<int, MM_DMA_A / 2>;
+    static_assert(MM_DMA - MM_DMA_A == MM_DMA_A, "A and B take the same number of loads");
+    // Stage kt with every stage it issues (up to kt + 2) full: straight-line
+    // code.  With S the slow operand and F the fast one: k-step 0 issues the
+    // second half of F(kt + 1), k-steps 1 and 2 S(kt + 2); the barrier leaves
+    // S(kt + 2) in flight; k-step 3 issues the first half of F(kt + 2).
+    MMFrags f;
+    auto step_steady = [&](int kt) {
+      multiply(f, 0);
+      read_step(kt, 1, f, std::true_type{});
+      issue(kt + 1, QB2{}, QALL{});
+      interleave(half_loads{});
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(f, 1);
+      read_step(kt, 2, f, std::true_type{});
+      issue(kt + 2, Q0{}, QA2{});
+      interleave(half_loads{});
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(f, 0);
+      read_step(kt, 3, f, std::true_type{});
+      issue(kt + 2, QA2{}, QA{});
+      interleave(half_loads{});
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<MM_DMA_A>();     // all but A(kt + 2): stage kt + 1 landed (this wave's part)
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(f, 1);
+      read_step(kt + 1, 0, f, std::true_type{});
+      issue(kt + 2, QA{}, QB2{});
+      interleave(half_loads{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The same issue pattern with guards (last stages, short k loops).
+    auto step_tail = [&](int kt) {
+      multiply(f, 0);
+      read_step(kt, 1, f, std::false_type{});
+      if (kt + 1 < nk) issue(kt + 1, QB2{}, QALL{});
+      multiply(f, 1);
+      read_step(kt, 2, f, std::false_type{});
+      if (kt + 2 < nk) issue(kt + 2, Q0{}, QA{});
+      multiply(f, 0);
+      read_step(kt, 3, f, std::false_type{});
+      const bool more = kt + 1 < nk;
+      if (more) {
+        if (kt + 2 < nk) wait_vmcnt<MM_DMA_A>();
+        else wait_vmcnt<0>();
+        ring_barrier();
+      }
+      multiply(f, 1);
+      if (more) {
+        read_step(kt + 1, 0, f, std::false_type{});
+        if (kt + 2 < nk) issue(kt + 2, QA{}, QB2{});
+      }
+    };
+    // Prologue: stage 0, S(1), the first half of F(1); wait for stage 0.
+    issue(0, Q0{}, QALL{});
+    if (1 < nk) {
+      issue(1, Q0{}, QB2{});
+      wait_vmcnt<QB2::value>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    ring_barrier();
+    read_step(0, 0, f, std::false_type{});
+    int kt = 0;
+    for (; kt + 2 < nk_full; ++kt) step_steady(kt);
+    for (; kt < nk; ++kt) step_tail(kt);
+    return;
+  }
+
   // Prologue: stage 0 whole, stage 1 whole or (when a steady step follows)
   // its part 0; wait for stage 0.
   const bool piped = 2 < nk_full;
@@ -312,15 +441,26 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 // a quarter of the gate rows, the same up rows and a quarter of the tokens.
 
 constexpr int GU_BN = MM_TN / 2;              // intermediate columns per tile
+#ifndef MOE_PF_DEEP
+#define MOE_PF_DEEP 1
+#endif
+constexpr int MM_GU_DEEP = MOE_PF_DEEP != 0 ? 1 : 0;   // weight rows (A) get the three-slot ring
+constexpr size_t GU_LDS = MM_GU_DEEP ? MM_LDS_DEEP : MM_LDS;
+#ifndef MOE_PF_DN_DEEP
+#define MOE_PF_DN_DEEP 1
+#endif
+constexpr int MM_DN_DEEP = MOE_PF_DN_DEEP != 0 ? 2 : 0;   // weight rows (B) get the three-slot ring
+constexpr size_t DN_LDS = MM_DN_DEEP ? MM_LDS_DEEP : MM_LDS;
 
 __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  int rt, ct;
-  if (!tile_colgroups(blockIdx.x, a.n_row_tiles, a.n_col_tiles, rt, ct)) return;
+  const TileList L = tile_list(a, a.n_col_tiles, 1);
+  int kr, rt, ct;
+  if (!tile_item(blockIdx.x, L, kr, rt, ct)) return;
 
-  const int n_routed_tiles = a.capacity / MM_TM;
+  const int n_routed_tiles = L.n_routed;
   const int H = a.H;
   int N, local = 0;
   const uint16_t *Wg, *Wu;
@@ -372,7 +512,7 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillAr
   const int wm = wv >> 1, wn = wv & 1;
   f32x16_t acc[4][4];
   zero_acc(acc);
-  mm_tile(smem, ld, H, wn * 64, GU_BN, wm * 128, acc);
+  mm_tile<MM_GU_DEEP>(smem, ld, H, wn * 64, GU_BN, wm * 128, acc);
 
   // epilogue: h[row][n] = bf16(silu(g) * u); A blocks 0-1 are gate, 2-3 up
   const int l32 = lane & 31, hi = lane >> 5;
@@ -405,16 +545,13 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillAr
 
 __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  __shared__ int tok_s[MM_TM];
-  __shared__ float w_s[MM_TM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(int(tid >> 6));
-  // work-group = (k range, tile); each k range's work-groups form one tile grid
-  const int grid = tile_grid(a.n_row_tiles, a.n_col_tiles);
-  const int kr = blockIdx.x / grid;
-  int rt, ct;
-  if (!tile_colgroups(blockIdx.x - kr * grid, a.n_row_tiles, a.n_col_tiles, rt, ct)) return;
-  const int n_routed_tiles = a.capacity / MM_TM;
+  // work-group = (k range, tile)
+  const TileList L = tile_list(a, a.n_col_tiles, a.k_split);
+  int kr, rt, ct;
+  if (!tile_item(blockIdx.x, L, kr, rt, ct)) return;
+  const int n_routed_tiles = L.n_routed;
   const int H = a.H;
   int K;
   const uint16_t* Wd;
@@ -423,19 +560,11 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs
     if (e < 0) return;
     K = a.I;
     Wd = a.wd + size_t(e) * H * a.I;
-    const int fl = a.sorted_ids[rt * MM_TM + tid];
-    const bool ok = fl < a.T * a.k;
-    tok_s[tid] = ok ? fl / a.k : -1;
-    w_s[tid] = ok ? a.topk_w[fl] : 0.f;
   } else {
     const int tiles_per_shared = a.t_pad / MM_TM;
     const int s = (rt - n_routed_tiles) / tiles_per_shared;
-    const int local = (rt - n_routed_tiles) % tiles_per_shared;
     K = a.Is;
     Wd = a.sd + size_t(s) * H * a.Is;
-    const int t = local * MM_TM + tid;
-    tok_s[tid] = t < a.T ? t : -1;
-    w_s[tid] = 1.0f;
   }
   const int n0 = ct * MM_TN;
   const int hrow0 = rt * MM_TM;
@@ -448,22 +577,41 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs
   TileLoads ld;
   ld.upper = 0;
   const int lrow = lane >> 3;
+  // The weight rows (B, from HBM) are the slow operand: load instructions
+  // 0..7, the activation rows 8..15.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {                 // instructions 0..7: activation rows
-    const int r = wv * 64 + j * 8;
-    set_load(ld, j, a.h + k_begin, r, hrow0 + r + lrow, a.h_stride, lane);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {                 // instructions 8..15: down-projection rows
+  for (int j = 0; j < 8; ++j) {                 // down-projection rows
     const int r = wv * 64 + j * 8;
     const int n = n0 + r + lrow;
-    set_load(ld, 8 + j, Wd + k_begin, MM_TM + r, n < H ? n : n0, K, lane);   // columns past H are never stored
+    set_load(ld, j, Wd + k_begin, MM_TM + r, n < H ? n : n0, K, lane);   // columns past H are never stored
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {                 // activation rows
+    const int r = wv * 64 + j * 8;
+    set_load(ld, 8 + j, a.h + k_begin, r, hrow0 + r + lrow, a.h_stride, lane);
   }
 
   const int wm = wv >> 1, wn = wv & 1;
   f32x16_t acc[4][4];
   zero_acc(acc);
-  mm_tile(smem, ld, k_len, wm * 128, 64, wn * 128, acc);   // its first barrier also publishes tok_s / w_s
+  mm_tile<MM_DN_DEEP>(smem, ld, k_len, wm * 128, 64, wn * 128, acc);
+
+  // the ring is free once every wave is done with it: the tile's token ids
+  // (-1: padding) and routing weights go there
+  __syncthreads();
+  int* tok_s = reinterpret_cast<int*>(smem);
+  float* w_s = reinterpret_cast<float*>(smem) + MM_TM;
+  if (rt < n_routed_tiles) {
+    const int fl = a.sorted_ids[rt * MM_TM + tid];
+    const bool ok = fl < a.T * a.k;
+    tok_s[tid] = ok ? fl / a.k : -1;
+    w_s[tid] = ok ? a.topk_w[fl] : 0.f;
+  } else {
+    const int t = (rt - n_routed_tiles) % (a.t_pad / MM_TM) * MM_TM + tid;
+    tok_s[tid] = t < a.T ? t : -1;
+    w_s[tid] = 1.0f;
+  }
+  __syncthreads();
 
   // epilogue: acc[t][n] += w * y
   const int l32 = lane & 31, hi = lane >> 5;
@@ -511,9 +659,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   // dynamic LDS above 64 KiB must be allowed per kernel (thread-safe one-time set-up)
   static const hipError_t attr_rc = [] {
     hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_gateup_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(MM_LDS));
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(GU_LDS));
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_down_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(MM_LDS));
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(DN_LDS));
     return e1 != hipSuccess ? e1 : e2;
   }();
   if (attr_rc != hipSuccess) return attr_rc;
@@ -523,7 +671,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   const int nmax = a.I > a.Is ? a.I : a.Is;
   g.n_row_tiles = n_rt;
   g.n_col_tiles = (nmax + GU_BN - 1) / GU_BN;
-  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(tile_grid(n_rt, g.n_col_tiles)), dim3(64 * MM_WAVES), MM_LDS, st, g);
+  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(tile_grid(long(n_rt) * g.n_col_tiles)), dim3(64 * MM_WAVES), GU_LDS, st,
+                     g);
   if (mark) mark->mark(st);
   PrefillArgs d = a;
   d.n_row_tiles = n_rt;
@@ -531,8 +680,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   // A few hundred output tiles leave the last round of work-groups mostly
   // idle (one work-group per CU): split k so there are at least ~4 rounds.
   d.k_split = down_k_split(n_rt * d.n_col_tiles, nmax);
-  hipLaunchKernelGGL(prefill_down_kernel, dim3(tile_grid(n_rt, d.n_col_tiles) * d.k_split), dim3(64 * MM_WAVES),
-                     MM_LDS, st, d);
+  hipLaunchKernelGGL(prefill_down_kernel, dim3(tile_grid(long(n_rt) * d.n_col_tiles * d.k_split)), dim3(64 * MM_WAVES),
+                     DN_LDS, st, d);
   if (mark) mark->mark(st);
   const long n = long(a.T) * a.H;
   const int blocks = int((n / 4 + 255) / 256);
