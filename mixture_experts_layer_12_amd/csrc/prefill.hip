@@ -26,17 +26,21 @@
 //    path, which is what limits these kernels;
 //  * operands move global -> LDS with the gfx950 direct-to-LDS loads, one
 //    wave instruction = 8 rows x 128 bytes (the load path moves 64-byte row
-//    pieces at well under half the rate), into a 2-stage ring of 64 values
-//    of k (2 x 64 KiB);
+//    pieces at well under half the rate), in stages of 64 values of k; the
+//    weight operand (from HBM) has three ring slots and the other two
+//    (5 x 32 KiB), so weight loads are issued about two stages ahead;
 //  * a stage is multiplied in four MFMA k-steps; while one k-step is
 //    multiplied the operands of the next are read from LDS (interleaved one
-//    read per MFMA), and the refill of the free ring slot is spread over
-//    three k-steps (one load between MFMAs) so the matrix cores never wait
-//    behind a burst of load issues;
+//    read per MFMA), and the refills are spread over the k-steps (a few
+//    loads between MFMAs) so the matrix cores never wait behind a burst of
+//    load issues;
 //  * the 16-byte chunks of each staged row are XOR-permuted so the 16 rows
 //    one operand read touches fall on distinct LDS banks.
 // Row tiles follow the dispatch padding of this path (256 rows per expert
-// segment), so a tile never spans two experts.
+// segment), so a tile never spans two experts.  An expert's last tile with
+// at most 128 rows in use is a half tile: only those 128 token rows are
+// staged and the four waves split the weight rows instead (each 2 x 4 or
+// 4 x 2 MFMA blocks), half the work of a full tile.
 #include "common.hpp"
 
 namespace moe {
@@ -56,22 +60,14 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 constexpr int MM_TM = 256;                    // token rows per tile (the dispatch padding of this path)
 constexpr int MM_TN = 256;                    // weight rows per tile
 constexpr int MM_BK = 64;                     // k per LDS stage: 128-byte staged rows
-constexpr int MM_KS = MM_BK / 16;             // MFMA k-steps per stage
-constexpr int MM_ROWS = MM_TM + MM_TN;        // staged rows per stage
 constexpr int MM_WAVES = 4;
 constexpr int MM_RPI = 8;                     // staged rows per load instruction (1 KiB)
-constexpr int MM_DMA = MM_ROWS / MM_RPI / MM_WAVES;   // 16 load instructions per wave per stage
-constexpr int MM_STAGE = MM_ROWS * MM_BK;     // bf16 elements per stage
-constexpr int MM_S = 2;                       // ring depth
-constexpr int MM_NP = MM_KS - 1;              // k-steps that carry a refill part
-constexpr int MM_PQ = (MM_DMA + MM_NP - 1) / MM_NP;   // loads per part
-static_assert(MM_PQ <= 8, "one load per MFMA pair");
-constexpr size_t MM_LDS = size_t(MM_S) * MM_STAGE * sizeof(uint16_t);   // 128 KiB
-// The deep ring: three slots for the A operand (the one that streams from
-// HBM) and two for B, 5 x 32 KiB, the whole LDS of a CU.
+constexpr int MM_NS = 256 / MM_RPI / MM_WAVES;   // load instructions per wave per stage for 256 rows (8)
+constexpr int MM_DMA = 2 * MM_NS;             // at most: two operands of 256 rows
+// The ring: three slots for the operand that streams from HBM and two for
+// the other, 5 x 32 KiB, the whole LDS of a CU.
 constexpr int MM_HALF = MM_TM * MM_BK;        // bf16 elements of one operand's slot
-constexpr int MM_DMA_A = MM_TN / MM_RPI / MM_WAVES;   // A load instructions per wave per stage (q < 8)
-constexpr size_t MM_LDS_DEEP = size_t(5) * MM_HALF * sizeof(uint16_t);   // 160 KiB
+constexpr size_t MM_LDS = size_t(5) * MM_HALF * sizeof(uint16_t);   // 160 KiB
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (expcnt and lgkmcnt left unconstrained).
@@ -172,28 +168,35 @@ __device__ __forceinline__ void set_load(TileLoads& ld, int q, const uint16_t* b
   ld.upper |= unsigned(chunk >= 4) << q;
 }
 
-struct MMFrags { u32x4_t a[2][4], b[2][4]; };   // [k-step parity][32-row block]
+template <int NI, int NJ>
+struct MMFrags { u32x4_t a[2][NI], b[2][NJ]; };   // [k-step parity][32-row block]
 
-// The work-group's 256 x 256 MFMA tile over K (a multiple of 32).  Staged
-// rows [0, 256) are the A operand, [256, 512) the B operand.  This wave's A
-// blocks (32 rows each) start at a0 + (i & 1) * 32 + (i >> 1) * a_step, its B
-// blocks at 256 + b0 + 32 j; acc[i][j] accumulates A block i x B block j:
-// register q of lane l holds row 8 (q / 4) + 4 (l / 32) + q % 4 of A block i
-// and row l % 32 of B block j.
+// One wave's share of the work-group's MFMA tile over K (a multiple of 32).
+// Staged rows [0, 256) are the A operand, [256, 512) the B operand.  This
+// wave has NI A blocks of 32 rows, at a0 + (i & 1) * 32 + (i >> 1) * a_step
+// (NI = 4) or a0 + i * a_step (NI = 2), and NJ B blocks at 256 + b0 + 32 j;
+// acc[i][j] accumulates A block i x B block j: register q of lane l holds
+// row 8 (q / 4) + 4 (l / 32) + q % 4 of A block i and row l % 32 of B
+// block j.  A full tile is NI = NJ = 4 in every wave (256 x 256); a half
+// tile stages only 128 rows of one operand and gives each wave 2 x 4 or
+// 4 x 2 blocks.
 //
-// DEEP = 0: a ring of two stages (`smem`, MM_LDS bytes); the refill of a
-// freed slot is spread over the next three k-steps and must land within
-// about one stage.  DEEP = 1 (A) or 2 (B): that operand, the one that
-// streams from HBM, has three slots and the other two (`smem`, MM_LDS_DEEP
-// bytes); its rows are load instructions q < 8 of `ld`, the other
-// operand's q >= 8.  After the barrier of stage kt the fast operand of
-// stage kt + 2 is issued first (k-steps 3 and 0) and then the slow operand
-// of stage kt + 3 (k-steps 1 and 2 of the next stage), so the barrier of
-// stage kt + 1 waits for everything but those last loads (loads complete in
-// issue order): slow loads get about two stages to arrive, fast loads one.
-template <int DEEP>
+// The ring (`smem`, MM_LDS bytes) has three slots for the SLOW
+// operand (1: A, 2: B), the one that streams from HBM, and two for the
+// other; the slow operand's rows are load instructions q < MM_NS of `ld`,
+// the fast operand's the next NF.  After the barrier of stage kt the fast
+// operand of stage kt + 2 is issued first (k-steps 3 and 0) and then the
+// slow operand of stage kt + 3 (k-steps 1 and 2 of the next stage), so the
+// barrier of stage kt + 1 waits for everything but those last loads (loads
+// complete in issue order): slow loads get about two stages to arrive,
+// fast loads one.
+template <int SLOW, int NI, int NJ, int NF>
 __device__ __forceinline__ void mm_tile(uint16_t* smem, const TileLoads& ld, int K, int a0, int a_step, int b0,
-                                        f32x16_t (&acc)[4][4]) {
+                                        f32x16_t (&acc)[NI][NJ]) {
+  static_assert(SLOW == 1 || SLOW == 2, "slow operand");
+  static_assert((NI == 4 || NI == 2) && (NJ == 4 || NJ == 2) && (NF == 8 || NF == 4), "tile shape");
+  constexpr int NQ = MM_NS + NF;               // load instructions per wave per stage
+  static_assert(NQ <= MM_DMA, "load table");
   const int lane = threadIdx.x & 63;
   const int nk = (K + MM_BK - 1) / MM_BK;     // stages; K % 64 == 32 leaves a half-full last one
   const int nk_full = K / MM_BK;
@@ -201,232 +204,161 @@ __device__ __forceinline__ void mm_tile(uint16_t* smem, const TileLoads& ld, int
   // offset + r * MM_BK (B rows are r = 256 .. 511).
   auto slow = [](int kt) { return (kt % 3) * MM_HALF; };        // slots 0 .. 2
   auto fast = [](int kt) { return (3 + kt % 2) * MM_HALF; };    // slots 3, 4
-  auto a_slot = [&](int kt) { return DEEP == 1 ? slow(kt) : DEEP == 2 ? fast(kt) : (kt % MM_S) * MM_STAGE; };
-  auto b_slot = [&](int kt) {
-    return DEEP == 1 ? fast(kt) - MM_HALF : DEEP == 2 ? slow(kt) - MM_HALF : (kt % MM_S) * MM_STAGE;
-  };
+  auto a_slot = [&](int kt) { return SLOW == 1 ? slow(kt) : fast(kt); };
+  auto b_slot = [&](int kt) { return (SLOW == 1 ? fast(kt) : slow(kt)) - MM_HALF; };
   // In a half-full last stage, lanes whose chunk lies past K load the chunk
   // 32 values lower instead (in bounds), and the k-steps past K multiply a
   // zero B operand.
   auto issue = [&](int kt, auto q0, auto q1) {   // load instructions q0 .. q1 - 1 of stage kt
     const int k0 = kt * MM_BK;
     const bool part = k0 + MM_BK > K;
-    const int oa = a_slot(kt), ob = b_slot(kt);
+    const int os = SLOW == 1 ? a_slot(kt) : b_slot(kt), of = SLOW == 1 ? b_slot(kt) : a_slot(kt);
     static_for<decltype(q0)::value, decltype(q1)::value>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       const int back = (part && ((ld.upper >> q) & 1)) ? 32 : 0;
-      uint16_t* d = smem + ((q < MM_DMA_A) == (DEEP != 2) ? oa : ob);
+      uint16_t* d = smem + (q < MM_NS ? os : of);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(ld.base[q] + (ld.off[q] + uint32_t(k0 - back))),
                                        (lds_void_t*)(d + ld.row[q] * MM_BK), 16, 0, 0);
     });
   };
   using Q0 = std::integral_constant<int, 0>;
-  using QP = std::integral_constant<int, MM_PQ>;
-  using QALL = std::integral_constant<int, MM_DMA>;
+  using QS2 = std::integral_constant<int, MM_NS / 2>;
+  using QS = std::integral_constant<int, MM_NS>;
+  using QF2 = std::integral_constant<int, MM_NS + NF / 2>;
+  using QALL = std::integral_constant<int, NQ>;
 
   // Operand reads: row (block base + l % 32), chunk 2 * kstep + l / 32.
   const int l32 = lane & 31, hi = lane >> 5;
-  auto read_step = [&](int kt, int ks, MMFrags& f, auto steady) {   // the operands of one MFMA k-step
+  MMFrags<NI, NJ> f;
+  auto read_step = [&](int kt, int ks, auto steady) {   // the operands of one MFMA k-step
     const int h = ks & 1;
     const uint16_t* sh = smem + l32 * MM_BK + (((2 * ks + hi) ^ mm_swz(l32)) << 3);
     const uint16_t* sa = sh + a_slot(kt);
     const uint16_t* sb = sh + b_slot(kt);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.a[h][i] = *reinterpret_cast<const u32x4_t*>(sa + (a0 + (i & 1) * 32 + (i >> 1) * a_step) * MM_BK);
+    for (int i = 0; i < NI; ++i) {
+      const int r = NI == 4 ? a0 + (i & 1) * 32 + (i >> 1) * a_step : a0 + i * a_step;
+      f.a[h][i] = *reinterpret_cast<const u32x4_t*>(sa + r * MM_BK);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[h][j] = *reinterpret_cast<const u32x4_t*>(sb + (MM_TM + b0 + j * 32) * MM_BK);
+    for (int j = 0; j < NJ; ++j) f.b[h][j] = *reinterpret_cast<const u32x4_t*>(sb + (MM_TM + b0 + j * 32) * MM_BK);
     if (!steady && kt * MM_BK + ks * 16 >= K) {     // past K in a half-full last stage
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f.b[h][j] = u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < NJ; ++j) f.b[h][j] = u32x4_t{0, 0, 0, 0};
     }
   };
-  auto multiply = [&](const MMFrags& f, int h) {   // one MFMA k-step
+  auto multiply = [&](int h) {   // one MFMA k-step
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(f.a[h][i], f.b[h][j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32_bf16(f.a[h][i], f.b[h][j], acc[i][j]);
   };
-  // The 8 operand reads of one k-step go between the first 8 of the 16 MFMAs
-  // of the previous k-step, so at most 8 reads are in flight and they have
-  // landed by the time their own MFMAs start; `nv` loads from memory go
-  // between the last 8 MFMAs (after the reads: the compiler keeps LDS reads
-  // and LDS-writing loads in program order).
+  // Full tile: the 8 operand reads of one k-step go between the first 8 of
+  // the 16 MFMAs of the previous k-step, so at most 8 reads are in flight
+  // and they have landed by the time their own MFMAs start; `nv` loads from
+  // memory go between the last 8 MFMAs (after the reads: the compiler keeps
+  // LDS reads and LDS-writing loads in program order).  Half tile: 6 reads
+  // over the first 6 of 8 MFMAs and the loads over the last `nv`.
   auto interleave = [](auto nv) {
     constexpr int NV = decltype(nv)::value;
+    constexpr int NM = NI * NJ, NR = NI + NJ;
+    if constexpr (NM == 16) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one load
-    }
-    if constexpr (NV < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - NV, 0);
-  };
-  using no_loads = std::integral_constant<int, 0>;
-  using part_loads = QP;
-
-  // One stage.  Before its last k-step every read of stage kt has been
-  // issued; the barrier there (which also waits for this wave's reads) makes
-  // the slot of stage kt free and stage kt + 1 visible.  Steady state
-  // (kt + 2 < nk_full): straight-line code; part 0 of the refill (stage
-  // kt + 2) goes into the last k-step of stage kt, parts 1 and 2 into the
-  // first k-steps of stage kt + 1, and all of it has landed by the barrier of
-  // stage kt + 1.
-  MMFrags f;
-  auto step_steady = [&](int kt) {
-    static_for<0, MM_KS - 1>([&](auto kc) {
-      constexpr int ks = decltype(kc)::value;
-      multiply(f, ks & 1);
-      read_step(kt, ks + 1, f, std::true_type{});
-      if constexpr (ks + 1 < MM_NP) {
-        issue(kt + 1, std::integral_constant<int, (ks + 1) * MM_PQ>{},
-              std::integral_constant<int, ((ks + 2) * MM_PQ < MM_DMA ? (ks + 2) * MM_PQ : MM_DMA)>{});
-        interleave(part_loads{});
-      } else {
-        interleave(no_loads{});
+      for (int q = 0; q < NR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    wait_vmcnt<0>();     // stage kt + 1 landed (this wave's part)
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one load
+      }
+      if constexpr (NR + NV < NM) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR - NV, 0);
+    } else {
+      static_assert(NV <= NM, "one load per MFMA");
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
+        if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+        if (q >= NM - NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one load
+      }
+    }
+  };
+  using fast_loads = std::integral_constant<int, NF / 2>;
+  using slow_loads = std::integral_constant<int, MM_NS / 2>;
+
+  // Stage kt with every stage it issues (up to kt + 2) full: straight-line
+  // code.  With S the slow operand and F the fast one: k-step 0 issues the
+  // second half of F(kt + 1), k-steps 1 and 2 S(kt + 2); the barrier leaves
+  // S(kt + 2) in flight; k-step 3 issues the first half of F(kt + 2).
+  auto step_steady = [&](int kt) {
+    multiply(0);
+    read_step(kt, 1, std::true_type{});
+    issue(kt + 1, QF2{}, QALL{});
+    interleave(fast_loads{});
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(1);
+    read_step(kt, 2, std::true_type{});
+    issue(kt + 2, Q0{}, QS2{});
+    interleave(slow_loads{});
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(0);
+    read_step(kt, 3, std::true_type{});
+    issue(kt + 2, QS2{}, QS{});
+    interleave(slow_loads{});
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<MM_NS>();     // all but S(kt + 2): stage kt + 1 landed (this wave's part)
     ring_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    multiply(f, (MM_KS - 1) & 1);
-    read_step(kt + 1, 0, f, std::true_type{});
-    issue(kt + 2, Q0{}, QP{});
-    interleave(part_loads{});
+    multiply(1);
+    read_step(kt + 1, 0, std::true_type{});
+    issue(kt + 2, QS{}, QF2{});
+    interleave(fast_loads{});
     __builtin_amdgcn_sched_barrier(0);
   };
-  // The last stages (and every stage of a short k loop): refills are issued
-  // whole; `pend` says the previous (steady) stage left parts 1.. of the
-  // refill of stage kt + 1 to this one.
-  auto step_tail = [&](int kt, bool pend) {
-    if (pend) issue(kt + 1, QP{}, QALL{});
-    static_for<0, MM_KS - 1>([&](auto kc) {
-      constexpr int ks = decltype(kc)::value;
-      multiply(f, ks & 1);
-      read_step(kt, ks + 1, f, std::false_type{});
-    });
+  // The same issue pattern with guards (last stages, short k loops).
+  auto step_tail = [&](int kt) {
+    multiply(0);
+    read_step(kt, 1, std::false_type{});
+    if (kt + 1 < nk) issue(kt + 1, QF2{}, QALL{});
+    multiply(1);
+    read_step(kt, 2, std::false_type{});
+    if (kt + 2 < nk) issue(kt + 2, Q0{}, QS{});
+    multiply(0);
+    read_step(kt, 3, std::false_type{});
     const bool more = kt + 1 < nk;
     if (more) {
-      wait_vmcnt<0>();
+      if (kt + 2 < nk) wait_vmcnt<MM_NS>();
+      else wait_vmcnt<0>();
       ring_barrier();
     }
-    multiply(f, (MM_KS - 1) & 1);
+    multiply(1);
     if (more) {
-      read_step(kt + 1, 0, f, std::false_type{});
-      if (kt + 2 < nk) issue(kt + 2, Q0{}, QALL{});
+      read_step(kt + 1, 0, std::false_type{});
+      if (kt + 2 < nk) issue(kt + 2, QS{}, QF2{});
     }
   };
-
-  if constexpr (DEEP != 0) {
-    using QA = std::integral_constant<int, MM_DMA_A>;
-    using QA2 = std::integral_constant<int, MM_DMA_A / 2>;
-    using QB2 = std::integral_constant<int, MM_DMA_A + (MM_DMA - MM_DMA_A) / 2>;
-    using half_loads = std::integral_constant<int, MM_DMA_A / 2>;
-    static_assert(MM_DMA - MM_DMA_A == MM_DMA_A, "A and B take the same number of loads");
-    // Stage kt with every stage it issues (up to kt + 2) full: straight-line
-    // code.  With S the slow operand and F the fast one: k-step 0 issues the
-    // second half of F(kt + 1), k-steps 1 and 2 S(kt + 2); the barrier leaves
-    // S(kt + 2) in flight; k-step 3 issues the first half of F(kt + 2).
-    MMFrags f;
-    auto step_steady = [&](int kt) {
-      multiply(f, 0);
-      read_step(kt, 1, f, std::true_type{});
-      issue(kt + 1, QB2{}, QALL{});
-      interleave(half_loads{});
-      __builtin_amdgcn_sched_barrier(0);
-      multiply(f, 1);
-      read_step(kt, 2, f, std::true_type{});
-      issue(kt + 2, Q0{}, QA2{});
-      interleave(half_loads{});
-      __builtin_amdgcn_sched_barrier(0);
-      multiply(f, 0);
-      read_step(kt, 3, f, std::true_type{});
-      issue(kt + 2, QA2{}, QA{});
-      interleave(half_loads{});
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<MM_DMA_A>();     // all but A(kt + 2): stage kt + 1 landed (this wave's part)
-      ring_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      multiply(f, 1);
-      read_step(kt + 1, 0, f, std::true_type{});
-      issue(kt + 2, QA{}, QB2{});
-      interleave(half_loads{});
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // The same issue pattern with guards (last stages, short k loops).
-    auto step_tail = [&](int kt) {
-      multiply(f, 0);
-      read_step(kt, 1, f, std::false_type{});
-      if (kt + 1 < nk) issue(kt + 1, QB2{}, QALL{});
-      multiply(f, 1);
-      read_step(kt, 2, f, std::false_type{});
-      if (kt + 2 < nk) issue(kt + 2, Q0{}, QA{});
-      multiply(f, 0);
-      read_step(kt, 3, f, std::false_type{});
-      const bool more = kt + 1 < nk;
-      if (more) {
-        if (kt + 2 < nk) wait_vmcnt<MM_DMA_A>();
-        else wait_vmcnt<0>();
-        ring_barrier();
-      }
-      multiply(f, 1);
-      if (more) {
-        read_step(kt + 1, 0, f, std::false_type{});
-        if (kt + 2 < nk) issue(kt + 2, QA{}, QB2{});
-      }
-    };
-    // Prologue: stage 0, S(1), the first half of F(1); wait for stage 0.
-    issue(0, Q0{}, QALL{});
-    if (1 < nk) {
-      issue(1, Q0{}, QB2{});
-      wait_vmcnt<QB2::value>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    ring_barrier();
-    read_step(0, 0, f, std::false_type{});
-    int kt = 0;
-    for (; kt + 2 < nk_full; ++kt) step_steady(kt);
-    for (; kt < nk; ++kt) step_tail(kt);
-    return;
-  }
-
-  // Prologue: stage 0 whole, stage 1 whole or (when a steady step follows)
-  // its part 0; wait for stage 0.
-  const bool piped = 2 < nk_full;
+  // Prologue: stage 0, S(1), the first half of F(1); wait for stage 0.
   issue(0, Q0{}, QALL{});
   if (1 < nk) {
-    if (piped) {
-      issue(1, Q0{}, QP{});
-      wait_vmcnt<MM_PQ>();
-    } else {
-      issue(1, Q0{}, QALL{});
-      wait_vmcnt<MM_DMA>();
-    }
+    issue(1, Q0{}, QF2{});
+    wait_vmcnt<QF2::value>();
   } else {
     wait_vmcnt<0>();
   }
   ring_barrier();
-  read_step(0, 0, f, std::false_type{});
+  read_step(0, 0, std::false_type{});
   int kt = 0;
   for (; kt + 2 < nk_full; ++kt) step_steady(kt);
-  bool pend = piped;
-  for (; kt < nk; ++kt) {
-    step_tail(kt, pend);
-    pend = false;
-  }
+  for (; kt < nk; ++kt) step_tail(kt);
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+template <int NI, int NJ>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NI][NJ]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 }
@@ -434,28 +366,86 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 // --------------------------------------------------------------- gate/up --
 // Tile: 256 sorted rows (tokens) x 128 intermediate columns.  Staged A rows
 // [0, 128) are gate rows, [128, 256) the up rows of the same columns; B rows
-// are the gathered token rows.  Wave (wm, wn) = (w / 2, w % 2) multiplies
-// tokens [128 wm, +128) with columns [64 wn, +64) of gate and up (A blocks:
-// gate 2, up 2), so a lane holds matching gate and up sums: 4 consecutive
-// intermediate columns of one token per register group.  Each wave stages
-// a quarter of the gate rows, the same up rows and a quarter of the tokens.
+// are the gathered token rows.  Full tile: wave (wm, wn) = (w / 2, w % 2)
+// multiplies tokens [128 wm, +128) with columns [64 wn, +64) of gate and up
+// (A blocks: gate 2, up 2).  Half tile (tokens [0, 128) only): wave w
+// multiplies them with columns [32 w, +32) of gate and up (A blocks: gate
+// 1, up 1).  Either way a lane holds matching gate and up sums: 4
+// consecutive intermediate columns of one token per register group.  Each
+// wave stages a quarter of the gate rows, the same up rows and a quarter of
+// the tokens.
 
 constexpr int GU_BN = MM_TN / 2;              // intermediate columns per tile
-#ifndef MOE_PF_DEEP
-#define MOE_PF_DEEP 1
-#endif
-constexpr int MM_GU_DEEP = MOE_PF_DEEP != 0 ? 1 : 0;   // weight rows (A) get the three-slot ring
-constexpr size_t GU_LDS = MM_GU_DEEP ? MM_LDS_DEEP : MM_LDS;
-#ifndef MOE_PF_DN_DEEP
-#define MOE_PF_DN_DEEP 1
-#endif
-constexpr int MM_DN_DEEP = MOE_PF_DN_DEEP != 0 ? 2 : 0;   // weight rows (B) get the three-slot ring
-constexpr size_t DN_LDS = MM_DN_DEEP ? MM_LDS_DEEP : MM_LDS;
+
+template <bool HALF>
+__device__ __forceinline__ void gateup_tile(const PrefillArgs& a, uint16_t* smem, bool routed, int local, int N,
+                                            const uint16_t* Wg, const uint16_t* Wu, int n0, int hrow0) {
+  constexpr int NI = HALF ? 2 : 4, NJ = 4, NF = HALF ? 4 : 8;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int H = a.H;
+  TileLoads ld;
+  ld.upper = 0;
+  const int lrow = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {                 // instructions 0..7: gate / up rows, 8 at a time
+    const int r = wv * 32 + j * 8;              // first row within the gate (or up) block
+    const int n = n0 + r + lrow;
+    const int src = n < N ? n : n0;             // rows past N are read but never stored
+    set_load(ld, 2 * j, Wg, r, src, H, lane);
+    set_load(ld, 2 * j + 1, Wu, GU_BN + r, src, H, lane);
+  }
+  const uint16_t* const xb = reinterpret_cast<const uint16_t*>(a.x);
+  constexpr int TPW = HALF ? 32 : 64;           // token rows staged per wave
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {                // instructions 8..: token rows
+    const int m = wv * TPW + j * 8 + lrow;
+    int tok;
+    if (routed) {
+      const int fl = a.sorted_ids[hrow0 + m];
+      tok = fl < a.T * a.k ? fl / a.k : 0;      // padding rows read a real row; their outputs are never used
+    } else {
+      tok = local * MM_TM + m;
+      tok = tok < a.T ? tok : 0;
+    }
+    set_load(ld, MM_NS + j, xb, MM_TN + wv * TPW + j * 8, tok, H, lane);
+  }
+
+  const int wm = HALF ? 0 : wv >> 1, wn = HALF ? wv : wv & 1;
+  constexpr int WC = HALF ? 32 : 64;            // columns of gate (and of up) per wave
+  f32x16_t acc[NI][NJ];
+  zero_acc(acc);
+  mm_tile<1, NI, NJ, NF>(smem, ld, H, wn * WC, GU_BN, wm * 128, acc);
+
+  // epilogue: h[row][n] = bf16(silu(g) * u); A blocks [0, NI/2) are gate, the rest up
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NI / 2; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + wn * WC + i * 32 + g * 8 + hi * 4;
+      if (n >= N) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int m = wm * 128 + j * 32 + l32;
+        float hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[i][j][4 * g + q]) * acc[i + NI / 2][j][4 * g + q];
+        *reinterpret_cast<u32x2_t*>(a.h + size_t(hrow0 + m) * a.h_stride + n) =
+            u32x2_t{pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3])};
+      }
+    }
+}
+
+// Whether row tile rt has at most 128 rows in use (rows 128 .. 255 are all
+// dispatch padding, or past the tokens of a shared expert).
+__device__ __forceinline__ bool half_tile(const PrefillArgs& a, int rt, int n_routed_tiles) {
+  if (rt < n_routed_tiles) return a.sorted_ids[rt * MM_TM + 128] >= a.T * a.k;
+  return (rt - n_routed_tiles) % (a.t_pad / MM_TM) * MM_TM + 128 >= a.T;
+}
 
 __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const TileList L = tile_list(a, a.n_col_tiles, 1);
   int kr, rt, ct;
   if (!tile_item(blockIdx.x, L, kr, rt, ct)) return;
@@ -481,72 +471,96 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillAr
   }
   const int n0 = ct * GU_BN;
   if (n0 >= N) return;
-  const int hrow0 = rt * MM_TM;
-
-  TileLoads ld;
-  ld.upper = 0;
-  const int lrow = lane >> 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {                 // instructions 0..7: gate / up rows, 8 at a time
-    const int r = wv * 32 + j * 8;              // first row within the gate (or up) block
-    const int n = n0 + r + lrow;
-    const int src = n < N ? n : n0;             // rows past N are read but never stored
-    set_load(ld, 2 * j, Wg, r, src, H, lane);
-    set_load(ld, 2 * j + 1, Wu, GU_BN + r, src, H, lane);
-  }
-  const uint16_t* const xb = reinterpret_cast<const uint16_t*>(a.x);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {                 // instructions 8..15: token rows
-    const int m = wv * 64 + j * 8 + lrow;
-    int tok;
-    if (routed) {
-      const int fl = a.sorted_ids[hrow0 + m];
-      tok = fl < a.T * a.k ? fl / a.k : 0;      // padding rows read a real row; their outputs are never used
-    } else {
-      tok = local * MM_TM + m;
-      tok = tok < a.T ? tok : 0;
-    }
-    set_load(ld, 8 + j, xb, MM_TN + wv * 64 + j * 8, tok, H, lane);
-  }
-
-  const int wm = wv >> 1, wn = wv & 1;
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-  mm_tile<MM_GU_DEEP>(smem, ld, H, wn * 64, GU_BN, wm * 128, acc);
-
-  // epilogue: h[row][n] = bf16(silu(g) * u); A blocks 0-1 are gate, 2-3 up
-  const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * 64 + i * 32 + g * 8 + hi * 4;
-      if (n >= N) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = wm * 128 + j * 32 + l32;
-        float hv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[i][j][4 * g + q]) * acc[i + 2][j][4 * g + q];
-        *reinterpret_cast<u32x2_t*>(a.h + size_t(hrow0 + m) * a.h_stride + n) =
-            u32x2_t{pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3])};
-      }
-    }
+  if (half_tile(a, rt, n_routed_tiles)) gateup_tile<true>(a, smem, routed, local, N, Wg, Wu, n0, rt * MM_TM);
+  else gateup_tile<false>(a, smem, routed, local, N, Wg, Wu, n0, rt * MM_TM);
 }
 
 // ------------------------------------------------------------------ down --
 // Tile: 256 sorted rows x 256 hidden columns.  Staged A rows are activation
 // rows (sorted order, contiguous), B rows the down-projection rows of the
-// hidden outputs.  Wave (wm, wn) multiplies rows [128 wm, +128) with columns
-// [128 wn, +128); register q of a lane holds one hidden column of 16 sorted
-// rows, which it scales by the routing weight and adds into the fp32
-// accumulator with hardware float atomics (lanes 0-31 cover 32 consecutive
-// columns of one row).  Each wave stages a quarter of each operand.
+// hidden outputs.  Full tile: wave (wm, wn) multiplies rows [128 wm, +128)
+// with columns [128 wn, +128).  Half tile (rows [0, 128) only): wave w
+// multiplies them with columns [64 w, +64).  Register q of a lane holds one
+// hidden column of 16 sorted rows, which it scales by the routing weight
+// and adds into the fp32 accumulator with hardware float atomics (lanes
+// 0-31 cover 32 consecutive columns of one row).  Each wave stages a
+// quarter of each operand.
+
+template <bool HALF>
+__device__ __forceinline__ void down_tile(const PrefillArgs& a, uint16_t* smem, const uint16_t* Wd, int K, int rt,
+                                          int n_routed_tiles, int n0, int k_begin, int k_len) {
+  constexpr int NI = 4, NJ = HALF ? 2 : 4, NF = HALF ? 4 : 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(int(tid >> 6));
+  const int H = a.H, hrow0 = rt * MM_TM;
+  TileLoads ld;
+  ld.upper = 0;
+  const int lrow = lane >> 3;
+  // The weight rows (B, from HBM) are the slow operand: load instructions
+  // 0..7, the activation rows the next NF.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {                 // down-projection rows
+    const int r = wv * 64 + j * 8;
+    const int n = n0 + r + lrow;
+    set_load(ld, j, Wd + k_begin, MM_TM + r, n < H ? n : n0, K, lane);   // columns past H are never stored
+  }
+  constexpr int RPW = HALF ? 32 : 64;           // activation rows staged per wave
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {                // activation rows
+    const int r = wv * RPW + j * 8;
+    set_load(ld, MM_NS + j, a.h + k_begin, r, hrow0 + r + lrow, a.h_stride, lane);
+  }
+
+  const int wm = HALF ? 0 : wv >> 1, wn = HALF ? wv : wv & 1;
+  constexpr int WC = HALF ? 64 : 128;           // hidden columns per wave
+  f32x16_t acc[NI][NJ];
+  zero_acc(acc);
+  mm_tile<2, NI, NJ, NF>(smem, ld, k_len, wm * 128, 64, wn * WC, acc);
+
+  // The tile's token ids (-1: padding) and routing weights of this wave's
+  // rows go to the slow operand's slot nk % 3, which no wave reads or fills
+  // any more: its last stage (nk - 3) was read before the barrier of stage
+  // nk - 2, which every wave has passed, and stage nk is never loaded.  Each
+  // wave writes the rows it reads (waves with the same rows write the same
+  // values), so no barrier is needed.
+  const int nk = (k_len + MM_BK - 1) / MM_BK;
+  int* tok_s = reinterpret_cast<int*>(smem + (nk % 3) * MM_HALF);
+  float* w_s = reinterpret_cast<float*>(tok_s + MM_TM);
+  const int n_asg = a.T * a.k;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int m = wm * 128 + u * 64 + lane;
+    if (rt < n_routed_tiles) {
+      const int fl = a.sorted_ids[hrow0 + m];
+      const bool ok = fl < n_asg;
+      tok_s[m] = ok ? fl / a.k : -1;
+      w_s[m] = ok ? a.topk_w[fl] : 0.f;
+    } else {
+      const int t = (rt - n_routed_tiles) % (a.t_pad / MM_TM) * MM_TM + m;
+      tok_s[m] = t < a.T ? t : -1;
+      w_s[m] = 1.0f;
+    }
+  }
+
+  // epilogue: acc[t][n] += w * y
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * WC + j * 32 + l32;
+    if (n >= H) continue;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = wm * 128 + i * 32 + (q >> 2) * 8 + hi * 4 + (q & 3);
+        const int t = tok_s[m];
+        if (t >= 0) unsafeAtomicAdd(a.acc + size_t(t) * H + n, w_s[m] * acc[i][j][q]);
+      }
+  }
+}
 
 __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(int(tid >> 6));
   // work-group = (k range, tile)
   const TileList L = tile_list(a, a.n_col_tiles, a.k_split);
   int kr, rt, ct;
@@ -567,67 +581,13 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs
     Wd = a.sd + size_t(s) * H * a.Is;
   }
   const int n0 = ct * MM_TN;
-  const int hrow0 = rt * MM_TM;
   // this work-group's k range [k_begin, k_begin + k_len): whole 64-deep stages except maybe the end
   const int k_chunk = (K + 64 * a.k_split - 1) / (64 * a.k_split) * 64;
   const int k_begin = kr * k_chunk;
   const int k_len = min(k_chunk, K - k_begin);
   if (k_len <= 0) return;
-
-  TileLoads ld;
-  ld.upper = 0;
-  const int lrow = lane >> 3;
-  // The weight rows (B, from HBM) are the slow operand: load instructions
-  // 0..7, the activation rows 8..15.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {                 // down-projection rows
-    const int r = wv * 64 + j * 8;
-    const int n = n0 + r + lrow;
-    set_load(ld, j, Wd + k_begin, MM_TM + r, n < H ? n : n0, K, lane);   // columns past H are never stored
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {                 // activation rows
-    const int r = wv * 64 + j * 8;
-    set_load(ld, 8 + j, a.h + k_begin, r, hrow0 + r + lrow, a.h_stride, lane);
-  }
-
-  const int wm = wv >> 1, wn = wv & 1;
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-  mm_tile<MM_DN_DEEP>(smem, ld, k_len, wm * 128, 64, wn * 128, acc);
-
-  // the ring is free once every wave is done with it: the tile's token ids
-  // (-1: padding) and routing weights go there
-  __syncthreads();
-  int* tok_s = reinterpret_cast<int*>(smem);
-  float* w_s = reinterpret_cast<float*>(smem) + MM_TM;
-  if (rt < n_routed_tiles) {
-    const int fl = a.sorted_ids[rt * MM_TM + tid];
-    const bool ok = fl < a.T * a.k;
-    tok_s[tid] = ok ? fl / a.k : -1;
-    w_s[tid] = ok ? a.topk_w[fl] : 0.f;
-  } else {
-    const int t = (rt - n_routed_tiles) % (a.t_pad / MM_TM) * MM_TM + tid;
-    tok_s[tid] = t < a.T ? t : -1;
-    w_s[tid] = 1.0f;
-  }
-  __syncthreads();
-
-  // epilogue: acc[t][n] += w * y
-  const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + j * 32 + l32;
-    if (n >= H) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = wm * 128 + i * 32 + (q >> 2) * 8 + hi * 4 + (q & 3);
-        const int t = tok_s[m];
-        if (t >= 0) unsafeAtomicAdd(a.acc + size_t(t) * H + n, w_s[m] * acc[i][j][q]);
-      }
-  }
+  if (half_tile(a, rt, n_routed_tiles)) down_tile<true>(a, smem, Wd, K, rt, n_routed_tiles, n0, k_begin, k_len);
+  else down_tile<false>(a, smem, Wd, K, rt, n_routed_tiles, n0, k_begin, k_len);
 }
 
 // ------------------------------------------------------------------ cast --
@@ -659,9 +619,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   // dynamic LDS above 64 KiB must be allowed per kernel (thread-safe one-time set-up)
   static const hipError_t attr_rc = [] {
     hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_gateup_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(GU_LDS));
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(MM_LDS));
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_down_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(DN_LDS));
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(MM_LDS));
     return e1 != hipSuccess ? e1 : e2;
   }();
   if (attr_rc != hipSuccess) return attr_rc;
@@ -671,7 +631,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   const int nmax = a.I > a.Is ? a.I : a.Is;
   g.n_row_tiles = n_rt;
   g.n_col_tiles = (nmax + GU_BN - 1) / GU_BN;
-  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(tile_grid(long(n_rt) * g.n_col_tiles)), dim3(64 * MM_WAVES), GU_LDS, st,
+  hipLaunchKernelGGL(prefill_gateup_kernel, dim3(tile_grid(long(n_rt) * g.n_col_tiles)), dim3(64 * MM_WAVES), MM_LDS, st,
                      g);
   if (mark) mark->mark(st);
   PrefillArgs d = a;
@@ -681,7 +641,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   // idle (one work-group per CU): split k so there are at least ~4 rounds.
   d.k_split = down_k_split(n_rt * d.n_col_tiles, nmax);
   hipLaunchKernelGGL(prefill_down_kernel, dim3(tile_grid(long(n_rt) * d.n_col_tiles * d.k_split)), dim3(64 * MM_WAVES),
-                     DN_LDS, st, d);
+                     MM_LDS, st, d);
   if (mark) mark->mark(st);
   const long n = long(a.T) * a.H;
   const int blocks = int((n / 4 + 255) / 256);
