@@ -151,6 +151,33 @@ def test_single_launch_decode_equals_multi_launch(m, name):
     _check_forward(m, wl, inp, path=3)
 
 
+@pytest.mark.parametrize("H_", [128, 160])
+def test_prefill_tile_classes(m, H_):
+    """Expert counts chosen at the prefill row-tile boundaries: 129 rows (one
+    full tile, 127 padding), 128 (a half tile: at most 128 rows in use), 385
+    (a full tile, then a last tile of 129 rows), exactly 256 (no padding) and
+    1 (a half tile of one row).  The routing is forced through one-hot router
+    rows; H = 160 also leaves a half-full last k stage."""
+    counts = [129, 128, 385, 256, 1]
+    E = len(counts)
+    T = sum(counts)
+    wl = W("prefill_tiles", T=T, H=H_, E=E, k=1, I=96, S=1, Is=64)
+    inp = _inputs(wl, 4)
+    choice = np.repeat(np.arange(E), counts)
+    np.random.default_rng(5).shuffle(choice)
+    x = np.random.default_rng(6).standard_normal((T, H_)).astype(np.float32)
+    x[:, :E] = 0.0
+    x[np.arange(T), choice] = 4.0
+    wr = np.zeros((E, H_), np.float32)
+    wr[np.arange(E), np.arange(E)] = 1.0
+    inp["x"] = synth.f32_to_bf16_bits(x)
+    inp["router_w"] = synth.f32_to_bf16_bits(wr)
+    inp["router_b"] = None
+    _, ref = _check_forward(m, wl, inp, path=2)
+    assert (ref["ids_used"][:, 0] == choice).all()
+    assert np.bincount(ref["ids_used"][:, 0], minlength=E).tolist() == counts
+
+
 @pytest.mark.parametrize("path", [1, 2, 3])
 def test_all_tokens_to_one_expert(m, path):
     wl = W("one_expert", T=20, H=128, E=8, k=2, I=64, S=1, Is=64)
