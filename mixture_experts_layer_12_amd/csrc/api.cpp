@@ -21,6 +21,7 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_til
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
 hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t st);
 hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, StageMarker* mark);
+hipError_t launch_sparse_route_select(const RouterArgs& ra, const SparseArgs& a, int rdt, int xdt, hipStream_t st);
 }  // namespace moe
 
 namespace {
@@ -468,7 +469,11 @@ SparseLayout make_sparse_layout(const moe_shape_t* s0, int c) {
   const int Tr = std::max(S.L.Tr, 1);
   size_t off = S.L.total;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
-  S.sel = take(size_t(Tr) * s.top_k * c * 4);
+  // kept channels: [T*k, c], or [T*E, c] when the selection runs for every
+  // expert next to a single-tile router (E <= 16, passes of <= 16 tokens)
+  size_t sel_rows = size_t(Tr) * s.top_k;
+  if (s.E <= 16) sel_rows = std::max(sel_rows, size_t(std::min(Tr, 16)) * s.E);
+  S.sel = take(sel_rows * c * 4);
   S.hs = take(size_t(Tr) * s.top_k * c * 4);
   size_t rows = 0;
   for (int Tc = 1; Tc <= Tr; ++Tc) rows = std::max(rows, size_t(Tc) * s.top_k * sparse_splits(&s, Tc, c));
@@ -518,7 +523,11 @@ int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float
     rbd.tile_expert = nullptr;
     moe::RouterArgs ra = router_args(s, Tc, xc, router_w, router_b, rbd, 1);
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
+    // one routing tile: the channel selection runs for every expert in the
+    // router's launch instead of waiting for it
+    const bool sel_all = nblocks == 1;
+    if (!sel_all)
+      if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     moe::SparseArgs a{};
     moe::DecodeArgs& d = a.d;
     d.x = xc;
@@ -544,6 +553,9 @@ int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float
     a.sel = reinterpret_cast<int32_t*>(ws + SL.sel);
     a.hs = reinterpret_cast<float*>(ws + SL.hs);
     a.spart = reinterpret_cast<float*>(ws + SL.spart);
+    a.sel_all = sel_all ? 1 : 0;
+    if (sel_all)
+      if (int e = hip_status(moe::launch_sparse_route_select(ra, a, s->router_dtype, s->x_dtype, st))) return e;
     if (int e = hip_status(moe::launch_sparse(a, s->w_dtype, s->x_dtype, st, nullptr))) return e;
   }
   return MOE_OK;

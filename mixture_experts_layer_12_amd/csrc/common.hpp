@@ -350,7 +350,8 @@ struct SparseArgs {
   const uint8_t* wdt;         // routed down, transposed: [E, I, H]
   int c;                      // channels kept per (token, engaged expert)
   int R;                      // splits of the kept channels in the down projection
-  int32_t* sel;               // [T*k, c] kept channels, ascending
+  int32_t* sel;               // [T*k, c] kept channels, ascending; with sel_all [T*E, c], every expert
+  int sel_all;                // 1: the selection ran for every (token, expert), alongside the router
   float* hs;                  // [T*k, c] routing-weighted activations of the kept channels
   float* spart;               // [T*k, R, H] down partial rows
 };

@@ -12,7 +12,11 @@
 //
 // Launches of one pass (T <= 64 tokens): router (+ dispatch), channel
 // selection, sparse gate/up and the shared experts' gate/up, sparse down and
-// the shared experts' down, combine.
+// the shared experts' down, combine.  When the router is one work-group
+// (E <= 16 experts, T <= 16 tokens) the selection runs in the router's
+// launch, for every (token, expert): it needs only the scores, so it no
+// longer waits for the routing, and the engaged rows are picked through
+// topk_ids afterwards (E / k times the selection work, all in parallel).
 //
 //   select:  one work-group of 16 waves per (token, engaged expert).  Scores
 //            become order-preserving 32-bit keys in LDS; a radix select over 4
@@ -73,12 +77,12 @@ static_assert(kSelBins <= 2 * kSelWaves * 64 && (1 << 10) >= kSelWaves * 64, "tw
 // histogram of the keys that match the digits chosen so far, counted with LDS
 // atomics (a wave's lanes rarely share a bin once 11 bits are used), then one
 // ordered compaction.  Keys stay in LDS.
-__global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArgs a) {
-  extern __shared__ uint32_t keys[];                 // [I], then hist [2048], then scratch
-  const int f = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Channels of token t, expert e into `out` (c ints); `keys` is LDS of
+// sparse_select_lds_bytes(I) bytes.
+__device__ __forceinline__ void select_channels(const SparseArgs& a, int t, int e, int32_t* out, uint32_t* keys) {
+  const int tid = threadIdx.x;
   constexpr int NT = kSelWaves * 64;
-  const int I = a.d.I, c = a.c, k = a.d.k;
-  const int t = f / k, e = a.topk_ids[f];
+  const int I = a.d.I, c = a.c;
   const float* s = a.scores + (size_t(t) * a.d.E + e) * I;
   uint32_t* hist = keys + I;
   int* misc = reinterpret_cast<int*>(hist + kSelBins);   // [0] bin, [1] remaining, [4..20) scan scratch
@@ -142,7 +146,6 @@ __global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArg
   const int eq_base = wg_exclusive_scan(n_eq, misc + 4);
   const int take_eq = min(max(remaining - eq_base, 0), n_eq);
   int pos = wg_exclusive_scan(n_gt + take_eq, misc + 4);
-  int32_t* out = a.sel + size_t(f) * c;
   int eq_seen = 0;
   for (int i = i0; i < i1; ++i) {
     const uint32_t kk = keys[i];
@@ -150,6 +153,37 @@ __global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArg
     if (kk == prefix) keep = eq_seen++ < take_eq;
     if (keep && pos < c) out[pos++] = i;      // exactly c are kept; the bound only guards the buffer
   }
+}
+
+__global__ void __launch_bounds__(kSelWaves * 64) sparse_select_kernel(SparseArgs a) {
+  extern __shared__ uint32_t keys[];                 // [I], then hist [2048], then scratch
+  const int f = blockIdx.x;
+  select_channels(a, f / a.d.k, a.topk_ids[f], a.sel + size_t(f) * a.c, keys);
+}
+
+// Router and channel selection in one launch, for a single-work-group
+// router: work-group 0 routes (logits, top-k, dispatch, as the router's
+// fused kernel), work-groups 1 .. T*E select the channels of every
+// (token, expert), which needs only the scores; the selection no longer
+// waits for the routing.  The engaged experts' rows are picked up later
+// through topk_ids.
+template <int RT, int XT, int MODE>
+__global__ void __launch_bounds__(kSelWaves * 64) sparse_route_select_kernel(RouterArgs ra, SparseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  if (blockIdx.x == 0) {
+    __shared__ float lg[256];
+    logits_tile<RT, XT, false, 1>(ra, 0, 0, 0, kLogitChunks, reinterpret_cast<float*>(lds), lg);
+    __syncthreads();
+    select_and_dispatch<false, MODE>(ra, lg, true, lds);
+    return;
+  }
+  const int f = blockIdx.x - 1;
+  select_channels(a, f / a.d.E, f % a.d.E, a.sel + size_t(f) * a.c, reinterpret_cast<uint32_t*>(lds));
+}
+
+// Row of `sel` with the kept channels of assignment f.
+__device__ __forceinline__ size_t sel_row(const SparseArgs& a, int f) {
+  return a.sel_all ? size_t(f / a.d.k) * a.d.E + a.topk_ids[f] : size_t(f);
 }
 
 // ------------------------------------------------------------- gate/up ---
@@ -165,7 +199,7 @@ __global__ void __launch_bounds__(kGuWaves * 64) sparse_gateup_kernel(SparseArgs
   const int rt = blockIdx.x, f = blockIdx.y, c = a.c, K = d.H;
   const int t = f / d.k, e = a.topk_ids[f];
   const int r = rt * 16 + (lane & 15);
-  const int chan = a.sel[size_t(f) * c + (r < c ? r : c - 1)];     // past the end: a kept row, output dropped
+  const int chan = a.sel[sel_row(a, f) * c + (r < c ? r : c - 1)];     // past the end: a kept row, output dropped
   RowPtr<WT> rg, ru;
   rg.init(d.wg, d.E, d.I, K, e, chan);
   ru.init(d.wu, d.E, d.I, K, e, chan);
@@ -217,7 +251,7 @@ __global__ void __launch_bounds__(256) sparse_down_kernel(SparseArgs a) {
   const int e = a.topk_ids[f];
   const int q0 = int(long(r) * c / a.R), q1 = int(long(r + 1) * c / a.R);
   for (int q = q0 + threadIdx.x; q < q1; q += 256) {
-    qsel[q - q0] = a.sel[size_t(f) * c + q];
+    qsel[q - q0] = a.sel[sel_row(a, f) * c + q];
     qh[q - q0] = a.hs[size_t(f) * c + q];
   }
   __syncthreads();
@@ -306,6 +340,43 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
 
 size_t sparse_select_lds_bytes(int I) { return (size_t(I) + kSelBins + 4 + kSelWaves) * 4; }
 
+size_t router_lds_bytes(int NW, int E, int n, bool stage);
+
+template <int RT, int XT, int MODE>
+static void launch_route_select_m(const RouterArgs& ra, const SparseArgs& a, hipStream_t st) {
+  const size_t lds_max = std::max(router_lds_bytes(16, 16, 16 * 16, false), sparse_select_lds_bytes(16384));
+  static const bool attr = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_route_select_kernel<RT, XT, MODE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_max));
+    return true;
+  }();
+  (void)attr;
+  const size_t lds = std::max(router_lds_bytes(16, ra.E, ra.T * ra.k, false), sparse_select_lds_bytes(a.d.I));
+  hipLaunchKernelGGL((sparse_route_select_kernel<RT, XT, MODE>), dim3(1 + a.d.T * a.d.E), dim3(kSelWaves * 64), lds,
+                     st, ra, a);
+}
+
+template <int RT, int XT>
+static void launch_route_select_t(const RouterArgs& ra, const SparseArgs& a, hipStream_t st) {
+  const int mode = topk_mode(ra.E, ra.k);
+  if (mode == kTopkT8) launch_route_select_m<RT, XT, kTopkT8>(ra, a, st);
+  else if (mode == kTopkT16) launch_route_select_m<RT, XT, kTopkT16>(ra, a, st);
+  else launch_route_select_m<RT, XT, kTopkRow16>(ra, a, st);
+}
+
+// The router of a single routing tile (E <= 16 experts, T <= 16 tokens) and
+// the channel selection of every (token, expert) in one launch; a.sel_all
+// must be set and a.sel must hold T*E rows.
+hipError_t launch_sparse_route_select(const RouterArgs& ra, const SparseArgs& a, int rdt, int xdt, hipStream_t st) {
+  if (!a.sel_all || ra.n_row_tiles * ra.n_col_tiles != 1 || ra.E > 16 || ra.T > 16) return hipErrorInvalidValue;
+  if (rdt == DT_F32 && xdt == DT_F32) launch_route_select_t<DT_F32, DT_F32>(ra, a, st);
+  else if (rdt == DT_F32) launch_route_select_t<DT_F32, DT_BF16>(ra, a, st);
+  else if (xdt == DT_F32) launch_route_select_t<DT_BF16, DT_F32>(ra, a, st);
+  else launch_route_select_t<DT_BF16, DT_BF16>(ra, a, st);
+  return hipGetLastError();
+}
+
+// With a.sel_all the selection already ran (launch_sparse_route_select).
 template <int WT, int XT>
 static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t st, StageMarker* mark) {
   const int n = a.d.T * a.d.k;
@@ -315,7 +386,8 @@ static hipError_t launch_sparse_t(const SparseArgs& a, hipStream_t st, StageMark
     return true;
   }();
   (void)attr;
-  hipLaunchKernelGGL(sparse_select_kernel, dim3(n), dim3(kSelWaves * 64), sparse_select_lds_bytes(a.d.I), st, a);
+  if (!a.sel_all)
+    hipLaunchKernelGGL(sparse_select_kernel, dim3(n), dim3(kSelWaves * 64), sparse_select_lds_bytes(a.d.I), st, a);
   if (mark) mark->mark(st);
   hipLaunchKernelGGL((sparse_gateup_kernel<WT, XT>), dim3((a.c + 15) / 16, n), dim3(kGuWaves * 64), 0, st, a);
   if (hipError_t e = launch_decode_shared(a.d, WT, XT, st)) return e;     // shared experts: dense

@@ -28,6 +28,7 @@ CASES = {
     "bf16_c1": (W("bf16_c1", T=2, H=192, E=6, k=3, I=64), 1),
     "bf16_wide_h_c300": (W("bf16_wide_h", T=2, H=4160, E=4, k=2, I=1536), 300),
     "f32x_bf16w_t8_c64": (W("f32x_bf16w", T=8, H=256, E=16, k=4, I=512, x_dtype="f32", r_dtype="bf16"), 64),
+    "bf16_k10_c20": (W("bf16_k10", T=3, H=128, E=12, k=10, I=64), 20),
 }
 
 
