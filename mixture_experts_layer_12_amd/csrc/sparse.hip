@@ -60,8 +60,12 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* lds_nw) {
   }
   if (lane == 63) lds_nw[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += lds_nw[w];
+  // the totals of the waves before this one: one read per lane, then a
+  // reduction over the first 16 lanes (integer sums: order does not matter)
+  int base = lane < wave ? lds_nw[lane] : 0;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) base += __shfl_xor(base, d);
+  base = __shfl(base, 0);
   __syncthreads();
   return base + incl - v;
 }
@@ -108,10 +112,12 @@ __device__ __forceinline__ void select_channels(const SparseArgs& a, int t, int 
     const int shift = sel_shift(pass), nb = 1 << sel_bits(pass);
     for (int i = tid; i < kSelBins; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < I; i += NT) {
-      const uint32_t kk = keys[i];
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & uint32_t(nb - 1)], 1u);
-    }
+    uint32_t kv[16];              // all reads of the pass first, then the counts
+#pragma unroll
+    for (int u = 0; u < 16; ++u) kv[u] = tid + u * NT < I ? keys[tid + u * NT] : 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (tid + u * NT < I && (kv[u] & pmask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & uint32_t(nb - 1)], 1u);
     __syncthreads();
     {
       // thread t holds bins nb-1-per*t .. nb-per*(t+1) (highest first); a
@@ -136,22 +142,28 @@ __device__ __forceinline__ void select_channels(const SparseArgs& a, int t, int 
   }
   // prefix is now the c-th largest key; keep every larger key and the first
   // `remaining` equal ones in index order.  Thread tid owns a contiguous chunk.
-  const int ch = (I + NT - 1) / NT;
+  const int ch = (I + NT - 1) / NT;     // at most 16
   const int i0 = min(I, tid * ch), i1 = min(I, i0 + ch);
+  uint32_t kc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kc[j] = i0 + j < i1 ? keys[i0 + j] : 0u;
   int n_gt = 0, n_eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    n_gt += keys[i] > prefix;
-    n_eq += keys[i] == prefix;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    n_gt += i0 + j < i1 && kc[j] > prefix;
+    n_eq += i0 + j < i1 && kc[j] == prefix;
   }
   const int eq_base = wg_exclusive_scan(n_eq, misc + 4);
   const int take_eq = min(max(remaining - eq_base, 0), n_eq);
   int pos = wg_exclusive_scan(n_gt + take_eq, misc + 4);
   int eq_seen = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t kk = keys[i];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (i0 + j >= i1) break;
+    const uint32_t kk = kc[j];
     bool keep = kk > prefix;
     if (kk == prefix) keep = eq_seen++ < take_eq;
-    if (keep && pos < c) out[pos++] = i;      // exactly c are kept; the bound only guards the buffer
+    if (keep && pos < c) out[pos++] = i0 + j;      // exactly c are kept; the bound only guards the buffer
   }
 }
 
