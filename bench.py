@@ -328,8 +328,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported by this build "
-              f"(the layer runs on a single MI355X; see the design notes for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(the layer runs on a single MI355X; the design notes describe how it would shard)", file=sys.stderr)
         sys.exit(2)
 
     import torch
