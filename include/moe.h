@@ -27,7 +27,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
- *     every buffer; the library allocates no memory and keeps no state.
+ *     every buffer; the library allocates no device memory.  Its only state
+ *     is process-wide and does not carry data from one call to the next:
+ *     one-time kernel attributes set on first use, the last HIP error of
+ *     each thread (moe_last_hip_error) and the completion-tag counter of the
+ *     single-launch decode (MOE_PATH_DECODE_FUSED).
  *   - Every device pointer must be 16-byte aligned (MOE_ERR_ALIGN otherwise).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  No call synchronises or copies device data to the
@@ -65,7 +69,10 @@ enum {
                            at most 64 tokens; needs router_dtype == x_dtype and
                            top_k <= 16.  While `stream` is being captured into a
                            graph the call runs path 1 instead (a captured launch
-                           would replay the completion tags of the capture). */
+                           would replay the completion tags of the capture).
+                           Opt-in only: it measures slower than path 1, and a
+                           wait that gives up is reported through the status
+                           words of moe_forward_tables_t, not the return code. */
 };
 
 /* return codes */
@@ -164,7 +171,9 @@ int moe_dispatch_dims(const moe_shape_t* s, int32_t* tile_m /* host */,
 
 /* Router and dispatch only: logits, softmax, top-k, renormalisation, and the
  * expert-sorted order.  x [T,H] (x_dtype), router_w [E,H] (router_dtype),
- * router_b f32 [E] or NULL.  The expert weights and `path` are not used. */
+ * router_b f32 [E] or NULL.  The expert weights and `path` are not used.
+ * The workspace needs moe_route_workspace_size(s) bytes (any workspace sized
+ * for moe_forward also serves). */
 int moe_route(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
               const moe_route_out_t* out /* host struct of device pointers */,
               void* workspace, size_t ws_bytes, void* stream);
@@ -220,6 +229,42 @@ int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float
                                const void* w_gate, const void* w_up, const void* w_down_t,
                                const void* ws_gate, const void* ws_up, const void* ws_down,
                                void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Where moe_forward leaves the routing of its last pass inside its workspace,
+ * as byte offsets from the workspace start (host call, no GPU access).  After
+ * a moe_forward call with shape *s has completed on its stream, the workspace
+ * holds, for the tokens of the last pass ([T - tokens, T)), the arrays of
+ * moe_route_out_t in the expert-sorted order of the path the forward took:
+ * flat ids f = t * top_k + j count from the first token of that pass, and
+ * segments are padded to multiples of tile_m (256 on the prefill path, 1 on
+ * the decode paths, which pad nothing).  tile_expert is written only when
+ * n_tiles > 0 (prefill); its offset is 0 otherwise.  The offsets describe a
+ * layout; they stay valid until the next call that uses the workspace.
+ * Meant for callers that want the routing the forward used (expert load
+ * statistics) without a second routing call.
+ */
+typedef struct {
+  int32_t path;        /* MOE_PATH_DECODE, MOE_PATH_PREFILL or MOE_PATH_DECODE_FUSED */
+  int32_t tokens;      /* tokens of the last pass (T for prefill; decode passes take at most 64) */
+  int32_t tile_m;      /* padding multiple of the sorted order */
+  int32_t capacity;    /* entries of sorted_ids */
+  int32_t n_tiles;     /* entries of tile_expert (0: not written) */
+  size_t topk_ids, topk_w, counts, offsets, sorted_ids, tile_expert, inv, active;
+  /* MOE_PATH_DECODE_FUSED only (0 on the other paths): two uint64 words.  The
+   * single launch relies on its work-groups running at the same time; every
+   * wait between them is bounded (about a second; the environment variable
+   * MOE_FUSED_WAIT_ROUNDS, read on each call, sets the number of polling
+   * rounds).  After the call has completed on its stream the two words are
+   * equal exactly when some wait of the last pass gave up: `out` is then not
+   * valid (its affected elements hold NaN) although the call returned MOE_OK. */
+  size_t status;
+} moe_forward_tables_t;
+int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t /* host */);
+
+/* Bytes of workspace moe_route needs for shape *s (host call); at most
+ * moe_workspace_size(s). */
+int moe_route_workspace_size(const moe_shape_t* s, size_t* bytes /* host */);
 
 /* The hipError_t value behind the most recent MOE_ERR_HIP returned to the
  * calling thread (0 if there was none).  Host call. */

@@ -26,7 +26,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
             "moe_last_hip_error", "moe_strerror", "moe_resolve_path", "moe_sparse_workspace_size",
-            "moe_forward_channel_sparse")
+            "moe_forward_channel_sparse", "moe_forward_tables", "moe_route_workspace_size",
+            "moe_probe_read", "moe_probe_mfma_bf16")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -37,6 +38,12 @@ class moe_shape_t(ctypes.Structure):
 class moe_route_out_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_ids", "topk_w", "counts", "offsets", "sorted_ids", "tile_expert", "inv", "active")]
+
+
+class moe_forward_tables_t(ctypes.Structure):
+    _fields_ = ([(n, ctypes.c_int32) for n in ("path", "tokens", "tile_m", "capacity", "n_tiles")] +
+                [(n, ctypes.c_size_t) for n in ("topk_ids", "topk_w", "counts", "offsets", "sorted_ids",
+                                                "tile_expert", "inv", "active", "status")])
 
 
 class MoeError(RuntimeError):
@@ -78,6 +85,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_sparse_workspace_size.restype = ctypes.c_int
     lib.moe_forward_channel_sparse.argtypes = [P(moe_shape_t), i32] + [vp] * 12 + [sz, vp]
     lib.moe_forward_channel_sparse.restype = ctypes.c_int
+    lib.moe_forward_tables.argtypes = [P(moe_shape_t), P(moe_forward_tables_t)]
+    lib.moe_forward_tables.restype = ctypes.c_int
+    lib.moe_route_workspace_size.argtypes = [P(moe_shape_t), P(sz)]
+    lib.moe_route_workspace_size.restype = ctypes.c_int
+    lib.moe_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.moe_probe_read.restype = ctypes.c_int
+    lib.moe_probe_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
+    lib.moe_probe_mfma_bf16.restype = ctypes.c_int
     lib.moe_resolve_path.argtypes = [P(moe_shape_t)]
     lib.moe_resolve_path.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
@@ -168,6 +183,52 @@ def moe_workspace_size(shape: moe_shape_t) -> int:
     if rc:
         raise MoeError(rc, "moe_workspace_size")
     return n.value
+
+
+def moe_probe_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Measurement probe (include/moe_probe.h): read ``nbytes`` of ``buf`` once."""
+    rc = load_library().moe_probe_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_probe_read")
+
+
+def moe_probe_mfma_bf16(iters: int, sink, stream=None) -> float:
+    """Measurement probe: back-to-back bf16 MFMAs on every compute unit; returns the launch's flops."""
+    fl = ctypes.c_double(0.0)
+    rc = load_library().moe_probe_mfma_bf16(int(iters), _ptr(sink), ctypes.byref(fl), _stream(stream))
+    if rc:
+        raise MoeError(rc, "moe_probe_mfma_bf16")
+    return fl.value
+
+
+def moe_route_workspace_size(shape: moe_shape_t) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_route_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_route_workspace_size")
+    return n.value
+
+
+def moe_forward_tables(shape: moe_shape_t) -> dict:
+    """Where moe_forward leaves the routing of its last pass in the workspace:
+    path, tokens, tile_m, capacity, n_tiles and the byte offsets of the arrays."""
+    t = moe_forward_tables_t()
+    rc = load_library().moe_forward_tables(ctypes.byref(shape), ctypes.byref(t))
+    if rc:
+        raise MoeError(rc, "moe_forward_tables")
+    return {n: getattr(t, n) for n, _ in moe_forward_tables_t._fields_}
+
+
+def fused_status_ok(shape: moe_shape_t, workspace) -> bool:
+    """After a completed MOE_PATH_DECODE_FUSED call: True unless a wait gave up
+    (the two status words of moe_forward_tables_t are equal).  Reads 16 bytes
+    of the workspace back to the host; the caller synchronises first."""
+    import torch
+    o = moe_forward_tables(shape)["status"]
+    if moe_forward_tables(shape)["path"] != MOE_PATH_DECODE_FUSED:
+        raise ValueError("status words exist on the single-launch decode path only")
+    w = workspace[o:o + 16].view(torch.int64).cpu()
+    return int(w[0]) != int(w[1])
 
 
 def moe_dispatch_dims(shape: moe_shape_t):

@@ -10,6 +10,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstdint>
+#include <cstdlib>
 #include <random>
 
 #include "common.hpp"
@@ -126,6 +127,21 @@ unsigned long long next_epoch() {
   return ctr.fetch_add(1, std::memory_order_relaxed) + 1;
 }
 
+// Polling rounds before a wait of the single-launch decode gives up (each
+// round is one pass over up to 512 flags and a short sleep): about a second
+// of waiting.  MOE_FUSED_WAIT_ROUNDS overrides it, read on every call, so
+// that a test can force every wait to give up (0) and check that the failure
+// is reported while every work-group still exits.
+int fused_spin_rounds() {
+  const char* v = std::getenv("MOE_FUSED_WAIT_ROUNDS");
+  if (v && *v) {
+    char* end = nullptr;
+    const long r = std::strtol(v, &end, 10);
+    if (end && *end == '\0' && r >= 0 && r <= (1L << 30)) return int(r);
+  }
+  return 1 << 21;
+}
+
 // route_only: buffers for moe_route over all T tokens.
 Layout make_layout(const moe_shape_t* s, bool route_only) {
   Layout L{};
@@ -162,7 +178,7 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     if (L.path == MOE_PATH_DECODE_FUSED) {
       L.n_items = fused_plan(s, Tr).n_items;
       L.flags = take(size_t(L.n_items) * 8);
-      L.error = take(8);
+      L.error = take(16);          // status pair: this call's tag, the tag of the last call that gave up
     }
   }
   if (!route_only && L.path == MOE_PATH_PREFILL) {
@@ -251,6 +267,36 @@ int moe_workspace_size(const moe_shape_t* s, size_t* bytes) {
   return MOE_OK;
 }
 
+int moe_route_workspace_size(const moe_shape_t* s, size_t* bytes) {
+  if (!s || !bytes) return MOE_ERR_NULL;
+  if (int rc = check_shape(s)) return rc;
+  *bytes = make_layout(s, true).total;
+  return MOE_OK;
+}
+
+int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t) {
+  if (!s || !t) return MOE_ERR_NULL;
+  if (int rc = check_shape(s)) return rc;
+  const Layout L = make_layout(s, false);
+  const bool prefill = L.path == MOE_PATH_PREFILL;
+  const int last = s->T == 0 ? 0 : (prefill ? s->T : s->T - (s->T - 1) / kDecodeMaxT * kDecodeMaxT);
+  t->path = L.path;
+  t->tokens = last;
+  t->tile_m = prefill ? L.tile_m : 1;       // decode passes route with tile_m 1 (no padding)
+  t->capacity = prefill ? L.cap : last * s->top_k;
+  t->n_tiles = prefill ? L.n_tiles : 0;
+  t->topk_ids = L.topk_ids;
+  t->topk_w = L.topk_w;
+  t->counts = L.counts;
+  t->offsets = L.offsets;
+  t->sorted_ids = L.sorted_ids;
+  t->tile_expert = prefill ? L.tile_expert : 0;
+  t->inv = L.inv;
+  t->active = L.active;
+  t->status = L.path == MOE_PATH_DECODE_FUSED ? L.error : 0;
+  return MOE_OK;
+}
+
 int moe_dispatch_dims(const moe_shape_t* s, int32_t* tile_m, int32_t* capacity, int32_t* n_tiles) {
   int rc = check_shape(s);
   if (rc) return rc;
@@ -273,9 +319,7 @@ int moe_route(const moe_shape_t* s, const void* x, const void* router_w, const f
   for (const void* p : ptrs)
     if (misaligned(p)) return MOE_ERR_ALIGN;
   const Layout L = make_layout(s, true);
-  size_t need = 0;
-  moe_workspace_size(s, &need);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   moe::RouteBufs rb = route_bufs(ws, L);
   rb.topk_ids = out->topk_ids;
@@ -406,7 +450,9 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       f.d = d;
       f.epoch = next_epoch();
       f.flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
-      f.error = reinterpret_cast<unsigned long long*>(ws + L.error);
+      f.call_tag = reinterpret_cast<unsigned long long*>(ws + L.error);
+      f.error = f.call_tag + 1;
+      f.spin_rounds = fused_spin_rounds();
       if (int e = hip_status(moe::launch_decode_fused(f, s->w_dtype, s->x_dtype, st))) return e;
       sev.mark(st);
       continue;

@@ -337,7 +337,9 @@ struct FusedArgs {
   int gu_rt_routed, gu_rt_shared;   // gate/up row tiles per routed / shared slot
   unsigned long long epoch;
   unsigned long long* flags;        // [n_items]
-  unsigned long long* error;        // holds the epoch when a wait of this call gave up
+  unsigned long long* call_tag;     // status pair, word 0: the epoch of this call (stored by item 0)
+  unsigned long long* error;        // status pair, word 1: the epoch of the last call in which a wait gave up
+  int spin_rounds;                  // polling rounds before a wait gives up
 };
 
 // Budgeted channel-sparse routed experts (decode).

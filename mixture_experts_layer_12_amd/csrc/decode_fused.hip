@@ -31,9 +31,16 @@
 // items in increasing order, so the lowest unfinished item can always run.
 // Each item ends by storing the call's epoch into its flag after its own
 // device-scope stores have completed; waits poll flags with device-scope
-// loads and give up after a bounded time (the combine then writes NaN, so a
-// co-residency failure cannot pass as a result).  The same item functions
-// serve the multi-launch kernels with ordinary memory accesses.
+// loads and give up after a bounded number of rounds.  A wait that gives up
+// stores the epoch into the error tag before its item signals; an item whose
+// wait gave up, or that finds the error tag at this call's epoch after its
+// waits, skips its body (it would read routing tables or activations that
+// were never written in this call) and only signals.  Every item is an
+// ancestor of every combine item, so once any wait has given up the combine
+// writes NaN over the whole output, and the status pair in the workspace
+// (this call's tag, stored by item 0; the error tag) holds two equal words
+// after the call.  The same item functions serve the multi-launch kernels
+// with ordinary memory accesses.
 #include <algorithm>
 
 #include "decode_items.hpp"
@@ -45,13 +52,16 @@ constexpr int kFusedThreads = 256;
 
 // Every flag in [lo, hi) equal to the epoch.  Wave 0 polls, 8 flags per lane
 // per round from the first one it has not yet seen set (flags only move to
-// the epoch during a call), then the work-group continues.
-__device__ __forceinline__ void wait_items(const FusedArgs& f, int lo, int hi) {
-  if ((threadIdx.x >> 6) == 0 && lo < hi) {
+// the epoch during a call), for at most f.spin_rounds rounds.  Returns, the
+// same for every thread, whether the item may run: its waits completed and
+// no wait of this call has given up.
+__device__ __forceinline__ bool wait_items(const FusedArgs& f, int lo, int hi) {
+  __shared__ int s_run;
+  if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
     int cur = lo + lane;
-    bool done = false;
-    for (int it = 0; it < (1 << 21); ++it) {
+    bool done = lo >= hi;
+    for (int it = 0; !done && it < f.spin_rounds; ++it) {
       bool ok[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -67,9 +77,15 @@ __device__ __forceinline__ void wait_items(const FusedArgs& f, int lo, int hi) {
       __builtin_amdgcn_s_sleep(2);
     }
     if (!done && lane == 0) __hip_atomic_store(f.error, f.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // read after the flags: an item that gave up stored the tag before its flag
+    const bool failed = __hip_atomic_load(f.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.epoch;
+    if (lane == 0) s_run = (done && !failed) ? 1 : 0;
   }
   __syncthreads();
+  const bool run = s_run != 0;
+  __syncthreads();          // every wave has read s_run before a later wait rewrites it
   asm volatile("" ::: "memory");
+  return run;
 }
 
 // Item i is complete: this thread's stores have reached memory (vmcnt counts
@@ -94,6 +110,7 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
   auto* red_dn = reinterpret_cast<f32x4_t(*)[RPW * NCT][64]>(smem);
   const int nrt_down = a.H / (16 * RPW);
   for (int i = blockIdx.x; i < f.n_items; i += gridDim.x) {
+    if (i == 0 && threadIdx.x == 0) __hip_atomic_store(f.call_tag, f.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (i < f.n_logit) {      // one group of 4 chunks of one tile -> its partial plane
       const int tile = i >> 2, q = i & 3;
       logits_tile<XT, XT, true, 1>(f.r, tile % f.r.n_row_tiles, tile / f.r.n_row_tiles, 4 * q, 4,
@@ -102,8 +119,7 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
       const int j = i - f.n_logit;
       gateup_item<WT, XT, NCT, true>(a, j % f.gu_rt_shared, a.n_routed_slots + j / f.gu_rt_shared, red_gu);
     } else if (i < f.end_select) {
-      wait_items(f, 0, f.n_logit);
-      switch (topk_mode(a.E, a.k)) {
+      if (wait_items(f, 0, f.n_logit)) switch (topk_mode(a.E, a.k)) {
         case kTopkT8: select_and_dispatch<true, kTopkT8>(f.r, f.r.rb.logits, false, smem); break;
         case kTopkT16: select_and_dispatch<true, kTopkT16>(f.r, f.r.rb.logits, false, smem); break;
         case kTopkT32: select_and_dispatch<true, kTopkT32>(f.r, f.r.rb.logits, false, smem); break;
@@ -115,33 +131,35 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
       if (f.route_in_gu) {
         // the item selects and dispatches from the logits into LDS past the cross-wave sums; the
         // first one (slot 0, row tile 0) also publishes the routing tables for the down items
-        wait_items(f, 0, f.n_logit);
-        const SmallRoute R(smem + kFusedGuInts<NCT>, a.T, a.E, a.k);
-        int rk, fs;
-        small_select<false>(f.r, f.r.rb.logits, false, R);
-        small_place<true>(f.r, R, j == 0, rk, fs);
-        if (j == 0) small_tables<true>(f.r, R, rk, fs);
-        gateup_item<WT, XT, NCT, true, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu, 0, &R);
-      } else {
-        wait_items(f, f.end_shared_gu, f.end_select);
+        if (wait_items(f, 0, f.n_logit)) {
+          const SmallRoute R(smem + kFusedGuInts<NCT>, a.T, a.E, a.k);
+          int rk, fs;
+          small_select<false>(f.r, f.r.rb.logits, false, R);
+          small_place<true>(f.r, R, j == 0, rk, fs);
+          if (j == 0) small_tables<true>(f.r, R, rk, fs);
+          gateup_item<WT, XT, NCT, true, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu, 0, &R);
+        }
+      } else if (wait_items(f, f.end_shared_gu, f.end_select)) {
         gateup_item<WT, XT, NCT, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu);
       }
     } else if (i < f.end_down) {
       const int j = i - f.end_gu;
       const int slot = j / nrt_down, rt = j % nrt_down;
+      bool run;
       if (slot < a.n_routed_slots) {
         const int b = f.end_select + slot * f.gu_rt_routed;
-        if (f.route_in_gu) wait_items(f, f.end_select, f.end_select + 1);   // the routing tables
-        wait_items(f, b, b + f.gu_rt_routed);
+        // the routing tables (with route_in_gu, published by the first routed gate/up item)
+        const bool tables = f.route_in_gu ? wait_items(f, f.end_select, f.end_select + 1) : true;
+        run = wait_items(f, b, b + f.gu_rt_routed) && tables;
       } else {
         const int b = f.n_logit + (slot - a.n_routed_slots) * f.gu_rt_shared;
-        wait_items(f, b, b + f.gu_rt_shared);
+        run = wait_items(f, b, b + f.gu_rt_shared);
       }
-      down_item<WT, NCT, true, RPW>(a, rt, slot, red_dn);
+      if (run) down_item<WT, NCT, true, RPW>(a, rt, slot, red_dn);
     } else {
-      wait_items(f, f.end_gu, f.end_down);
+      const bool run = wait_items(f, f.end_gu, f.end_down);
       const long i4 = long(i - f.end_down) * kFusedThreads + threadIdx.x;
-      if (__hip_atomic_load(f.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == f.epoch) {
+      if (!run) {
         if (i4 < long(a.T) * (a.H / 4)) {
           const float nan = __builtin_nanf("");
           if constexpr (XT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = f32x4_t{nan, nan, nan, nan};

@@ -740,11 +740,11 @@ __device__ __forceinline__ void combine_item(const DecodeArgs a, long i4) {
 // routed slots and the S shared ones; each counts in once its device-scope
 // stores of the partials have completed, and the last to count in sums, for
 // every token, the k routed rows and the S shared rows in the order of
-// combine_item (same bits) and writes the outputs.  Ordinary loads read the
-// current rows: the writers stored them with device-scope stores, and each
-// 128-byte line of a row group is written by one work-group only, so no
-// cache on the reader's side can hold an older copy.  dn_count[rt] is zeroed
-// by the router launch of the same pass.
+// combine_item (same bits) and writes the outputs.  The rows are read with
+// device-scope loads: with 16-output row groups two groups share a 128-byte
+// line, and the last work-group of the neighbouring group may already have
+// pulled that line into this XCD's L2 before this group's writers finished.
+// dn_count[rt] is zeroed by the router launch of the same pass.
 template <int OT>
 __device__ __forceinline__ void down_combine(const DecodeArgs a, int rt, int slot, int rows) {
   __shared__ int last;
@@ -762,8 +762,8 @@ __device__ __forceinline__ void down_combine(const DecodeArgs a, int rt, int slo
   for (int i = tid; i < a.T * r4; i += blockDim.x) {
     const int t = i / r4, h = rt * rows + 4 * (i - t * r4);
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.k; ++j) v += ld_f32x4<false>(a.partials + size_t(a.inv[t * a.k + j]) * H + h);
-    for (int s = 0; s < a.S; ++s) v += ld_f32x4<false>(a.partials + size_t(a.T * a.k + s * a.T + t) * H + h);
+    for (int j = 0; j < a.k; ++j) v += ld_f32x4<true>(a.partials + size_t(a.inv[t * a.k + j]) * H + h);
+    for (int s = 0; s < a.S; ++s) v += ld_f32x4<true>(a.partials + size_t(a.T * a.k + s * a.T + t) * H + h);
     const long o = (long(t) * H + h) / 4;
     if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[o] = v;
     else reinterpret_cast<u32x2_t*>(a.out)[o] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};

@@ -102,9 +102,15 @@ def dispatch(ids, E, M):
 
 def sparse_ffn_one(x, Wg, Wu, Wd, scores, c):
     """Brute force: rank channels by score (higher first, equal scores by
-    lower index), keep the first c, and sum their contributions one by one."""
+    lower index, NaN below every number), keep the first c, and sum their
+    contributions one by one."""
     I = len(Wg)
-    ranked = sorted(range(I), key=lambda i: (-scores[i], i))[:c]
+
+    def rank_key(i):
+        v = scores[i]
+        return (1, 0.0, i) if math.isnan(v) else (0, -v, i)
+
+    ranked = sorted(range(I), key=rank_key)[:c]
     y = [0.0] * len(x)
     for i in ranked:
         g = _dot(Wg[i], x)

@@ -191,8 +191,16 @@ def dispatch(ids: np.ndarray, E: int, M: int) -> dict:
 # weights) is not part of this computation: scores are an input.
 
 def select_channels(scores: np.ndarray, c: int) -> np.ndarray:
-    """Indices of the c highest scores (ties to the lower index), ascending."""
-    order = np.argsort(-np.asarray(scores, dtype=np.float64), kind="stable")
+    """Indices of the c highest scores, ascending.
+
+    Ranking: a higher score first; equal scores go to the lower index; a NaN
+    score ranks below every number (-inf included), NaNs among themselves by
+    index.  The rule is stated as explicit sort keys rather than left to how
+    a sort happens to place NaN."""
+    s = np.asarray(scores, dtype=np.float64)
+    nan = np.isnan(s)
+    neg = np.where(nan, 0.0, -s)                     # placeholder for NaN: decided by the first key
+    order = np.lexsort((np.arange(s.size), neg, nan))   # keys: NaN last, then -score, then index
     return np.sort(order[:c])
 
 

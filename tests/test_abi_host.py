@@ -16,9 +16,13 @@ def m():
 
 
 def _declared(root):
-    text = open(os.path.join(root, "include", "moe.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(root, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(root, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(m, root):
@@ -154,3 +158,53 @@ def test_argument_errors_before_launch(m):
     s0 = m.make_shape(0, 256, 8, 128, 2)
     assert lib.moe_forward(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None, None,
                            0, None) == m.MOE_OK
+
+
+def _shape(m, **kw):
+    base = dict(T=8, H=256, E=8, I=128, top_k=2, n_shared=0, I_shared=0, x_dtype=1, w_dtype=1,
+                router_dtype=1, path=0)
+    base.update(kw)
+    return m.moe_shape_t(*[base[n] for n, _ in m.moe_shape_t._fields_])
+
+
+@pytest.mark.parametrize("kw, path, tokens, tile_m", [
+    (dict(T=8), 1, 8, 1),                    # one decode pass, no padding
+    (dict(T=70, w_dtype=2), 1, 6, 1),        # decode passes of 64: the last pass holds 6 tokens
+    (dict(T=64), 1, 64, 1),
+    (dict(T=300), 2, 300, 256),              # prefill, segments padded to 256 rows
+    (dict(T=8, path=3), 3, 8, 1),            # single-launch decode
+])
+def test_forward_tables_layout(m, kw, path, tokens, tile_m):
+    s = _shape(m, **kw)
+    t = m.moe_forward_tables(s)
+    assert (t["path"], t["tokens"], t["tile_m"]) == (path, tokens, tile_m)
+    k, E = s.top_k, s.E
+    n = tokens * k
+    if tile_m == 1:
+        assert t["capacity"] == n and t["n_tiles"] == 0 and t["tile_expert"] == 0
+    else:
+        assert t["capacity"] == -(-(n + E * (tile_m - 1)) // tile_m) * tile_m
+        assert t["n_tiles"] == t["capacity"] // tile_m
+    ws = m.moe_workspace_size(s)
+    spans = [(t["topk_ids"], 4 * n), (t["topk_w"], 4 * n), (t["counts"], 4 * E), (t["offsets"], 4 * (E + 1)),
+             (t["sorted_ids"], 4 * t["capacity"]), (t["inv"], 4 * n), (t["active"], 4 * (E + 1))]
+    if t["n_tiles"]:
+        spans.append((t["tile_expert"], 4 * t["n_tiles"]))
+    spans.sort()
+    for (o, b), (o2, _) in zip(spans, spans[1:]):
+        assert o % 16 == 0 and o + b <= o2              # aligned, disjoint
+    assert spans[-1][0] + spans[-1][1] <= ws
+
+
+def test_route_workspace_is_at_most_the_forward_workspace(m):
+    for kw in (dict(T=8), dict(T=4096, I=14336, H=4096), dict(T=1, E=256, top_k=8, w_dtype=2)):
+        s = _shape(m, **kw)
+        assert 0 < m.moe_route_workspace_size(s) <= m.moe_workspace_size(s)
+    # moe_route rejects a workspace below its own size before touching the GPU
+    s = _shape(m, T=8)
+    need = m.moe_route_workspace_size(s)
+    buf = (ctypes.c_int32 * 16)()
+    out = m.moe_route_out_t(ctypes.addressof(buf), ctypes.addressof(buf), None, None, None, None, None, None)
+    p = ctypes.addressof(buf)
+    assert m.load_library().moe_route(ctypes.byref(s), p, p, None, ctypes.byref(out), p, need - 1,
+                                      None) == m.MOE_ERR_WORKSPACE

@@ -66,9 +66,16 @@ SMALL = {
     "fp8_tails_t40": W("fp8_tails_t40", T=40, H=352, E=16, k=6, I=96, S=2, Is=160, w_dtype="fp8_e4m3"),
     "fp8_f32x_t3": W("fp8_f32x_t3", T=3, H=96, E=5, k=2, I=64, x_dtype="f32", w_dtype="fp8_e4m3",
                      r_dtype="f32"),
+    # prefill down GEMM with its k range split in two (K = 2048) and in four (K = 4096): the
+    # shared expert's own K is cut into four ranges too, which leaves two of them empty (96 =
+    # 64 + 32, the second half-full) or ragged with a half-full last stage (2080 = 576 + 576 +
+    # 576 + 352)
+    "prefill_ksplit2": W("prefill_ksplit2", T=300, H=256, E=4, k=2, I=2048, zipf_s=1.2),
+    "prefill_ksplit4_shared": W("prefill_ksplit4_shared", T=290, H=256, E=4, k=2, I=4096, S=1, Is=96),
+    "prefill_ksplit4_ragged": W("prefill_ksplit4_ragged", T=333, H=224, E=5, k=2, I=4096, S=1, Is=2080),
 }
 BF16_BOTH_PATHS = ["mixtral_small_bf16", "deepseek_small_t8", "deepseek_small_t40", "prefill_small_zipf",
-                   "k_equals_E", "t1_k1"]
+                   "k_equals_E", "t1_k1", "prefill_ksplit2", "prefill_ksplit4_shared", "prefill_ksplit4_ragged"]
 
 
 @pytest.fixture(scope="module")
@@ -218,6 +225,62 @@ def test_route_bit_exact(m, name):
     assert act[0] == len(d["active"]) and np.array_equal(act[1:1 + act[0]], d["active"])
 
 
+def _forward_tables(m, wl, t, path, ws):
+    """Run moe_forward and read the routing of its last pass from the workspace."""
+    import torch
+    shape = H.shape_of(m, wl, path)
+    H.run_forward(m, wl, t, path=path, ws=ws)
+    torch.cuda.synchronize()
+    L = m.moe_forward_tables(shape)
+    n = L["tokens"] * wl.k
+
+    def arr(key, count, dtype=torch.int32):
+        o = L[key]
+        return ws[o:o + 4 * count].view(dtype).cpu().numpy()
+    r = dict(topk_ids=arr("topk_ids", n).reshape(-1, wl.k), topk_w=arr("topk_w", n, torch.float32).reshape(-1, wl.k),
+             counts=arr("counts", wl.E), offsets=arr("offsets", wl.E + 1), sorted_ids=arr("sorted_ids", L["capacity"]),
+             inv=arr("inv", n), active=arr("active", wl.E + 1))
+    if L["n_tiles"]:
+        r["tile_expert"] = arr("tile_expert", L["n_tiles"])
+    return L, r
+
+
+# (case, path): decode with the routing in the gate/up prologue (few assignments), with a
+# separate selection launch, several passes (the tables hold the last one), the single
+# launch with and without a selection item, and prefill (256-row padding)
+TABLE_CASES = [("qwen_small_q4_t1", 1), ("e256_t1_k8", 1), ("deepseek_small_t8", 1), ("deepseek_small_t40", 1),
+               ("q4_bf16x_t70", 1), ("f32_t100_shared", 1), ("e40_k10", 1), ("deepseek_small_t8", 3),
+               ("deepseek_small_t40", 3), ("qwen_small_q4_t1", 3), ("prefill_small_zipf", 2),
+               ("prefill_ksplit4_ragged", 2), ("n10k_prefill", 2), ("k_equals_E", 2)]
+
+
+@pytest.mark.parametrize("name, path", TABLE_CASES)
+def test_forward_routing_tables_bit_exact(m, name, path):
+    """The dispatch arrays the forward itself used (decode: no padding, tile_m 1;
+    prefill: segments padded to 256 rows), compared element by element with the
+    oracle's dispatch of the same expert choice, and the choice with the oracle's."""
+    wl = SMALL[name]
+    inp = _inputs(wl, 11)
+    t = synth.to_torch(inp)
+    ws = m.alloc_workspace(H.shape_of(m, wl, path))
+    ws.fill_(0x7B)
+    L, r = _forward_tables(m, wl, t, path, ws)
+    assert L["path"] == path
+    T0 = wl.T - L["tokens"]
+    dec = oracle.decode_workload_inputs(inp, wl)
+    l, p, _, _ = oracle.route(dec["x"][T0:], dec["Wr"], dec["b"], wl.k)
+    H.check_ids(r["topk_ids"], l, wl.k)
+    w_ref = oracle.renormalize(p, r["topk_ids"].astype(np.int64))
+    assert np.allclose(r["topk_w"], w_ref, rtol=2e-6, atol=1e-7)
+    d = oracle.dispatch(r["topk_ids"].astype(np.int64), wl.E, L["tile_m"])
+    assert L["capacity"] == d["capacity"]
+    keys = ("counts", "offsets", "sorted_ids", "inv") + (("tile_expert",) if L["n_tiles"] else ())
+    for key in keys:
+        assert np.array_equal(r[key], d[key]), key
+    act = r["active"]
+    assert act[0] == len(d["active"]) and np.array_equal(act[1:1 + act[0]], d["active"])
+
+
 @pytest.mark.parametrize("T, E, k", [(1, 256, 8), (3, 64, 8), (4, 8, 2), (40, 16, 6), (5, 256, 70), (2, 100, 12)])
 def test_equal_logits_pick_lowest_indices(m, T, E, k):
     """All logits equal (zero router weights, no bias): every token takes experts
@@ -301,6 +364,34 @@ def test_full_size_route(m, full_inputs, name):
         assert np.array_equal(r[key], d[key]), key
 
 
+def _stratified_tokens(wl, r, rng):
+    """Tokens of a full-size call to check against the oracle: every token up to
+    64 of them; beyond that, for each expert the tokens of the first and last
+    rows of its segment in the 256-padded prefill order and of the rows on
+    either side of each 128-row half-tile boundary inside it, plus a few at
+    random."""
+    if wl.T <= 64:
+        return np.arange(wl.T)
+    ids = r["topk_ids"].astype(np.int64)
+    d = oracle.dispatch(ids, wl.E, 256)
+    n = wl.T * wl.k
+    pick = set()
+    for e in range(wl.E):
+        c = int(d["counts"][e])
+        if c == 0:
+            continue
+        o = int(d["offsets"][e])
+        rows = {0, c - 1}
+        for b in range(128, c + 128, 128):        # half-tile boundaries inside the segment
+            rows.update(q for q in (b - 1, b) if q < c)
+        for q in rows:
+            f = int(d["sorted_ids"][o + q])
+            assert f < n
+            pick.add(f // wl.k)
+    pick.update(int(v) for v in rng.choice(wl.T, size=6, replace=False))
+    return np.array(sorted(pick))
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_forward_sampled(m, full_inputs, name):
     import torch
@@ -312,14 +403,14 @@ def test_full_size_forward_sampled(m, full_inputs, name):
     got = H.to_f64(out)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(0)
-    tokens = np.arange(wl.T) if wl.T <= 8 else np.sort(rng.choice(wl.T, size=6, replace=False))
+    tokens = _stratified_tokens(wl, r, rng)
     ref, l, _ = H.oracle_tokens(wl, t, tokens)
     ids_gpu = r["topk_ids"][tokens]
     if (ids_gpu != oracle.select_topk(l, wl.k)).any():
         H.check_ids(ids_gpu, l, wl.k)
         ref, _, _ = H.oracle_tokens(wl, t, tokens, ids_gpu=ids_gpu.astype(np.int64))
     err = H.relerr(got[tokens], ref)
-    print(f"{name}: sampled tokens {tokens.tolist()} relerr {err:.3e}", flush=True)
+    print(f"{name}: {len(tokens)} sampled tokens relerr {err:.3e}", flush=True)
     assert err <= 1e-2, err
 
 
@@ -370,3 +461,38 @@ def test_graph_replay_matches_eager(m, name, path):
             o, e = H.to_f64(out), H.to_f64(eager)
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
             assert (np.abs(o - e) <= ulp).all(), r
+
+
+@pytest.mark.parametrize("name", ["deepseek_small_t8", "qwen_small_q4_t1", "e32_t40_passes"])
+def test_single_launch_decode_reports_a_wait_that_gives_up(m, name):
+    """The single-launch decode with its wait bound forced to 0 from the host:
+    every wait gives up at once, so every item that depends on another skips
+    its body and every work-group still exits.  The output must be all NaN
+    and the status words must report the failure; a normal call on the same
+    workspace afterwards reports success and equals the multi-launch decode."""
+    import os
+    import torch
+    wl = SMALL[name]
+    t = synth.to_torch(_inputs(wl, 12))
+    shape = H.shape_of(m, wl, 3)
+    ws = m.alloc_workspace(shape)
+    ws.fill_(0x3C)
+    old = os.environ.get("MOE_FUSED_WAIT_ROUNDS")
+    os.environ["MOE_FUSED_WAIT_ROUNDS"] = "0"
+    try:
+        out = H.run_forward(m, wl, t, path=3, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["MOE_FUSED_WAIT_ROUNDS"]
+        else:
+            os.environ["MOE_FUSED_WAIT_ROUNDS"] = old
+    last = H.to_f64(out)[wl.T - m.moe_forward_tables(shape)["tokens"]:]
+    assert np.isnan(last).all()
+    assert not m.fused_status_ok(shape, ws)
+    fused = H.run_forward(m, wl, t, path=3, ws=ws)
+    multi = H.run_forward(m, wl, t, path=1)
+    torch.cuda.synchronize()
+    assert m.fused_status_ok(shape, ws)
+    assert torch.equal(fused.view(torch.int16) if fused.dtype == torch.bfloat16 else fused,
+                       multi.view(torch.int16) if multi.dtype == torch.bfloat16 else multi)

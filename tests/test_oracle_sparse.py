@@ -27,6 +27,39 @@ def test_select_channels_hand_example():
     assert oracle.select_channels(np.zeros(6), 4).tolist() == [0, 1, 2, 3]
 
 
+def test_select_channels_nan_ranks_lowest():
+    """NaN ranks below every number, -inf included; NaNs among themselves and
+    equal numbers go to the lower index (hand-worked)."""
+    nan, inf = float("nan"), float("inf")
+    # the two numbers first (1 at index 1, 0 at index 3), then the NaN at the lower index
+    assert oracle.select_channels([nan, 1.0, nan, 0.0], 3).tolist() == [0, 1, 3]
+    assert oracle.select_channels([nan, 1.0, nan, 0.0], 2).tolist() == [1, 3]
+    assert oracle.select_channels([nan, 1.0, nan, 0.0], 4).tolist() == [0, 1, 2, 3]
+    # -inf is a number: it outranks every NaN
+    assert oracle.select_channels([nan, -inf], 1).tolist() == [1]
+    assert oracle.select_channels([-inf, nan, -inf], 2).tolist() == [0, 2]
+    assert oracle.select_channels([nan, nan, nan], 2).tolist() == [0, 1]
+    # +inf first, ties at +inf by index
+    assert oracle.select_channels([1.0, inf, nan, inf], 2).tolist() == [1, 3]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_channels_nan_matches_brute_force(seed):
+    """The masked FFN with NaN and repeated scores equals the brute force,
+    whose ranking spells the rule out per channel."""
+    rng = np.random.default_rng(40 + seed)
+    I, H = 11, 7
+    x = rng.normal(size=H)
+    Wg, Wu, Wd = rng.normal(size=(I, H)), rng.normal(size=(I, H)), rng.normal(size=(H, I))
+    scores = np.round(rng.normal(size=I), 1)
+    scores[rng.choice(I, size=4, replace=False)] = np.nan
+    scores[rng.choice(I, size=1)] = -np.inf
+    for c in (1, 5, 8, I):
+        want = loops.sparse_ffn_one(x.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist(), scores.tolist(), c)
+        got = oracle.masked_swiglu(x[None], Wg, Wu, Wd, oracle.select_channels(scores, c))[0]
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), c
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_full_budget_is_the_dense_layer(seed):
     rng = np.random.default_rng(seed)
