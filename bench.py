@@ -3,16 +3,32 @@
 
 One step = one whole layer call (router + dispatch, expert gate/up, expert
 down + weighted combine) through the C ABI on one batch of synthetic inputs
-already resident in HBM.  The default workload is the Mixtral-8x7B-shaped
-decode layer (T=8 tokens, hidden 4096, 8 experts, top-2, SwiGLU intermediate
-14336, bf16 weights).  Weight sets are rotated between steps so that every
+already resident in HBM.  Weight sets are rotated between steps so that every
 step streams its weights from HBM rather than from the 256 MB Infinity Cache.
 
-Prints ONE JSON line on stdout.  Besides the throughput it carries
+With no --workload the run covers the whole metric: the headline record is
+the Mixtral-8x7B-shaped decode layer at T=8 (hidden 4096, 8 experts, top-2,
+SwiGLU intermediate 14336, bf16 weights), and the same JSON line nests the
+records of the 256-expert Q4_0 decode at T=1 (top-8 + 1 shared expert), the
+DeepSeek-MoE-16B-shaped decode at T=8 and T=64, and the Mixtral-shaped
+4096-token prefill with Zipf routing.  --workload NAME times one workload.
+
+Prints ONE JSON line on stdout.  Each record carries
+  value, ms_per_step  tokens/s and time of exactly --steps timed steps;
+  spread        median / p10 / p90 of ms per step over 5 repetitions of the
+                timed loop;
   roofline      the dominant kernel's algorithmic bytes (or flops) per launch
                 divided by its average launch duration, measured with HIP
-                events recorded on the launch stream around that kernel;
-  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample.
+                events recorded on the launch stream around that kernel, with
+                frac against the published peak and frac_measured against
+                the probes below;
+  layer         the same for the whole layer: algorithmic bytes (or flops)
+                of one call over ms_per_step;
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample,
+                with all BLAS threads and with one.
+The headline line also carries `probes`: a cold streaming read of >= 1 GiB
+and the bandwidth-versus-bytes curve of one read kernel (including the
+Q4_0 layer's 18 MB), and back-to-back bf16 MFMAs on every compute unit.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -52,6 +68,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         evs = []
@@ -62,6 +79,11 @@ class HipEvents:
                 raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
             evs.append(e.value)
         return evs
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -147,11 +169,17 @@ def layer_flops(wl):
 
 
 def kernel_source_hash():
+    """Hash of everything that decides what the kernels do and how they are
+    launched: every source of the library (kernels, launch code, path and grid
+    choice in api.cpp) and the compiler flags."""
+    from mixture_experts_layer_12_amd import build as b
     h = hashlib.sha256()
-    for f in ("common.hpp", "decode_items.hpp", "router_items.hpp", "decode.hip", "decode_fused.hip", "prefill.hip",
-              "router.hip"):
-        with open(os.path.join(ROOT, "mixture_experts_layer_12_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "mixture_experts_layer_12_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    h.update(" ".join(b.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -170,14 +198,26 @@ def load_traffic(workload, kernel):
 
 # ------------------------------------------------------------- CPU oracle ----
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, t, tokens_max=16, min_seconds=5.0):
     """The fp64 oracle on a bounded sample of the same workload: the first
     min(T, tokens_max) tokens of weight copy 0, decoding from the stored bits
-    only the experts those tokens reach.  Repeated until min_seconds."""
+    only the experts those tokens reach.  Repeated for at least min_seconds
+    with every BLAS thread, then once with one thread."""
     import numpy as np
     import torch
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     n_tok = min(wl.T, tokens_max)
 
@@ -225,11 +265,15 @@ def cpu_baseline(wl, t, tokens_max=16, min_seconds=5.0):
         if el >= min_seconds or el > 0 and reps >= 50:
             break
     threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        once()
+        el1 = time.perf_counter() - t1
     return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_tok} of {wl.T} tokens of one layer call (weight copy 0), x{reps} repetitions, "
                       f"fp64 numpy oracle including decoding the stored weights of the experts those tokens reach; "
                       f"{el:.1f} s",
-            "host_cpus": os.cpu_count()}
+            "value_1_thread": n_tok / el1, "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 # ------------------------------------------------------- channel-sparse -----
@@ -306,50 +350,82 @@ def bench_sparse(args, m, wl, inp, copies, dev):
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
-# ------------------------------------------------------------------ main ----
+# ---------------------------------------------------------------- probes ----
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_decode_t8", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for ~10 GiB)")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
-    ap.add_argument("--path", default="auto", choices=["auto", "decode", "fused", "prefill"],
-                    help="execution path (auto: the library's choice for the shape)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
-    args = ap.parse_args()
+PROBE_SIZES_MB = [1, 2, 4, 8, 16, 18.04, 32, 64, 128, 256, 512, 1024, 4096]
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              f"(the layer runs on a single MI355X; the design notes describe how it would shard)", file=sys.stderr)
-        sys.exit(2)
 
+def run_probes(m, dev, hip):
+    """Measured peaks: a cold streaming read (median over distinct >= 1 GiB
+    regions), the bandwidth of one read kernel against the bytes it reads (each
+    size read at distinct offsets of an 8 GiB buffer, so every read is cold),
+    and bf16 MFMA throughput on register operands."""
     import torch
-    if args.calibrate_copy:
-        src = torch.ones(2 ** 29, dtype=torch.int16, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+    total = 8 * 2 ** 30
+    buf = torch.zeros(total, dtype=torch.uint8, device=dev)
+    sink = torch.empty(2 ** 20, dtype=torch.uint8, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    curve = []
+    off = 0
+    for mb in PROBE_SIZES_MB:
+        nbytes = int(mb * 1e6) // 4096 * 4096 if mb != int(mb) else int(mb) * 2 ** 20
+        reps = max(2, min(20, total // nbytes))
+        gbs = []
+        for r in range(reps):
+            if off + nbytes > total:
+                off = 0
+            evs = hip.create(2)
+            torch.cuda.synchronize()
+            hip.record(evs[0], sh)
+            m.moe_probe_read(buf.data_ptr() + off, nbytes, sink, stream=sh)
+            hip.record(evs[1], sh)
+            torch.cuda.synchronize()
+            ms = hip.elapsed_ms(evs[0], evs[1])
+            hip.destroy(evs)
+            gbs.append(nbytes / (ms * 1e-3) / 1e9)
+            off += nbytes
+        gbs.sort()
+        curve.append({"bytes": nbytes, "gbs_median": round(gbs[len(gbs) // 2], 1), "gbs_max": round(gbs[-1], 1),
+                      "reads": reps})
+        log(f"[probe] read {nbytes / 1e6:9.2f} MB: median {gbs[len(gbs) // 2]:7.1f} GB/s")
+    big = [c["gbs_median"] for c in curve if c["bytes"] >= 2 ** 30]
+    stream_peak = max(big)
+    del buf
+    # MFMA: about 5 ms per launch, best of 3
+    iters = 40000
+    best = 0.0
+    for _ in range(3):
+        evs = hip.create(2)
         torch.cuda.synchronize()
-        log("[bench] copied 1 GiB x5")
-        return
-    import mixture_experts_layer_12_amd as m
-    if not os.path.exists(m.LIB_PATH):
-        import __graft_entry__
-        __graft_entry__.build()
-    m.load_library()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
+        hip.record(evs[0], sh)
+        fl = m.moe_probe_mfma_bf16(iters, sink, stream=sh)
+        hip.record(evs[1], sh)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(evs[0], evs[1])
+        hip.destroy(evs)
+        best = max(best, fl / (ms * 1e-3) / 1e12)
+    log(f"[probe] cold streaming read {stream_peak:.1f} GB/s; bf16 MFMA {best:.1f} TFLOP/s")
+    torch.cuda.empty_cache()
+    return {"stream_read_gbs": stream_peak, "mfma_bf16_tflops": round(best, 1), "read_curve": curve,
+            "command": "bench.py probes: moe_probe_read / moe_probe_mfma_bf16 (include/moe_probe.h)"}
 
-    wl = synth.WORKLOADS[args.workload]
+
+def curve_at(probes, nbytes):
+    """Measured read bandwidth of one kernel reading about nbytes (nearest curve point)."""
+    if not probes:
+        return None
+    c = min(probes["read_curve"], key=lambda p: abs(math.log(p["bytes"] / nbytes)))
+    return c["gbs_median"]
+
+
+# --------------------------------------------------------------- measure ----
+
+def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
+    """One workload: its record (value, spread, roofline, layer, cpu_baseline)."""
+    import torch
     copies = args.copies or max(1, min(32, math.ceil(COLD_BYTES / layer_bytes(wl))))
     log(f"[bench] workload {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} S={wl.S} Is={wl.Is} "
         f"w={wl.w_dtype} x={wl.x_dtype}; {copies} weight copies of {layer_bytes(wl) / 1e9:.2f} GB")
@@ -393,12 +469,8 @@ def main():
     for i in range(max(args.warmup, 1)):
         step(i)
     torch.cuda.synchronize()
-    eager_elapsed = timed(step, args.steps, args.warmup)
-    eager_value = wl.T * args.steps / eager_elapsed
-    graph_value = None
-
     if not args.graph:
-        elapsed = eager_elapsed
+        fn = step
         timing = "eager launches"
     else:
         # one captured graph per weight copy, replayed in rotation: every replay
@@ -412,22 +484,30 @@ def main():
                      inp["w_down"][c], inp["ws_gate"][c], inp["ws_up"][c], inp["ws_down"][c], out, ws)
                 m.moe_forward(*a, stream=cap.cuda_stream)
             graphs.append(g)
-        replay = lambda i: graphs[i % copies].replay()
+        fn = lambda i: graphs[i % copies].replay()
         for i in range(args.warmup):
-            replay(i)
-        elapsed = timed(replay, args.steps, args.warmup)
-        graph_value = wl.T * args.steps / elapsed
+            fn(i)
         timing = "hipGraph replay, one graph per weight copy"
-    log(f"[bench] warmup {args.warmup}; timed {args.steps} steps ({timing})")
+    elapsed = timed(fn, args.steps, args.warmup)
     ms_per_step = elapsed * 1e3 / args.steps
     value = wl.T * args.steps / elapsed
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s (eager {eager_value:.1f} tokens/s)")
+    # spread: the same timed loop repeated
+    reps = [ms_per_step] + [timed(fn, args.steps, args.warmup + r * args.steps) * 1e3 / args.steps
+                            for r in range(1, args.reps)]
+    srt = sorted(reps)
+
+    def pct(q):
+        return srt[min(len(srt) - 1, max(0, int(round(q * (len(srt) - 1)))))]
+    spread = {"reps": len(reps), "median_ms": round(pct(0.5), 5), "p10_ms": round(pct(0.1), 5),
+              "p90_ms": round(pct(0.9), 5), "ms": [round(v, 5) for v in reps]}
+    log(f"[bench] {wl.name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} tokens/s ({timing}); "
+        f"reps median {spread['median_ms'] * 1e3:.1f} us, p10 {spread['p10_ms'] * 1e3:.1f}, "
+        f"p90 {spread['p90_ms'] * 1e3:.1f}")
 
     # stage timing with HIP events recorded on the launch stream
     prefill = path_name == "prefill"
     fused = path_name == "decode_fused"
     n_ev = 5 if prefill else (2 if fused else 4)
-    hip = HipEvents()
     evs = [hip.create(n_ev) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -436,64 +516,86 @@ def main():
     stage = [[hip.elapsed_ms(e[j], e[j + 1]) for j in range(n_ev - 1)] for e in evs]
     for e in evs:
         hip.destroy(e)
-    avg = [sum(s[j] for s in stage) / len(stage) for j in range(n_ev - 1)]
+    avg = [sum(s_[j] for s_ in stage) / len(stage) for j in range(n_ev - 1)]
     names = (["router", "prefill_gateup", "prefill_down", "cast"] if prefill
              else (["decode_fused"] if fused else ["router", "decode_gateup", "decode_down"]))
     log("[bench] stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, avg)))
 
     # engaged experts per weight copy (from the run's own routing)
     n_active = []
+    rws = torch.empty(m.moe_route_workspace_size(shape), dtype=torch.uint8, device=dev)
     for c in range(copies):
         r_out = dict(topk_ids=torch.empty(wl.T * wl.k, dtype=torch.int32, device=dev),
                      topk_w=torch.empty(wl.T * wl.k, dtype=torch.float32, device=dev),
                      active=torch.empty(wl.E + 1, dtype=torch.int32, device=dev))
-        m.moe_route(shape, inp["x"][c], inp["router_w"][c], inp["router_b"][c], r_out, ws, stream=sh)
+        m.moe_route(shape, inp["x"][c], inp["router_w"][c], inp["router_b"][c], r_out, rws, stream=sh)
         torch.cuda.synchronize()
         n_active.append(int(r_out["active"][0].item()))
     steps_copies = [(args.warmup + i) % copies for i in range(args.steps)]
     mean_active = sum(n_active[c] for c in steps_copies) / args.steps
+    stream_peak = probes["stream_read_gbs"] if probes else None
+    mfma_peak = probes["mfma_bf16_tflops"] if probes else None
 
+    def fmeas(a, peak):
+        return None if not peak else round(a / peak, 4)
+
+    stages = {n: round(v, 5) for n, v in zip(names, avg)}
     if prefill:
         kname = "prefill_gateup"
         fl = gateup_flops(wl)
         achieved = fl / (avg[1] * 1e-3) / 1e12
+        lay = layer_flops(wl) / (ms_per_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(wl.name, kname),
                 "kernel": kname, "launch_ms": round(avg[1], 5), "alg_flops_per_launch": fl,
-                "layer_tflops": round(layer_flops(wl) / (ms_per_step * 1e-3) / 1e12, 2)}
-    elif fused:
-        # one launch runs the whole layer: its algorithmic bytes over its duration
-        kname = "decode_fused"
-        lay = sum(layer_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
-        achieved = lay / (avg[0] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name, kname),
-                "kernel": kname, "launch_ms": round(avg[0], 5), "alg_bytes_per_launch": int(lay),
-                "mean_active_experts": round(mean_active, 3),
-                "layer_gbs": round(lay / (ms_per_step * 1e-3) / 1e9, 1)}
+                "frac_measured": fmeas(achieved, mfma_peak)}
+        down_fl = layer_flops(wl) - fl - 2.0 * wl.T * wl.H * wl.E
+        layer = {"bound": "mfma", "achieved": round(lay, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(lay / MFMA_BF16_PEAK_TFLOPS, 4), "frac_measured": fmeas(lay, mfma_peak),
+                 "alg_flops_per_call": layer_flops(wl), "stage_ms": stages,
+                 "down_tflops": round(down_fl / (avg[2] * 1e-3) / 1e12, 2)}
     else:
-        kname = "decode_gateup"
-        alg = sum(gateup_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
-        achieved = alg / (avg[1] * 1e-3) / 1e9
-        lay = sum(layer_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
-        dn = sum(down_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+        lay_b = sum(layer_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+        lay = lay_b / (ms_per_step * 1e-3) / 1e9
+        if fused:
+            kname = "decode_fused"
+            alg = lay_b
+            achieved = alg / (avg[0] * 1e-3) / 1e9
+            klaunch = avg[0]
+        else:
+            kname = "decode_gateup"
+            alg = sum(gateup_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+            achieved = alg / (avg[1] * 1e-3) / 1e9
+            klaunch = avg[1]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name, kname),
-                "kernel": kname, "launch_ms": round(avg[1], 5), "alg_bytes_per_launch": int(alg),
-                "mean_active_experts": round(mean_active, 3),
-                "down_kernel_gbs": round(dn / (avg[2] * 1e-3) / 1e9, 1),
-                "layer_gbs": round(lay / (ms_per_step * 1e-3) / 1e9, 1)}
+                "kernel": kname, "launch_ms": round(klaunch, 5), "alg_bytes_per_launch": int(alg),
+                "frac_measured": fmeas(achieved, stream_peak)}
+        layer = {"bound": "hbm", "achieved": round(lay, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(lay / HBM_PEAK_GBS, 4), "frac_measured": fmeas(lay, stream_peak),
+                 "alg_bytes_per_call": int(lay_b), "mean_active_experts": round(mean_active, 3),
+                 "stage_ms": stages}
+        at = curve_at(probes, lay_b)
+        if at:
+            layer["read_curve_gbs_at_layer_bytes"] = at
+            layer["frac_of_curve_at_layer_bytes"] = round(lay / at, 4)
+        if not fused:
+            dn = sum(down_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+            layer["down_gbs"] = round(dn / (avg[2] * 1e-3) / 1e9, 1)
     log(f"[bench] roofline: {roof}")
+    log(f"[bench] layer: {layer}")
 
     cpu = None
     if not args.no_cpu:
         t_cpu = {k: v[0] for k, v in inp.items()}
-        cpu = cpu_baseline(wl, t_cpu)
+        cpu = cpu_baseline(wl, t_cpu, min_seconds=cpu_seconds)
         log(f"[bench] cpu oracle: {cpu}")
+    del inp, ws, out
+    torch.cuda.empty_cache()
 
     # arithmetic type of the expert dot products (weights x activations)
     dtype = {"bf16": "bf16", "f32": "f32", "q4_0": "q4_0xf16", "q8_0": "q8_0xf16", "fp8_e4m3": "fp8e4m3xbf16"}[wl.w_dtype]
-    rec = {
+    return {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
@@ -501,9 +603,74 @@ def main():
                    "n_shared": wl.S, "I_shared": wl.Is, "weights": wl.w_dtype, "activations": wl.x_dtype,
                    "router": wl.r_dtype, "path": path_name, "weight_copies": copies,
                    "timing": timing, "parallelism": "single-gpu"},
+        "spread": spread,
         "roofline": roof,
+        "layer": layer,
         "cpu_baseline": cpu,
     }
+
+
+# ------------------------------------------------------------------ main ----
+
+# the workloads the metric names besides the headline: decode at batch one (the
+# 256-expert Q4_0 layer), decode at batch 8 and 64 of the DeepSeek-shaped layer,
+# and the 4096-token prefill
+NESTED = ["qwen_a3b_decode_q4", "deepseek16b_decode_t8", "deepseek16b_decode_t64", "mixtral_prefill_t4096"]
+HEADLINE = "mixtral_decode_t8"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed loop for the spread")
+    ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
+                    help="time this workload only (default: the headline with the metric's other workloads nested)")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for ~10 GiB)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-probes", action="store_true", help="skip the bandwidth and MFMA probes")
+    ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "fused", "prefill"],
+                    help="execution path (auto: the library's choice for the shape)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(the layer runs on a single MI355X; the design notes describe how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        src = torch.ones(2 ** 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB x5")
+        return
+    import mixture_experts_layer_12_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    hip = HipEvents()
+    single = args.workload is not None
+    probes = None if (args.no_probes or single) else run_probes(m, dev, hip)
+    rec = measure(args, m, synth.WORKLOADS[args.workload or HEADLINE], dev, hip, probes)
+    if not single:
+        rec["probes"] = probes
+        rec["workloads"] = []
+        for name in NESTED:
+            if args.path != "auto":
+                break
+            rec["workloads"].append(measure(args, m, synth.WORKLOADS[name], dev, hip, probes, cpu_seconds=3.0))
+    rec["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(rec), flush=True)
 
 
