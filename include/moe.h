@@ -83,7 +83,9 @@ enum {
   MOE_ERR_DTYPE = -3,      /* unsupported dtype or dtype/path combination */
   MOE_ERR_ALIGN = -4,      /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -5,  /* workspace smaller than moe_workspace_size() */
-  MOE_ERR_HIP = -6         /* a HIP launch failed (hipGetLastError) */
+  MOE_ERR_HIP = -6,        /* a HIP launch failed (hipGetLastError) */
+  MOE_ERR_TOO_LARGE = -7   /* moe_forward_noalloc: the shape needs more workspace than its
+                              static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES) */
 };
 
 /*
@@ -265,6 +267,27 @@ int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t /* host */)
 /* Bytes of workspace moe_route needs for shape *s (host call); at most
  * moe_workspace_size(s). */
 int moe_route_workspace_size(const moe_shape_t* s, size_t* bytes /* host */);
+
+/*
+ * moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, layouts, paths and results are those of
+ * moe_forward; the workspace is a static device array of the library
+ * (MOE_NOALLOC_SCRATCH_BYTES bytes, held by every GPU the library runs on
+ * from its first call there until the process ends).  Shapes whose
+ * moe_workspace_size exceeds it are rejected with MOE_ERR_TOO_LARGE before
+ * anything else happens.  The call allocates nothing.  All calls on one GPU
+ * share the array, which keeps the last call's contents: calls that overlap
+ * in time on one GPU (several streams or threads) race and must not be
+ * issued; calls ordered on one stream are fine.  The first call on a device
+ * looks the array's address up with that device current (HIP's current
+ * device must be the device of `stream`).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const void* ws_gate, const void* ws_up, const void* ws_down,
+                        void* out, void* stream);
 
 /* The hipError_t value behind the most recent MOE_ERR_HIP returned to the
  * calling thread (0 if there was none).  Host call. */

@@ -22,12 +22,14 @@ MOE_F32, MOE_BF16, MOE_Q4_0, MOE_Q8_0, MOE_FP8_E4M3 = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_DECODE_FUSED = 0, 1, 2, 3
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
+MOE_ERR_TOO_LARGE = -7
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
             "moe_last_hip_error", "moe_strerror", "moe_resolve_path", "moe_sparse_workspace_size",
             "moe_forward_channel_sparse", "moe_forward_tables", "moe_route_workspace_size",
-            "moe_probe_read", "moe_probe_mfma_bf16")
+            "moe_probe_read", "moe_probe_mfma_bf16", "moe_forward_noalloc")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_tables.restype = ctypes.c_int
     lib.moe_route_workspace_size.argtypes = [P(moe_shape_t), P(sz)]
     lib.moe_route_workspace_size.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_probe_read.argtypes = [vp, sz, vp, vp]
     lib.moe_probe_read.restype = ctypes.c_int
     lib.moe_probe_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
@@ -260,6 +264,17 @@ def moe_forward(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up, w_down,
                                     _ptr(ws_down), _ptr(out), _ptr(workspace), nb, _stream(stream))
     if check and rc:
         raise MoeError(rc, "moe_forward")
+    return rc
+
+
+def moe_forward_noalloc(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                        out, stream=None, check=True) -> int:
+    """moe_forward with the library's static device scratch as its workspace (allocates nothing)."""
+    rc = load_library().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(router_w), _ptr(router_b),
+                                            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up),
+                                            _ptr(ws_down), _ptr(out), _stream(stream))
+    if check and rc:
+        raise MoeError(rc, "moe_forward_noalloc")
     return rc
 
 

@@ -195,6 +195,13 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
 thread_local int g_last_hip_error = 0;
+}  // namespace
+
+namespace moe {
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace moe
+
+namespace {
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
@@ -247,6 +254,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failure";
+    case MOE_ERR_TOO_LARGE: return "shape needs more workspace than the static scratch of moe_forward_noalloc";
     default: return "unknown error code";
   }
 }
