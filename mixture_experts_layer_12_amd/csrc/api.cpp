@@ -27,7 +27,10 @@ hipError_t launch_sparse_route_select(const RouterArgs& ra, const SparseArgs& a,
 
 namespace {
 
-constexpr int kEpilogueMaxSlots = 16;   // decode: expert slots per output row group for the combine epilogue
+#ifndef MOE_EPILOGUE_MAX_SLOTS
+#define MOE_EPILOGUE_MAX_SLOTS 16
+#endif
+constexpr int kEpilogueMaxSlots = MOE_EPILOGUE_MAX_SLOTS;   // decode: expert slots per output row group for the combine epilogue
 constexpr long kRouteInGateUpMaxGroups = 1024;   // decode: gate/up grids that select in their own prologue
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
 constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
@@ -142,6 +145,25 @@ int fused_spin_rounds() {
   return 1 << 21;
 }
 
+// MFMA steps of the decode kernels along a reduction of length K (one step =
+// the K one 16-byte load per lane group covers), as n_steps in decode_items.hpp.
+int decode_steps(int w_dtype, int K) {
+  switch (w_dtype) {
+    case MOE_F32: return K / 16;
+    case MOE_BF16: return K / 32;
+    case MOE_FP8_E4M3: return (K + 63) / 64;
+    default: return (K / 32 + 3) / 4;     // Q4_0, Q8_0
+  }
+}
+
+// Down-projection shape of a multi-launch decode pass of Tc tokens.
+moe::DownShape pass_down_shape(const moe_shape_t* s, int Tc) {
+  const int S = s->n_shared, Is = S > 0 ? s->I_shared : 0;
+  const int n_slots = std::min(s->E, Tc * s->top_k) + S;
+  return moe::decode_down_shape(moe::decode_one_col_tile(Tc, s->top_k, s->E), s->H, n_slots,
+                                decode_steps(s->w_dtype, std::max(s->I, Is)));
+}
+
 // route_only: buffers for moe_route over all T tokens.
 Layout make_layout(const moe_shape_t* s, bool route_only) {
   Layout L{};
@@ -173,7 +195,13 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     // fp16 (Q4_0, Q8_0, fp8) | fp32 | bf16 hi + lo planes
     const size_t elem = (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16) ? 4 : 2;
     L.h = take(size_t(L.h_plane) * elem);
-    L.partials = take(size_t(rows) * H * 4);
+    // partial rows: one plane per k range of the down projection (the passes' largest count)
+    int planes = 1;
+    if (L.path == MOE_PATH_DECODE && T > 0) {
+      planes = pass_down_shape(s, Tr).ks;
+      if (T % kDecodeMaxT) planes = std::max(planes, pass_down_shape(s, T % kDecodeMaxT).ks);
+    }
+    L.partials = take(size_t(planes) * rows * H * 4);
     L.dn_count = take(size_t(roundup(H / 16, 4)) * 4);
     if (L.path == MOE_PATH_DECODE_FUSED) {
       L.n_items = fused_plan(s, Tr).n_items;
@@ -444,6 +472,15 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
     d.h_stride = L.h_stride;
     d.partials = reinterpret_cast<float*>(ws + L.partials);
+    d.part_plane = long(Tc * s->top_k + s->n_shared * Tc) * s->H;
+    if (fused) {                   // the single-launch items use one k range and their own row groups
+      d.dn_ksplit = 1;
+      d.dn_rpw = 1;
+    } else {
+      const moe::DownShape ds = pass_down_shape(s, Tc);
+      d.dn_ksplit = ds.ks;
+      d.dn_rpw = ds.rpw;
+    }
     d.out = oc;
     // combine in the down launch's epilogue when few work-groups write each output row group
     // (their arrival counts serialise on one counter per group); else in a launch of its own
@@ -597,6 +634,9 @@ int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float
     d.h_plane = long(Tc * s->top_k + s->n_shared * Tc) * L.h_stride;
     d.h_stride = L.h_stride;
     d.partials = reinterpret_cast<float*>(ws + L.partials);
+    d.part_plane = long(Tc * s->top_k + s->n_shared * Tc) * s->H;
+    d.dn_ksplit = 1;             // the shared experts' down writes one plane (read by the sparse combine)
+    d.dn_rpw = moe::decode_down_shape(Tc <= 16, s->H, s->n_shared, 0).rpw;
     d.n_row_tiles = (std::max(s->I, d.Is) + 15) / 16;
     d.out = static_cast<uint8_t*>(out) + size_t(t0) * s->H * xb;
     a.topk_ids = rb.topk_ids;

@@ -268,6 +268,45 @@ __host__ __device__ inline bool small_route(int T, int E, int k) {
   return T * k <= kSmallN && T * E <= 1024 && long(T) * E * E <= kRankWork;
 }
 
+// Multi-launch decode: one 16-token column tile per pass (NCT = 1) unless the
+// routed slots average more than 8 tokens (then 4 tiles, NCT = 4).
+__host__ __device__ inline bool decode_one_col_tile(int T, int k, int E) { return T <= 16 || T * k <= 8 * E; }
+
+// Multi-launch decode down projection: row tiles of 16 outputs per work-group
+// (rpw) and k ranges (ks) per output row group.  With one column tile a
+// work-group covers 4 row tiles while that still leaves >= 2048 work-groups,
+// else 2 (H % 32 == 0) or 1.  The reduction over the intermediate dimension
+// is then cut into 2 ranges, one work-group each, while the grid stays below
+// 4096 work-groups and each wave keeps at least 8 steps of its range: a
+// single round of large work-groups leaves the chip idle behind its slowest
+// CU (measured on the Mixtral-shaped batch of 8: one range 190 us, two 166,
+// four 171-179, eight 188-198).  `steps` is the number of MFMA steps along
+// the longest K.
+#ifndef MOE_DN_GRID_TARGET
+#define MOE_DN_GRID_TARGET 4096
+#endif
+#ifndef MOE_DN_MAX_KS
+#define MOE_DN_MAX_KS 2
+#endif
+#ifndef MOE_DN_RPW4_MIN_GRID
+#define MOE_DN_RPW4_MIN_GRID 2048
+#endif
+#ifndef MOE_DN_MIN_WAVE_STEPS
+#define MOE_DN_MIN_WAVE_STEPS 8
+#endif
+constexpr int kDownMaxKs = MOE_DN_MAX_KS;
+struct DownShape { int rpw, ks; };
+__host__ inline DownShape decode_down_shape(bool one_col_tile, int H, int n_slots, int steps) {
+  DownShape d{1, 1};
+  if (!one_col_tile) return d;
+  if (H % 64 == 0 && (H / 64) * n_slots >= MOE_DN_RPW4_MIN_GRID) d.rpw = 4;
+  else if (H % 32 == 0) d.rpw = 2;
+  const long grid = long(H / (16 * d.rpw)) * n_slots;
+  while (d.ks < kDownMaxKs && grid * d.ks * 2 <= MOE_DN_GRID_TARGET && steps / (4 * d.ks * 2) >= MOE_DN_MIN_WAVE_STEPS)
+    d.ks *= 2;
+  return d;
+}
+
 // ------------------------------------------------------ kernel arguments --
 
 // Routing state inside the workspace (or caller buffers for moe_route).
@@ -309,7 +348,10 @@ struct DecodeArgs {
   void* h;              // activations between the two launches
   long h_plane;         // elements per plane (bf16 hi/lo planes)
   int h_stride;         // elements per h row
-  float* partials;      // down: [T*k + S*T][H] weighted expert output rows
+  float* partials;      // down: [dn_ksplit][T*k + S*T][H] weighted expert output rows, one plane per k range
+  long part_plane;      // floats per plane of partials
+  int dn_ksplit;        // down: ranges the reduction over I is cut into (1 or 2), one work-group each
+  int dn_rpw;           // down: row tiles of 16 outputs per work-group (1, 2 or 4; 1 with NCT 4)
   void* out;            // [T, H]
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
   int route_in_gu;      // 1: the routed gate/up work-groups select and dispatch from the logits themselves

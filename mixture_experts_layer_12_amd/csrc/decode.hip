@@ -47,36 +47,43 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
 
 // OT >= 0: with the combine epilogue, outputs of dtype OT (partials stored
 // with device-scope stores); OT < 0: partials only.
+// Work-group (x, slot): k range x / n_rt of row group x % n_rt.
 template <int WT, int NCT, int RPW, int OT, bool PASSES>
 __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][RPW * NCT][64];
   const int slot = grid_slot(a);
+  const int n_rt = a.H / (16 * RPW);
+  const int rt = blockIdx.x % n_rt, kr = blockIdx.x / n_rt;
   if constexpr (PASSES) {
-    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, slot, red, c0); c0 += 16 * NCT)
+    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, rt, slot, red, c0, kr, a.dn_ksplit);
+         c0 += 16 * NCT)
       __syncthreads();
   } else {
-    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, blockIdx.x, slot, red);
+    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, rt, slot, red, 0, kr, a.dn_ksplit);
   }
-  if constexpr (OT >= 0) down_combine<OT>(a, blockIdx.x, slot, RPW * 16);
+  if constexpr (OT >= 0) down_combine<OT>(a, rt, slot, RPW * 16);
 }
 
-// Row tiles of 16 outputs per down-projection work-group when the token
-// columns fit one MFMA tile (the tiles share every activation load): four
-// while that still leaves at least 2048 work-groups, else two (fewer
-// work-groups starve the memory stream).
-#ifndef MOE_DN_RPW
-#define MOE_DN_RPW 4
+// Row tiles per work-group and k ranges come with the arguments
+// (decode_down_shape, chosen by the host, which sizes the partial planes).
+// The launch also requests MOE_DN_LDS_PAD bytes of LDS it does not use:
+// with at most 16 KiB of its own that caps the kernel at 3 work-groups per
+// CU.  Fewer concurrent weight streams per CU read HBM faster here (the
+// Mixtral-shaped batch of 8: 4 per CU 179 us, 3 per CU 176, 2 per CU 171,
+// 1 per CU 200, before the other down settings above).
+#ifndef MOE_DN_LDS_PAD
+#define MOE_DN_LDS_PAD 36864
 #endif
 template <int WT, int NCT, int OT, bool PASSES>
 static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
-  constexpr int R = NCT == 1 ? MOE_DN_RPW : 1;
-  if (R >= 4 && a.H % 64 == 0 && (a.H / 64) * n_slots >= 2048)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, R, OT, PASSES>), dim3(a.H / 64, n_slots), dim3(256), 0, st, a);
-  else if (R >= 2 && a.H % 32 == 0)
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, (R >= 2 ? 2 : 1), OT, PASSES>), dim3(a.H / 32, n_slots), dim3(256),
-                       0, st, a);
+  const dim3 b(256);
+  const size_t pad = MOE_DN_LDS_PAD;
+  if (NCT == 1 && a.dn_rpw == 4)
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 4, OT, PASSES>), dim3(a.H / 64 * a.dn_ksplit, n_slots), b, pad, st, a);
+  else if (NCT == 1 && a.dn_rpw == 2)
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 2, OT, PASSES>), dim3(a.H / 32 * a.dn_ksplit, n_slots), b, pad, st, a);
   else
-    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT, PASSES>), dim3(a.H / 16, n_slots), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT, PASSES>), dim3(a.H / 16 * a.dn_ksplit, n_slots), b, pad, st, a);
 }
 
 template <int OT>
@@ -108,12 +115,12 @@ static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
 }
 
 // One 16-token column tile per pass unless the routed slots average more than
-// 8 tokens: the one-tile kernels keep more weight bytes in flight per wave,
-// and the rare slot with more tokens takes another pass.
+// 8 tokens (decode_one_col_tile): the one-tile kernels keep more weight bytes
+// in flight per wave, and the rare slot with more tokens takes another pass.
 template <int WT, int XT>
 static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
   if (a.T <= 16) launch_decode_t<WT, XT, 1, false>(a, n_gu_row_tiles, st, mark);
-  else if (a.T * a.k <= 8 * a.E) launch_decode_t<WT, XT, 1, true>(a, n_gu_row_tiles, st, mark);
+  else if (decode_one_col_tile(a.T, a.k, a.E)) launch_decode_t<WT, XT, 1, true>(a, n_gu_row_tiles, st, mark);
   else launch_decode_t<WT, XT, 4, false>(a, n_gu_row_tiles, st, mark);
 }
 
@@ -149,6 +156,9 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
   if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
+  if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
+      a.H % (16 * a.dn_rpw) != 0)
+    return hipErrorInvalidValue;
   if (wdt == DT_F32) {
     if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, n_gu_row_tiles, st, mark);
     else launch_decode_x<DT_F32, DT_BF16>(a, n_gu_row_tiles, st, mark);

@@ -306,7 +306,7 @@ __device__ __forceinline__ f32x4_t mma_ready(const AReady<F>& a, const XFrag<F, 
 #define MOE_GU_UNROLL_BF16 4
 #endif
 #ifndef MOE_DN_UNROLL_BF16
-#define MOE_DN_UNROLL_BF16 4
+#define MOE_DN_UNROLL_BF16 2
 #endif
 // bf16 and fp8 load one 16-byte word per matrix and step, the others more.
 template <int WT, int NCT>
@@ -607,8 +607,10 @@ struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 
 // One work-group: RPW x 16 hidden outputs (rows of the down projection) of
 // one expert slot, for the slot's token columns [c0, c0 + 16 * NCT) (returns
-// whether more follow, as gateup_item).  Its 4 waves split the
-// slot's intermediate dimension; partial sums meet in LDS.  A wave's RPW row
+// whether more follow, as gateup_item), over k range kr of ks: the steps of
+// the reduction over the slot's intermediate dimension are cut into ks equal
+// ranges, and this work-group's partial rows go to plane kr of `partials`.
+// Its 4 waves split the range; partial sums meet in LDS.  A wave's RPW row
 // tiles share each activation fragment it loads, which cuts the activation
 // loads per weight byte by RPW (they otherwise add a fifth of the weight
 // stream's load instructions).  The result rows are the routing-weighted
@@ -619,7 +621,7 @@ struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 // work-group of the same launch); COH implies it.
 template <int WT, int NCT, bool COH, int RPW = 1, bool CST = COH>
 __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64],
-                                          int c0 = 0) {
+                                          int c0 = 0, int kr = 0, int ks = 1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   const uint8_t* base = routed ? a.wd : a.sd;     // selects, as in gateup_item
@@ -659,7 +661,8 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
   }
   const int nct = (n_e - c0 + 15) >> 4;
   const int nsteps = n_steps<WT>(K);
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  const int kb = kr * nsteps / ks, ke = (kr + 1) * nsteps / ks;
+  const int s0 = kb + wave * (ke - kb) / 4, s1 = kb + (wave + 1) * (ke - kb) / 4;
   f32x4_t acc[RPW][NCT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -708,9 +711,19 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
       const int c = c0 + ct * 16 + (lane & 15);
       if (c >= n_e) continue;
       // lane holds rows 4*(lane/16) + 0..3 of row tile r for token column c
-      st_f32x4<COH || CST>(a.partials + size_t(hrow0 + c) * H + row0 + r * 16 + (lane >> 4) * 4, v * sd_rows[r]);
+      st_f32x4<COH || CST>(a.partials + size_t(kr) * a.part_plane + size_t(hrow0 + c) * H + row0 + r * 16 +
+                               (lane >> 4) * 4, v * sd_rows[r]);
     }
   return more;
+}
+
+// One output row of one expert slot: the sum of its k-range planes in order.
+template <bool COH>
+__device__ __forceinline__ f32x4_t partial_row(const DecodeArgs& a, size_t row, int h) {
+  const float* p = a.partials + row * a.H + h;
+  f32x4_t r = ld_f32x4<COH>(p);
+  for (int q = 1; q < a.dn_ksplit; ++q) r += ld_f32x4<COH>(p + size_t(q) * a.part_plane);
+  return r;
 }
 
 // out[t] = sum over j of the partial row of assignment t*k + j (found through
@@ -720,7 +733,6 @@ __device__ __forceinline__ void combine_item(const DecodeArgs a, long i4) {
   const int H4 = a.H / 4;
   if (i4 >= long(a.T) * H4) return;
   const int t = int(i4 / H4), h4 = int(i4 % H4);
-  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(a.partials);
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < a.k; j0 += 8) {     // the rows of 8 assignments located first, then added in order
     int row[8];
@@ -728,9 +740,9 @@ __device__ __forceinline__ void combine_item(const DecodeArgs a, long i4) {
     for (int u = 0; u < 8; ++u) row[u] = j0 + u < a.k ? ld_i32<COH>(a.inv + t * a.k + j0 + u) : 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j0 + u < a.k) v += p[size_t(row[u]) * H4 + h4];
+      if (j0 + u < a.k) v += partial_row<false>(a, size_t(row[u]), 4 * h4);
   }
-  for (int s = 0; s < a.S; ++s) v += p[size_t(a.T * a.k + s * a.T + t) * H4 + h4];
+  for (int s = 0; s < a.S; ++s) v += partial_row<false>(a, size_t(a.T * a.k + s * a.T + t), 4 * h4);
   if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
   else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
 }
@@ -755,15 +767,15 @@ __device__ __forceinline__ void down_combine(const DecodeArgs a, int rt, int slo
   __syncthreads();
   if (tid == 0)
     last = __hip_atomic_fetch_add(a.dn_count + rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           unsigned(A + a.S - 1);
+           unsigned((A + a.S) * a.dn_ksplit - 1);
   __syncthreads();
   if (!last) return;
   const int H = a.H, r4 = rows / 4;
   for (int i = tid; i < a.T * r4; i += blockDim.x) {
     const int t = i / r4, h = rt * rows + 4 * (i - t * r4);
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.k; ++j) v += ld_f32x4<true>(a.partials + size_t(a.inv[t * a.k + j]) * H + h);
-    for (int s = 0; s < a.S; ++s) v += ld_f32x4<true>(a.partials + size_t(a.T * a.k + s * a.T + t) * H + h);
+    for (int j = 0; j < a.k; ++j) v += partial_row<true>(a, size_t(a.inv[t * a.k + j]), h);
+    for (int s = 0; s < a.S; ++s) v += partial_row<true>(a, size_t(a.T * a.k + s * a.T + t), h);
     const long o = (long(t) * H + h) / 4;
     if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[o] = v;
     else reinterpret_cast<u32x2_t*>(a.out)[o] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};

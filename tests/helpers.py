@@ -153,3 +153,21 @@ def oracle_tokens(wl, t, tokens, ids_gpu=None):
         Wd = expert_f64(t, "ws_down", wl, s, wl.S, wl.H, wl.Is)
         out += oracle.swiglu_ffn(x, Wg, Wu, Wd)
     return out, l, ids
+
+
+def same_up_to_rounding(a, b) -> bool:
+    """Two GPU outputs of the same layer that differ only in the order of their
+    fp32 sums.  bf16 outputs: each element within one bf16 ulp of the other
+    plus 1e-5 of the largest magnitude (an element near zero is a difference
+    of large fp32 terms, whose summation error is absolute, not relative to
+    the small result).  fp32 outputs: within a normwise 1e-5."""
+    import torch
+    o, e = to_f64(a), to_f64(b)
+    if a.dtype == torch.bfloat16:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
+        bad = np.abs(o - e) > ulp + 1e-5 * np.abs(e).max()
+        if bad.any():
+            i = np.unravel_index(np.argmax(np.abs(o - e) - ulp), e.shape)
+            print(f"same_up_to_rounding: {int(bad.sum())} elements differ, worst at {i}: {o[i]!r} vs {e[i]!r}")
+        return not bad.any()
+    return relerr(o, e) <= 1e-5

@@ -110,14 +110,17 @@ def test_resolve_path(m):
 
 def test_single_launch_decode_workspace(m):
     """The single-launch decode adds completion flags to the decode workspace;
-    the multi-launch decode of the same shape needs less."""
+    the multi-launch decode of the same shape cuts its down projection into 2
+    k ranges instead and holds one more plane of partial rows."""
     fused = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE_FUSED))
     multi = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE))
+    plane = 16 * 4096 * 4              # T*k = 16 partial rows of H = 4096 floats
 
     # work list: 4 logits planes, 1 selection, 8 x 896 gate/up tiles, 8 x 128 down row groups (32 outputs
     # each), 32 combine blocks
     n_items = 4 + 1 + 8 * 896 + 8 * 128 + 32
-    assert fused - multi >= n_items * 8
+    assert fused - (multi - plane) >= n_items * 8
+    assert fused - (multi - plane) < n_items * 8 + 4096
 
 
 def test_workspace_size_and_dims(m):

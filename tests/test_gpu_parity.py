@@ -73,6 +73,13 @@ SMALL = {
     "prefill_ksplit2": W("prefill_ksplit2", T=300, H=256, E=4, k=2, I=2048, zipf_s=1.2),
     "prefill_ksplit4_shared": W("prefill_ksplit4_shared", T=290, H=256, E=4, k=2, I=4096, S=1, Is=96),
     "prefill_ksplit4_ragged": W("prefill_ksplit4_ragged", T=333, H=224, E=5, k=2, I=4096, S=1, Is=2080),
+    # decode down projection with its reduction cut into two k ranges, summed in the down
+    # launch's combine epilogue; with a shared expert whose shorter K splits unevenly (35 steps),
+    # and with more than 16 slots (a combine launch of its own) and shared experts whose K of 3
+    # steps leaves one range a single step
+    "dn_ks2_t8": W("dn_ks2_t8", T=8, H=256, E=8, k=2, I=2048),
+    "dn_ks2_shared_t5": W("dn_ks2_shared_t5", T=5, H=256, E=8, k=2, I=4096, S=1, Is=1120),
+    "dn_ks2_wide_t8": W("dn_ks2_wide_t8", T=8, H=256, E=32, k=4, I=4096, S=2, Is=96),
 }
 BF16_BOTH_PATHS = ["mixtral_small_bf16", "deepseek_small_t8", "deepseek_small_t40", "prefill_small_zipf",
                    "k_equals_E", "t1_k1", "prefill_ksplit2", "prefill_ksplit4_shared", "prefill_ksplit4_ragged"]
@@ -141,11 +148,12 @@ def test_forward_multi_launch_decode(m, name):
 
 
 @pytest.mark.parametrize("name", sorted(n for n in SMALL if _fused_ok(SMALL[n])))
-def test_single_launch_decode_equals_multi_launch(m, name):
+def test_single_launch_decode_matches_multi_launch(m, name):
     """The single-launch decode runs the same work items in one resident-grid
     launch, with handoffs through device-scope stores and flags: its output
-    must be bit-identical to the multi-launch decode, and within the oracle's
-    tolerance."""
+    must be within the oracle's tolerance and equal to the multi-launch
+    decode up to the order of the fp32 sums (the multi-launch down
+    projection may cut its reduction into k ranges)."""
     import torch
     wl = SMALL[name]
     inp = _inputs(wl, 9)
@@ -153,8 +161,7 @@ def test_single_launch_decode_equals_multi_launch(m, name):
     multi = H.run_forward(m, wl, t, path=1)
     fused = H.run_forward(m, wl, t, path=3)
     torch.cuda.synchronize()
-    assert torch.equal(fused.view(torch.int16) if fused.dtype == torch.bfloat16 else fused,
-                       multi.view(torch.int16) if multi.dtype == torch.bfloat16 else multi)
+    assert H.same_up_to_rounding(fused, multi)
     _check_forward(m, wl, inp, path=3)
 
 
@@ -416,16 +423,16 @@ def test_full_size_forward_sampled(m, full_inputs, name):
 
 @pytest.mark.parametrize("name", [n for n in FULL if "decode" in n and _fused_ok(synth.WORKLOADS[n])])
 def test_full_size_decode_paths_agree(m, full_inputs, name):
-    """At the benchmarked sizes the single-launch and multi-launch decode give
-    the same bits."""
+    """At the benchmarked sizes the single-launch and multi-launch decode agree
+    up to the order of their fp32 sums (each is checked against the oracle on
+    its own by the sampled test)."""
     import torch
     wl = synth.WORKLOADS[name]
     t = full_inputs(name)
     multi = H.run_forward(m, wl, t, path=1)
     fused = H.run_forward(m, wl, t, path=3)
     torch.cuda.synchronize()
-    same = (fused.view(torch.int16) == multi.view(torch.int16)) if fused.dtype == torch.bfloat16 else (fused == multi)
-    assert bool(same.all()), int((~same).sum())
+    assert H.same_up_to_rounding(fused, multi)
 
 
 @pytest.mark.parametrize("name, path", [("deepseek_small_t40", 1), ("qwen_small_q4_t5", 0),
@@ -494,5 +501,4 @@ def test_single_launch_decode_reports_a_wait_that_gives_up(m, name):
     multi = H.run_forward(m, wl, t, path=1)
     torch.cuda.synchronize()
     assert m.fused_status_ok(shape, ws)
-    assert torch.equal(fused.view(torch.int16) if fused.dtype == torch.bfloat16 else fused,
-                       multi.view(torch.int16) if multi.dtype == torch.bfloat16 else multi)
+    assert H.same_up_to_rounding(fused, multi)
