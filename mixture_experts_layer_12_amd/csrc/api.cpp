@@ -17,7 +17,7 @@
 
 namespace moe {
 hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStream_t st, bool logits_only = false);
-hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
+hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark);
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
 hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t st);
@@ -517,11 +517,17 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     if (pro) {
       d.route_in_gu = 1;
       d.route = ra;
+      // the shared experts' gate/up runs in the logits launch (it needs no routing), which
+      // launch_decode makes itself
+      d.shared_in_router = d.S > 0 && ra.logit_parts == 4 ? 1 : 0;
     }
-    if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st, pro)))
-      return e;
-    sev.mark(st);
-    if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, n_gu_rt, st, events ? &sev : nullptr)))
+    if (!d.shared_in_router) {
+      if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st, pro)))
+        return e;
+      sev.mark(st);
+    }
+    if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, s->router_dtype, n_gu_rt, st,
+                                              events ? &sev : nullptr)))
       return e;
   }
   return MOE_OK;

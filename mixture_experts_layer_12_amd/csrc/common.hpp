@@ -356,6 +356,8 @@ struct DecodeArgs {
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
   int route_in_gu;      // 1: the routed gate/up work-groups select and dispatch from the logits themselves
   RouterArgs route;     // ... with these arguments (logits in route.rb.logits)
+  int shared_in_router; // with route_in_gu: the decode launches start with one for the router logits and
+                        // the shared experts' gate/up together; the gate/up launch covers routed slots only
 };
 
 // Output rows per down item of the single-launch decode: two row tiles when

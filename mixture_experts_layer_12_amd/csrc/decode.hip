@@ -20,21 +20,39 @@ __device__ __forceinline__ int grid_slot(const DecodeArgs& a) {
 // PRO: a.route_in_gu; every routed work-group first selects and dispatches
 // from the logits in LDS (dynamic LDS of small_route_ints(256, ...) ints) and
 // takes its slot's routing from there; the one of slot 0, row tile 0 also
-// writes the routing tables for the down launch.  One pass.
-template <int WT, int XT, int NCT, bool PASSES, bool PRO>
+// writes the routing tables for the down launch.  One pass.  Here the routed
+// slots' rows of the grid come first: a grid slightly larger than the CU
+// count puts its last rows on CUs that already hold a work-group, and two
+// routing prologues sharing a CU take twice as long (the shared experts'
+// work-groups, which do not route, absorb that instead).
+// XS (with PRO, fp16-operand families): the activations [T, H] are staged
+// into LDS as fp16 past the routing region, their loads issued before the
+// routing's (they do not depend on it) and stored once the selection is done.
+template <int WT, int XT, int NCT, bool PASSES, bool PRO, bool XS = false>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
-  const int slot = grid_slot(a);
+  const int slot = PRO ? int(blockIdx.y) : grid_slot(a);
   if constexpr (PRO) {
     extern __shared__ __attribute__((aligned(16))) int lds[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + small_route_ints(256, a.route.T, a.route.E, a.route.k));
+    const int n8 = a.T * a.H / 8;
+    XStage<XT> xst;
+    if constexpr (XS) xst = stage_x_load<XT>(a.x, n8);
     if (slot < a.n_routed_slots) {
       const SmallRoute R(lds, a.route.T, a.route.E, a.route.k);
       const bool writer = blockIdx.x == 0 && slot == 0;
       int rk, fslot;
-      small_select<false>(a.route, a.route.rb.logits, false, R);
-      small_place<false>(a.route, R, writer, rk, fslot);
+      route_select_place<false>(a.route, a.route.rb.logits, false, R, writer, rk, fslot, [&] {
+        if constexpr (XS) stage_x_store<XT>(xst, n8, xs);
+      });
       if (writer) small_tables<false>(a.route, R, rk, fslot);
-      gateup_item<WT, XT, NCT, false, true>(a, blockIdx.x, slot, red, 0, &R);
+      gateup_item<WT, XT, NCT, false, true, XS>(a, blockIdx.x, slot, red, 0, &R, xs);
+      return;
+    }
+    if constexpr (XS) {
+      stage_x_store<XT>(xst, n8, xs);
+      __syncthreads();
+      gateup_item<WT, XT, NCT, false, false, XS>(a, blockIdx.x, slot, red, 0, nullptr, xs);
       return;
     }
   }
@@ -42,6 +60,43 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
     for (int c0 = 0; gateup_item<WT, XT, NCT, false>(a, blockIdx.x, slot, red, c0); c0 += 16 * NCT) __syncthreads();
   } else {
     gateup_item<WT, XT, NCT, false>(a, blockIdx.x, slot, red);
+  }
+}
+
+// Router logits and the shared experts' gate/up in one launch (route_in_gu
+// with shared experts): the shared rows do not depend on the routing, so
+// they stream while the logits are computed, and the routed gate/up launch
+// that follows needs one work-group per routed row tile only.  Work-groups
+// [0, 4 * tiles) compute the logits (four partial planes per 16 x 16 tile,
+// as router_logits_kernel), the rest one shared row tile each; the grid also
+// clears route.zero_f32.  XS: the shared work-groups stage the activations.
+template <int RT, int WT, int XT, bool XS>
+__global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a) {
+  __shared__ f32x4_t red[4][2][64];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  const RouterArgs& r = a.route;
+  if (r.zero_f32) {
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < r.zero_n / 4; i += long(gridDim.x) * blockDim.x)
+      reinterpret_cast<f32x4_t*>(r.zero_f32)[i] = z;
+  }
+  const int n_logit = 4 * r.n_row_tiles * r.n_col_tiles;
+  if (int(blockIdx.x) < n_logit) {
+    const int tile = blockIdx.x >> 2, q = blockIdx.x & 3;
+    logits_tile<RT, XT, false, 1>(r, tile % r.n_row_tiles, tile / r.n_row_tiles, 4 * q, 4,
+                                  reinterpret_cast<float*>(lds), r.rb.logits + size_t(q) * r.T * r.E);
+    return;
+  }
+  const int j = blockIdx.x - n_logit, gu_rt = (a.Is + 15) / 16;
+  const int slot = a.n_routed_slots + j / gu_rt, rt = j % gu_rt;
+  if constexpr (XS) {
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+    const int n8 = a.T * a.H / 8;
+    stage_x_store<XT>(stage_x_load<XT>(a.x, n8), n8, xs);
+    __syncthreads();
+    gateup_item<WT, XT, 1, false, false, true>(a, rt, slot, red, 0, nullptr, xs);
+  } else {
+    gateup_item<WT, XT, 1, false>(a, rt, slot, red);
   }
 }
 
@@ -95,12 +150,39 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 
 // With a.dn_count the combine runs in the down launch's epilogue; without,
 // in a launch of its own.
+template <int RT, int WT, int XT>
+static void launch_router_shared(const DecodeArgs& a, bool stage, hipStream_t st) {
+  const int grid = 4 * a.route.n_row_tiles * a.route.n_col_tiles + a.S * ((a.Is + 15) / 16);
+  const size_t logit_lds = size_t(4) * 64 * 4 * sizeof(float);
+  const size_t x_lds = size_t(a.T) * a.H * 2;
+  if constexpr (Fam<WT>::v == DT_Q4) {
+    if (stage) {
+      hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, true>), dim3(grid), dim3(256),
+                         logit_lds > x_lds ? logit_lds : x_lds, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false>), dim3(grid), dim3(256), logit_lds, st, a);
+}
+
 template <int WT, int XT, int NCT, bool PASSES>
-static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
-  dim3 g1(n_gu_row_tiles, a.n_routed_slots + a.S), b(256);
-  if (NCT == 1 && !PASSES && a.route_in_gu)
-    hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, 1, false, true>), g1, b,
-                       size_t(small_route_ints(256, a.T, a.E, a.k)) * 4, st, a);
+static void launch_decode_t(const DecodeArgs& a, int rdt, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
+  constexpr bool fp16_family = Fam<WT>::v == DT_Q4;
+  // activations staged in LDS: at most kStageX8 rounds of 8 values per thread
+  const bool stage = fp16_family && long(a.T) * a.H <= long(kStageX8) * 256 * 8;
+  const bool srouter = NCT == 1 && !PASSES && a.route_in_gu && a.shared_in_router;
+  if (srouter) {
+    if (rdt == DT_F32) launch_router_shared<DT_F32, WT, XT>(a, stage, st);
+    else launch_router_shared<DT_BF16, WT, XT>(a, stage, st);
+    if (mark) mark->mark(st);
+  }
+  dim3 g1(n_gu_row_tiles, a.n_routed_slots + (srouter ? 0 : a.S)), b(256);
+  const size_t route_lds = size_t(small_route_ints(256, a.T, a.E, a.k)) * 4;
+  if (NCT == 1 && !PASSES && a.route_in_gu && stage)
+    hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, 1, false, true, fp16_family>), g1, b,
+                       route_lds + size_t(a.T) * a.H * 2, st, a);
+  else if (NCT == 1 && !PASSES && a.route_in_gu)
+    hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, 1, false, true>), g1, b, route_lds, st, a);
   else
     hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, PASSES, false>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
@@ -118,10 +200,10 @@ static void launch_decode_t(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t
 // 8 tokens (decode_one_col_tile): the one-tile kernels keep more weight bytes
 // in flight per wave, and the rare slot with more tokens takes another pass.
 template <int WT, int XT>
-static void launch_decode_x(const DecodeArgs& a, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
-  if (a.T <= 16) launch_decode_t<WT, XT, 1, false>(a, n_gu_row_tiles, st, mark);
-  else if (decode_one_col_tile(a.T, a.k, a.E)) launch_decode_t<WT, XT, 1, true>(a, n_gu_row_tiles, st, mark);
-  else launch_decode_t<WT, XT, 4, false>(a, n_gu_row_tiles, st, mark);
+static void launch_decode_x(const DecodeArgs& a, int rdt, int n_gu_row_tiles, hipStream_t st, StageMarker* mark) {
+  if (a.T <= 16) launch_decode_t<WT, XT, 1, false>(a, rdt, n_gu_row_tiles, st, mark);
+  else if (decode_one_col_tile(a.T, a.k, a.E)) launch_decode_t<WT, XT, 1, true>(a, rdt, n_gu_row_tiles, st, mark);
+  else launch_decode_t<WT, XT, 4, false>(a, rdt, n_gu_row_tiles, st, mark);
 }
 
 // Gate/up and down of the shared experts only (a.n_routed_slots must be 0):
@@ -153,27 +235,28 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int n_gu_row_tiles, hipStream_t st,
+hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
   if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
+  if (a.shared_in_router && (!a.route_in_gu || a.S == 0 || a.route.logit_parts != 4)) return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
     return hipErrorInvalidValue;
   if (wdt == DT_F32) {
-    if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, n_gu_row_tiles, st, mark);
-    else launch_decode_x<DT_F32, DT_BF16>(a, n_gu_row_tiles, st, mark);
+    if (xdt == DT_F32) launch_decode_x<DT_F32, DT_F32>(a, rdt, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_F32, DT_BF16>(a, rdt, n_gu_row_tiles, st, mark);
   } else if (wdt == DT_BF16) {
-    if (xdt == DT_F32) launch_decode_x<DT_BF16, DT_F32>(a, n_gu_row_tiles, st, mark);
-    else launch_decode_x<DT_BF16, DT_BF16>(a, n_gu_row_tiles, st, mark);
+    if (xdt == DT_F32) launch_decode_x<DT_BF16, DT_F32>(a, rdt, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_BF16, DT_BF16>(a, rdt, n_gu_row_tiles, st, mark);
   } else if (wdt == DT_Q4) {
-    if (xdt == DT_F32) launch_decode_x<DT_Q4, DT_F32>(a, n_gu_row_tiles, st, mark);
-    else launch_decode_x<DT_Q4, DT_BF16>(a, n_gu_row_tiles, st, mark);
+    if (xdt == DT_F32) launch_decode_x<DT_Q4, DT_F32>(a, rdt, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_Q4, DT_BF16>(a, rdt, n_gu_row_tiles, st, mark);
   } else if (wdt == DT_Q8) {
-    if (xdt == DT_F32) launch_decode_x<DT_Q8, DT_F32>(a, n_gu_row_tiles, st, mark);
-    else launch_decode_x<DT_Q8, DT_BF16>(a, n_gu_row_tiles, st, mark);
+    if (xdt == DT_F32) launch_decode_x<DT_Q8, DT_F32>(a, rdt, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_Q8, DT_BF16>(a, rdt, n_gu_row_tiles, st, mark);
   } else if (wdt == DT_FP8) {
-    if (xdt == DT_F32) launch_decode_x<DT_FP8, DT_F32>(a, n_gu_row_tiles, st, mark);
-    else launch_decode_x<DT_FP8, DT_BF16>(a, n_gu_row_tiles, st, mark);
+    if (xdt == DT_F32) launch_decode_x<DT_FP8, DT_F32>(a, rdt, n_gu_row_tiles, st, mark);
+    else launch_decode_x<DT_FP8, DT_BF16>(a, rdt, n_gu_row_tiles, st, mark);
   } else {
     return hipErrorInvalidValue;
   }

@@ -134,8 +134,7 @@ __global__ void __launch_bounds__(kFusedThreads) decode_fused_kernel(FusedArgs f
         if (wait_items(f, 0, f.n_logit)) {
           const SmallRoute R(smem + kFusedGuInts<NCT>, a.T, a.E, a.k);
           int rk, fs;
-          small_select<false>(f.r, f.r.rb.logits, false, R);
-          small_place<true>(f.r, R, j == 0, rk, fs);
+          route_select_place<true>(f.r, f.r.rb.logits, false, R, j == 0, rk, fs, [] {});
           if (j == 0) small_tables<true>(f.r, R, rk, fs);
           gateup_item<WT, XT, NCT, true, true>(a, j % f.gu_rt_routed, j / f.gu_rt_routed, red_gu, 0, &R);
         }

@@ -373,6 +373,70 @@ __device__ __forceinline__ void stream_steps(int s0, int s1, Load load, Body bod
 template <int WT, int XT, int NCT>
 struct GUStep { AFrag<WT> g, u; XRaw<Fam<WT>::v, XT> x[NCT]; };
 
+// Activations staged once per work-group as fp16 rows [T, K] in LDS, for the
+// fp16-operand families (Q4_0, Q8_0) of small latency-bound batches: the
+// weight loads of a step then need no activation loads beside them, so a
+// wave can keep all of its steps' weight loads in flight at once.  The fp16
+// values are the ones cook_x forms (same rounding), so the results are the
+// same bits.  stage_x_load issues a thread's loads, stage_x_store converts
+// and stores them (8 values per thread and round; T * K / 8 <= kStageX8 *
+// blockDim.x).
+constexpr int kStageX8 = 4;
+template <int XT> struct XStage { u32x4_t t[kStageX8][XT == DT_F32 ? 2 : 1]; };
+
+template <int XT>
+__device__ __forceinline__ XStage<XT> stage_x_load(const void* x, int n8) {
+  XStage<XT> r;
+#pragma unroll
+  for (int q = 0; q < kStageX8; ++q) {
+    const int i = min(int(threadIdx.x) + q * int(blockDim.x), n8 - 1);
+    if constexpr (XT == DT_F32) {
+      r.t[q][0] = ldg16(reinterpret_cast<const float*>(x) + size_t(i) * 8);
+      r.t[q][1] = ldg16(reinterpret_cast<const float*>(x) + size_t(i) * 8 + 4);
+    } else {
+      r.t[q][0] = ldg16(reinterpret_cast<const uint16_t*>(x) + size_t(i) * 8);
+    }
+  }
+  return r;
+}
+
+template <int XT>
+__device__ __forceinline__ void stage_x_store(const XStage<XT>& r, int n8, uint16_t* xs) {
+#pragma unroll
+  for (int q = 0; q < kStageX8; ++q) {
+    const int i = int(threadIdx.x) + q * int(blockDim.x);
+    if (i >= n8) continue;
+    u32x4_t v;
+    if constexpr (XT == DT_F32) {
+      const u32x4_t t0 = r.t[q][0], t1 = r.t[q][1];
+      v = u32x4_t{pack_f16(__uint_as_float(t0[0]), __uint_as_float(t0[1])),
+                  pack_f16(__uint_as_float(t0[2]), __uint_as_float(t0[3])),
+                  pack_f16(__uint_as_float(t1[0]), __uint_as_float(t1[1])),
+                  pack_f16(__uint_as_float(t1[2]), __uint_as_float(t1[3]))};
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[m] = bf16x2_to_f16x2(r.t[q][0][m]);
+    }
+    *reinterpret_cast<u32x4_t*>(xs + size_t(i) * 8) = v;
+  }
+}
+
+// The fp16 B operand of one step read from the staged rows (Q4_0 family
+// layout, as load_x_raw + cook_x): zero past K or for an empty column.
+__device__ __forceinline__ XFrag<DT_Q4, DT_F32> lds_x_frag(const uint16_t* xrow, bool ok, int s, int g, int K) {
+  XFrag<DT_Q4, DT_F32> b;
+  const int nblk = K / 32;
+  const int blk = 4 * s + g;
+  ok = ok && blk < nblk;
+  const uint16_t* p = xrow + (ok ? blk : 0) * 32;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + f * 8);
+    b.v[f] = ok ? v : u32x4_t{0, 0, 0, 0};
+  }
+  return b;
+}
+
 
 // ------------------------------------------------------------- gate/up --
 
@@ -383,9 +447,14 @@ struct GUStep { AFrag<WT> g, u; XRaw<Fam<WT>::v, XT> x[NCT]; };
 // same value.
 // PRO: the routing of routed slots comes from the work-group's own selection
 // in LDS (`R`, tile_m 1) instead of the tables in memory.
-template <int WT, int XT, int NCT, bool COH, bool PRO = false>
+// XS: the activations come from fp16 rows staged in LDS at `xs` ([T, K],
+// Q4_0 / Q8_0 families, one column tile), and a wave issues the weight loads
+// of up to 4 steps at once.
+template <int WT, int XT, int NCT, bool COH, bool PRO = false, bool XS = false>
 __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[2 * NCT][64],
-                                            int c0 = 0, const SmallRoute* R = nullptr) {
+                                            int c0 = 0, const SmallRoute* R = nullptr,
+                                            const uint16_t* xs = nullptr) {
+  static_assert(!XS || (Fam<WT>::v == DT_Q4 && NCT == 1), "staged activations: fp16-operand families, one tile");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = slot < a.n_routed_slots;
   // the matrices of the slot's family: selects on a uniform flag (a branch per field lets the
@@ -440,7 +509,8 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
       if constexpr (PRO) tok = routed ? R->sorted[seg + c] / a.k : c;
       else tok = routed ? ld_i32<COH>(a.sorted_ids + seg + c) / a.k : c;
     }
-    xrow[ct] = reinterpret_cast<const uint8_t*>(a.x) + size_t(tok) * K * xb;
+    xrow[ct] = XS ? reinterpret_cast<const uint8_t*>(xs + size_t(tok) * K)
+                  : reinterpret_cast<const uint8_t*>(a.x) + size_t(tok) * K * xb;
   }
   const int nct = (n_e - c0 + 15) >> 4;
 
@@ -450,16 +520,18 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) accg[ct] = accu[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = Unroll<WT, NCT>::v;
+  constexpr int U = XS ? 4 : Unroll<WT, NCT>::v;
   auto load = [&](int s) {
     GUStep<WT, XT, NCT> st;
     st.g = load_a<WT>(rg, s, g, K);
     st.u = load_a<WT>(ru, s, g, K);
+    if constexpr (!XS) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      if (NCT == 1 || ct < nct) {
-        if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<F, XT>(xrow[ct], s, g, K);
-      }
+      for (int ct = 0; ct < NCT; ++ct)
+        if (NCT == 1 || ct < nct) {
+          if (!MOE_GU_MASKED_B || xok[ct]) st.x[ct] = load_x_raw<F, XT>(xrow[ct], s, g, K);
+        }
+    }
     return st;
   };
   auto body = [&](int s, const GUStep<WT, XT, NCT>& st) {
@@ -467,7 +539,14 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (NCT == 1 || ct < nct) {
-        const XFrag<F, XT> b = cook_x<F, XT>(st.x[ct], xok[ct], s, g, K);
+        XFrag<F, XT> b;
+        if constexpr (XS) {
+          const XFrag<DT_Q4, DT_F32> bl = lds_x_frag(reinterpret_cast<const uint16_t*>(xrow[ct]), xok[ct], s, g, K);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) b.v[f] = bl.v[f];
+        } else {
+          b = cook_x<F, XT>(st.x[ct], xok[ct], s, g, K);
+        }
         accg[ct] = mma_ready<F, XT>(ag, b, accg[ct]);
         accu[ct] = mma_ready<F, XT>(au, b, accu[ct]);
       }

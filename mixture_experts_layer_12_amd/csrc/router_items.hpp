@@ -640,22 +640,42 @@ __device__ __forceinline__ void small_select(const RouterArgs a, const float* l,
   if (E > 64)
     for (int p = tid; p < T * ((E + 63) >> 6) * k; p += NT) reinterpret_cast<uint64_t*>(R.part)[p] = 0ull;
   const size_t plane = size_t(T) * E;
+  const bool four = !l_in_lds && a.logit_parts != 1;
+  const bool with_bias = four && a.bias;
   for (int b = 0; b < T * E4; b += 4 * NT) {
-    float v[4];
+    int idx[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int p = min(b + u * NT + tid, T * E4 - 1);
-      const int i = p / E4, idx = i * E + min(p - i * E4, E - 1);
-      if (l_in_lds) {
-        v[u] = l[idx];
-      } else if (a.logit_parts == 1) {
-        v[u] = ld_f32<COH>(l + idx);
-      } else {
-        float acc = ld_f32<COH>(l + idx);
-        acc += ld_f32<COH>(l + plane + idx);
-        acc += ld_f32<COH>(l + 2 * plane + idx);
-        acc += ld_f32<COH>(l + 3 * plane + idx);
-        acc += a.bias ? a.bias[idx % E] : 0.f;
+      const int i = p / E4;
+      idx[u] = i * E + min(p - i * E4, E - 1);
+    }
+    // Every load of the batch is issued before the first sum (the branches
+    // only decide which loads exist), so the batch costs one round trip; the
+    // sums then follow the fixed order of the other readers of the planes.
+    float v[4], q1[4], q2[4], q3[4], bs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = l_in_lds ? l[idx[u]] : ld_f32<COH>(l + idx[u]);
+    if (four) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        q1[u] = ld_f32<COH>(l + plane + idx[u]);
+        q2[u] = ld_f32<COH>(l + 2 * plane + idx[u]);
+        q3[u] = ld_f32<COH>(l + 3 * plane + idx[u]);
+      }
+    }
+    if (with_bias) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bs[u] = a.bias[idx[u] % E];
+    }
+    if (four) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float acc = v[u];
+        acc += q1[u];
+        acc += q2[u];
+        acc += q3[u];
+        acc += with_bias ? bs[u] : 0.f;
         v[u] = acc;
       }
     }
@@ -857,12 +877,22 @@ __device__ __forceinline__ void small_tables(const RouterArgs a, const SmallRout
   }
 }
 
+// Phases 1-4 into R (small_select, then `between` -- work of the caller that
+// needs no routing, placed where it overlaps the selection's barriers --
+// then small_place, which ends with a barrier).
+template <bool COH, class F>
+__device__ __forceinline__ void route_select_place(const RouterArgs a, const float* l, bool l_in_lds, const SmallRoute& R,
+                                                   bool store, int& rk, int& slot, F between) {
+  small_select<COH>(a, l, l_in_lds, R);
+  between();
+  small_place<COH>(a, R, store, rk, slot);
+}
+
 template <bool COH>
 __device__ __forceinline__ void route_small(const RouterArgs a, const float* l, bool l_in_lds, int* lds) {
   const SmallRoute R(lds, a.T, a.E, a.k);
   int rk, slot;
-  small_select<COH>(a, l, l_in_lds, R);
-  small_place<COH>(a, R, true, rk, slot);
+  route_select_place<COH>(a, l, l_in_lds, R, true, rk, slot, [] {});
   small_tables<COH>(a, R, rk, slot);
 }
 
