@@ -141,6 +141,28 @@ static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
     hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 1, OT, PASSES>), dim3(a.H / 16 * a.dn_ksplit, n_slots), b, pad, st, a);
 }
 
+// One token: a work-group per 16 output rows over every slot (down_one_item),
+// the activation rows staged in dynamic LDS.
+template <int WT, int OT>
+__global__ void __launch_bounds__(256) decode_down_one_kernel(DecodeArgs a) {
+  __shared__ f32x4_t red[4][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t hs[];
+  down_one_item<WT, OT>(a, blockIdx.x, hs, red);
+}
+
+// Whether the one-token down (decode_down_one_kernel) applies, and its LDS.
+template <int WT>
+static bool down_one_fits(const DecodeArgs& a, size_t& lds) {
+  if constexpr (WT == DT_FP8) {
+    return false;
+  } else {
+    if (a.T != 1 || a.H % 16 || (a.S > 0 && a.Is != a.I)) return false;
+    const int len = (n_steps<WT>(a.I) + 3) / 4;
+    lds = size_t(a.k + a.S) * a.h_stride * h_elem_bytes<WT>() * h_planes<WT>();
+    return (a.k + a.S) * len <= kDownOneLoads && lds <= 48 * 1024;
+  }
+}
+
 template <int OT>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   combine_item<OT, false>(a, long(blockIdx.x) * blockDim.x + threadIdx.x);
@@ -186,7 +208,16 @@ static void launch_decode_t(const DecodeArgs& a, int rdt, int n_gu_row_tiles, hi
   else
     hipLaunchKernelGGL((decode_gateup_kernel<WT, XT, NCT, PASSES, false>), g1, b, 0, st, a);
   if (mark) mark->mark(st);
-  if (a.dn_count) {
+  size_t one_lds = 0;
+  bool one = false;
+  if constexpr (NCT == 1 && !PASSES && WT != DT_FP8) {
+    if (down_one_fits<WT>(a, one_lds)) {
+      hipLaunchKernelGGL((decode_down_one_kernel<WT, XT>), dim3(a.H / 16), b, one_lds, st, a);
+      one = true;
+    }
+  }
+  if (one) {
+  } else if (a.dn_count) {
     launch_down<WT, NCT, XT, PASSES>(a, a.n_routed_slots + a.S, st);
   } else {
     launch_down<WT, NCT, -1, PASSES>(a, a.n_routed_slots + a.S, st);

@@ -805,6 +805,122 @@ __device__ __forceinline__ f32x4_t partial_row(const DecodeArgs& a, size_t row, 
   return r;
 }
 
+// ------------------------------------------------------ down, one token --
+// A batch of one token: its k routed experts are distinct, so its activation
+// rows are rows 0 .. k-1 (expert order) followed by the S shared rows, one
+// per slot.  One work-group covers 16 output rows for every slot and adds the
+// slots itself -- no partial rows, no arrival counter, no second round trip
+// for a combine.  The activation rows are staged into LDS (every plane of the
+// family's format); each wave issues the weight loads of all its (slot, step)
+// pairs at once (at most kDownOneLoads), then multiplies them into one
+// accumulator in slot order, and the waves are added in order (deterministic).
+// Needs every slot to share one K (no shared experts, or I_shared == I).
+constexpr int kDownOneLoads = 16;
+
+template <int WT> constexpr int h_elem_bytes() { return Fam<WT>::v == DT_F32 ? 4 : 2; }
+template <int WT> constexpr int h_planes() { return Fam<WT>::v == DT_BF16 ? 2 : 1; }
+
+// B fragment of step s from the staged activations (layout as load_h_raw's,
+// planes plane_bytes apart).
+template <int F>
+__device__ __forceinline__ HFrag<F> lds_h_frag(const uint8_t* hs, size_t plane_bytes, size_t row_off, int s, int g,
+                                               int K) {
+  HFrag<F> b;
+  if constexpr (F == DT_F32) {
+    const u32x4_t t = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(hs) + row_off + s * 16 + g * 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) b.v[m] = __uint_as_float(t[m]);
+  } else if constexpr (F == DT_BF16) {
+    const uint16_t* hp = reinterpret_cast<const uint16_t*>(hs) + row_off + s * 32 + g * 8;
+    b.hi = *reinterpret_cast<const u32x4_t*>(hp);
+    b.lo = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(hp) + plane_bytes);
+  } else {
+    static_assert(F == DT_Q4, "fp8 rows take per-slot scales");
+    const int nblk = K / 32;
+    int blk = 4 * s + g;
+    blk = blk < nblk ? blk : nblk - 1;
+    const uint16_t* hp = reinterpret_cast<const uint16_t*>(hs) + row_off + blk * 32;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) b.v[f] = *reinterpret_cast<const u32x4_t*>(hp + f * 8);
+  }
+  return b;
+}
+
+template <int WT, int OT>
+__device__ __forceinline__ void down_one_item(const DecodeArgs a, int rt, uint8_t* hs, f32x4_t (*red)[64]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  constexpr int F = Fam<WT>::v;
+  constexpr int EB = h_elem_bytes<WT>(), NP = h_planes<WT>();
+  const int K = a.I, H = a.H;
+  const int n_slots = a.k + a.S;
+  // every routed slot's expert and activation row, one per lane (a vector
+  // load each, in bounds for any slot count): slot j < k is the j-th active
+  // expert, whose row is its prefix count; slot k + s is the shared expert s,
+  // row k + s.  Lanes are read back with readlane (uniform slot index).
+  const int A = ld_i32<false>(a.active);
+  int el = ld_i32<false>(a.active + 1 + (lane < a.k ? lane : a.k - 1));
+  el = el < 0 ? 0 : (el >= a.E ? a.E - 1 : el);   // entries past A are stale
+  const int hl = ld_i32<false>(a.cprefix + el);
+  // this wave's steps of every slot, all loads in flight at once
+  const int nsteps = n_steps<WT>(K);
+  const int s0 = wave * nsteps / 4, len = (wave + 1) * nsteps / 4 - s0;
+  const int n_pairs = n_slots * len;
+  AFrag<WT> af[kDownOneLoads];
+#pragma unroll
+  for (int i = 0; i < kDownOneLoads; ++i) {
+    if (i < n_pairs) {
+      const int j = i / len, st = s0 + i % len;
+      const bool routed = j < a.k;
+      if (routed && j >= A) continue;
+      RowPtr<WT> rw;
+      rw.init(routed ? a.wd : a.sd, routed ? a.E : a.S, H, K, routed ? __builtin_amdgcn_readlane(el, j) : j - a.k,
+              rt * 16 + (lane & 15));
+      af[i] = load_a<WT>(rw, st, g, K);
+    }
+  }
+  // then stage every plane of rows [0, k + S) of the activations, four
+  // 16-byte chunks per thread in flight
+  const size_t plane_bytes = size_t(n_slots) * a.h_stride * EB;
+  const int n16 = int(plane_bytes / 16), tot16 = n16 * NP;
+  constexpr int kChunks = 4;
+  for (int base = 0; base < tot16; base += 256 * kChunks) {
+    u32x4_t v[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = base + c * 256 + tid, p = idx >= n16, i = idx - p * n16;
+      if (idx < tot16) v[c] = ldg16(reinterpret_cast<const uint8_t*>(a.h) + (size_t(p) * a.h_plane * EB + size_t(i) * 16));
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = base + c * 256 + tid;
+      if (idx < tot16) *reinterpret_cast<u32x4_t*>(hs + size_t(idx) * 16) = v[c];
+    }
+  }
+  __syncthreads();                               // staged activations visible
+  const bool hok = (lane & 15) == 0;             // the token is column 0
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kDownOneLoads; ++i) {
+    if (i < n_pairs) {
+      const int j = i / len, st = s0 + i % len;
+      if (j < a.k && j >= A) continue;
+      const int hrow = j < a.k ? __builtin_amdgcn_readlane(hl, j) : j;
+      const auto hr = lds_h_frag<F>(hs, plane_bytes, size_t(hrow) * a.h_stride, st, g, K);
+      acc = mma_h<F>(prep_a<WT>(af[i]), cook_h<F>(hr, hok, st, g, K), acc);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4_t v = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) v += red[w][lane];
+  if (!hok) return;
+  const long o = (long(rt) * 16 + g * 4) / 4;   // this lane's four outputs of the one token
+  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[o] = v;
+  else reinterpret_cast<u32x2_t*>(a.out)[o] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+
 // out[t] = sum over j of the partial row of assignment t*k + j (found through
 // inv), then the shared experts' rows, in that fixed order; 4 outputs per thread.
 template <int OT, bool COH>

@@ -80,6 +80,17 @@ SMALL = {
     "dn_ks2_t8": W("dn_ks2_t8", T=8, H=256, E=8, k=2, I=2048),
     "dn_ks2_shared_t5": W("dn_ks2_shared_t5", T=5, H=256, E=8, k=2, I=4096, S=1, Is=1120),
     "dn_ks2_wide_t8": W("dn_ks2_wide_t8", T=8, H=256, E=32, k=4, I=4096, S=2, Is=96),
+    # one token whose slots share one K: the down projection adds every slot of a row group in one
+    # work-group (Q4_0 and Q8_0 with a shared expert, bf16 with two steps per wave, fp32 with
+    # uneven steps per wave), and one with more (slot, step) pairs than a wave holds, which keeps
+    # the partial rows and the combine
+    "t1_one_q4_shared": W("t1_one_q4_shared", T=1, H=288, E=64, k=8, I=128, S=1, Is=128,
+                          x_dtype="f32", w_dtype="q4_0", r_dtype="f32"),
+    "t1_one_q8_shared": W("t1_one_q8_shared", T=1, H=160, E=32, k=6, I=160, S=2, Is=160, w_dtype="q8_0"),
+    "t1_one_bf16_2steps": W("t1_one_bf16_2steps", T=1, H=224, E=16, k=4, I=256, S=2, Is=256),
+    "t1_one_f32": W("t1_one_f32", T=1, H=96, E=6, k=2, I=96, S=1, Is=96,
+                    x_dtype="f32", w_dtype="f32", r_dtype="f32"),
+    "t1_pairs_over": W("t1_pairs_over", T=1, H=128, E=32, k=8, I=256, S=2, Is=256),
 }
 BF16_BOTH_PATHS = ["mixtral_small_bf16", "deepseek_small_t8", "deepseek_small_t40", "prefill_small_zipf",
                    "k_equals_E", "t1_k1", "prefill_ksplit2", "prefill_ksplit4_shared", "prefill_ksplit4_ragged"]
