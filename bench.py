@@ -615,6 +615,100 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
 # the workloads the metric names besides the headline: decode at batch one (the
 # 256-expert Q4_0 layer), decode at batch 8 and 64 of the DeepSeek-shaped layer,
 # and the 4096-token prefill
+def measure_cache(args, m, wl, dev, n_layers=4, calls=48):
+    """Costs of the host-resident expert cache on a decode layer shape.
+
+    n_layers layers of routed experts live in pinned host memory.  Router
+    biases fix each layer's experts: layer l engages experts (32 j + l) mod E,
+    so that the next layer's experts are this layer's plus one -- the
+    prefetch rule of the expert-cache page holds exactly.  Scenarios, each
+    timed over `calls` calls that cycle through the layers (wall clock; every
+    call waits for its routing anyway):
+      resident   moe_forward with the layer's experts on the device (no cache);
+      hit        every expert resident in the cache (slots >= all layers' experts);
+      miss       the cache flushed before every call: top_k copies per call;
+      no_prefetch  2 * top_k slots, no prefetch: each call's experts were
+                 evicted by the two layers before it, so all miss;
+      prefetch   2 * top_k slots, depth 1, shift 1: each call's experts were
+                 copied in during the previous call;
+      prefetch_random  as prefetch, but the routing of each call is the
+                 router's own (random) choice, so the prediction rarely holds.
+    """
+    import torch
+    E, k = wl.E, wl.k
+    shape = m.make_shape(wl.T, wl.H, wl.E, wl.I, k, wl.S, wl.Is, wl.x_dtype, wl.w_dtype, wl.r_dtype, 1)
+    inp = synth.make_inputs_torch(wl, args.seed, device=dev, copies=n_layers)
+    one = lambda key, l: inp[key][l] if isinstance(inp[key], list) else inp[key]  # noqa: E731
+    host = []
+    for l in range(n_layers):
+        stacks = []
+        for key in ("w_gate", "w_up", "w_down"):
+            src = one(key, l).contiguous().view(torch.uint8).reshape(-1)
+            h = torch.empty(src.numel(), dtype=torch.uint8, pin_memory=True)
+            h.copy_(src)
+            stacks.append(h)
+        host.append(tuple(stacks))
+    biases = []
+    for l in range(n_layers):
+        b = torch.zeros(E, dtype=torch.float32, device=dev)
+        b[[(32 * j + l) % E for j in range(k)]] = 30.0
+        biases.append(b)
+    xs = [torch.randn(wl.T, wl.H, generator=torch.Generator(device=dev).manual_seed(100 + c), device=dev)
+          .to(torch.float32 if wl.x_dtype == "f32" else torch.bfloat16) for c in range(calls)]
+    ws = m.alloc_workspace(shape, dev)
+    out = torch.empty_like(xs[0])
+    copy = torch.cuda.Stream()
+
+    def run(n_slots, depth, biased, flush=False, resident=False):
+        region = torch.empty(m.moe_cache_region_bytes(shape, n_slots), dtype=torch.uint8, device=dev)
+        c = m.moe_cache_create(shape, host, region, n_slots, depth, 1, copy)
+        try:
+            def call(i):
+                l = i % n_layers
+                b = biases[l] if biased else None
+                if resident:
+                    m.moe_forward(shape, xs[i], one("router_w", l), b, one("w_gate", l), one("w_up", l),
+                                  one("w_down", l), one("ws_gate", l), one("ws_up", l), one("ws_down", l), out, ws)
+                    return
+                if flush:
+                    m.moe_cache_flush(c)
+                m.moe_forward_cached(c, l, shape, xs[i], one("router_w", l), b, one("ws_gate", l), one("ws_up", l),
+                                     one("ws_down", l), out, ws)
+            for i in range(2 * n_layers):      # warm-up: fills the cache for the hit scenario
+                call(i)
+            torch.cuda.synchronize()
+            copy.synchronize()
+            m.moe_cache_stats(c, reset=True)
+            t0 = time.perf_counter()
+            for i in range(calls):
+                call(i)
+            torch.cuda.synchronize()
+            copy.synchronize()
+            dt = time.perf_counter() - t0
+            st = m.moe_cache_stats(c, reset=True)
+        finally:
+            torch.cuda.synchronize()
+            m.moe_cache_destroy(c)
+        r = {"us_per_call": round(dt / calls * 1e6, 2), "slots": n_slots, "prefetch_depth": depth}
+        if not resident:
+            r.update({kk: int(v) for kk, v in st.items()})
+            r["h2d_gbs"] = round(st["bytes_copied"] / dt / 1e9, 2) if st["bytes_copied"] else 0.0
+        return r
+
+    res = {"resident": run(2 * k, 0, True, resident=True),
+           "hit": run(n_layers * k, 0, True),
+           "miss": run(2 * k, 0, True, flush=True),
+           "no_prefetch": run(2 * k, 0, True),
+           "prefetch": run(2 * k, 1, True),
+           "prefetch_random": run(2 * k, 1, False)}
+    expert_bytes = 2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + mat_bytes(wl.w_dtype, wl.H, wl.I)
+    return {"metric": "expert-cache layer call latency", "unit": "us/call", "higher_is_better": False,
+            "n_gpus": 1, "data": "synthetic", "dtype": wl.w_dtype,
+            "config": {"workload": wl.name, "layers": n_layers, "calls": calls, "expert_bytes": expert_bytes,
+                       "T": wl.T, "E": E, "top_k": k, "routing": "router bias 30 on experts (32 j + layer) mod E"},
+            "scenarios": res, "kernel_source_hash": kernel_source_hash()}
+
+
 NESTED = ["qwen_a3b_decode_q4", "deepseek16b_decode_t8", "deepseek16b_decode_t64", "mixtral_prefill_t4096"]
 HEADLINE = "mixtral_decode_t8"
 
@@ -634,6 +728,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time hipGraph replays instead of eager launches")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "fused", "prefill"],
                     help="execution path (auto: the library's choice for the shape)")
+    ap.add_argument("--cache", action="store_true",
+                    help="instead: hit, miss and prefetch costs of the host-resident expert cache "
+                         "(workload qwen_a3b_decode_q4 unless --workload is given)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -659,6 +756,10 @@ def main():
     m.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.cache:
+        rec = measure_cache(args, m, synth.WORKLOADS[args.workload or "qwen_a3b_decode_q4"], dev)
+        print(json.dumps(rec), flush=True)
+        return
     hip = HipEvents()
     single = args.workload is not None
     probes = None if (args.no_probes or single) else run_probes(m, dev, hip)

@@ -84,8 +84,11 @@ enum {
   MOE_ERR_ALIGN = -4,      /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -5,  /* workspace smaller than moe_workspace_size() */
   MOE_ERR_HIP = -6,        /* a HIP launch failed (hipGetLastError) */
-  MOE_ERR_TOO_LARGE = -7   /* moe_forward_noalloc: the shape needs more workspace than its
-                              static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES) */
+  MOE_ERR_TOO_LARGE = -7,  /* moe_forward_noalloc: the shape needs more workspace than its
+                              static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES);
+                              moe_forward_cached: a pass can engage more experts than
+                              the cache has slots */
+  MOE_ERR_NOT_PINNED = -8  /* moe_cache_create: a host expert stack is not pinned host memory */
 };
 
 /*
@@ -288,6 +291,88 @@ int moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* router_
                         const void* w_gate, const void* w_up, const void* w_down,
                         const void* ws_gate, const void* ws_up, const void* ws_down,
                         void* out, void* stream);
+
+/*
+ * Host-resident routed experts with a GPU expert cache and predictive
+ * prefetching ("FATE: how to speed up MoE inference in llama.cpp with an
+ * expert cache and prefetching", ai-manual.ru, sections "How the expert cache
+ * works" and "Predictive prefetching: guessing the future").
+ *
+ * The routed experts of n_layers layers stay in pinned host memory (in the
+ * layouts above, one stack per matrix and layer).  A device region the caller
+ * allocates holds n_slots expert slots shared by all layers.  Each decode
+ * pass of moe_forward_cached routes on the GPU, reads the engaged experts back
+ * (the call waits for that), and looks each up in the cache: a hit uses the
+ * resident copy, a miss copies the expert into the least recently used slot
+ * that the pass does not need, on copy_stream.  The expert launches wait for
+ * those copies only.  Then, for each of the next prefetch_depth layers d
+ * (cyclically: after the last layer comes layer 0 of the next token), the
+ * experts (e + d * prefetch_shift) mod E of every engaged expert e are
+ * copied in ahead of time on copy_stream, overlapping with the compute of
+ * this layer and the routing of the next; the page's example predicts, from
+ * experts 3 and 7 in one layer, experts 4 and 8 in the next (shift 1).  A
+ * slot is overwritten only after every launch that reads it has finished.
+ *
+ * Results are those of moe_forward on the decode path (MOE_PATH_DECODE) with
+ * the same weights on the device: the same kernels read the same bytes.
+ * Shared experts and router weights stay device-resident and are passed per
+ * call.  A cache is used from one host thread and one compute stream at a
+ * time; calls through it synchronise that stream once per decode pass.  The
+ * library allocates no device memory; moe_cache_create allocates the host
+ * bookkeeping and HIP events, which moe_cache_destroy frees.
+ */
+typedef struct {
+  const void* w_gate;   /* (host, pinned) [E, I, H] in w_dtype's layout */
+  const void* w_up;     /* (host, pinned) [E, I, H] */
+  const void* w_down;   /* (host, pinned) [E, H, I] */
+} moe_host_experts_t;
+
+typedef struct {
+  uint64_t lookups;        /* engaged (pass, expert) pairs looked up */
+  uint64_t hits;           /* ... found resident (prefetched ones included) */
+  uint64_t misses;         /* ... copied in on demand */
+  uint64_t prefetches;     /* experts copied in ahead of time */
+  uint64_t prefetch_hits;  /* hits on a prefetched expert, its first use */
+  uint64_t bytes_copied;   /* host-to-device bytes enqueued (misses and prefetches) */
+} moe_cache_stats_t;
+
+typedef struct moe_expert_cache moe_expert_cache_t;
+
+/* Device bytes of a cache region of n_slots slots for the shape's routed
+ * experts (its T and path are ignored). Host call. */
+int moe_cache_region_bytes(const moe_shape_t* s, int32_t n_slots, size_t* bytes /* (host) */);
+
+/* Creates a cache over `layers` (host array of n_layers entries, each stack
+ * pinned: MOE_ERR_NOT_PINNED otherwise) in `region` (device, 256-byte
+ * aligned, at least moe_cache_region_bytes; it must outlive the cache).
+ * 1 <= n_slots <= 65536; 0 <= prefetch_depth < n_layers (0: no prefetch);
+ * prefetch_shift is any integer (taken mod E).  copy_stream: a hipStream_t
+ * of default priority, not the compute stream.  Nothing is copied yet.
+ * *out receives the handle (host). */
+int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_experts_t* layers,
+                     void* region, size_t region_bytes, int32_t n_slots, int32_t prefetch_depth,
+                     int32_t prefetch_shift, void* copy_stream, moe_expert_cache_t** out);
+
+/* Waits for the cache's copies, then frees its bookkeeping and events.  The
+ * caller must have synchronised every stream that ran moe_forward_cached. */
+int moe_cache_destroy(moe_expert_cache_t* c);
+
+/* Layer `layer`'s forward, as moe_forward with the routed experts read from
+ * the cache.  s must equal the shape given to moe_cache_create except for T
+ * and path (the call always takes the decode path); workspace as
+ * moe_workspace_size for s with path MOE_PATH_DECODE.  Each pass of at most
+ * 64 tokens needs n_slots >= min(E, tokens * top_k) (MOE_ERR_TOO_LARGE,
+ * checked before anything is enqueued).  Synchronises `stream` once per pass. */
+int moe_forward_cached(moe_expert_cache_t* c, int32_t layer, const moe_shape_t* s, const void* x,
+                       const void* router_w, const float* router_b,
+                       const void* ws_gate, const void* ws_up, const void* ws_down,
+                       void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Counters since creation or the last reset (reset != 0 zeroes them after the read). */
+int moe_cache_stats(moe_expert_cache_t* c, moe_cache_stats_t* out /* (host) */, int32_t reset);
+
+/* Forgets every resident expert (the next lookups miss); copies in flight still complete. */
+int moe_cache_flush(moe_expert_cache_t* c);
 
 /* The hipError_t value behind the most recent MOE_ERR_HIP returned to the
  * calling thread (0 if there was none).  Host call. */

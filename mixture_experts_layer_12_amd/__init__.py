@@ -23,13 +23,15 @@ MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL, MOE_PATH_DECODE_FUSED = 0, 1, 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 MOE_ERR_TOO_LARGE = -7
+MOE_ERR_NOT_PINNED = -8
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}
 EXPORTED = ("moe_workspace_size", "moe_dispatch_dims", "moe_route", "moe_forward", "moe_forward_profiled",
             "moe_last_hip_error", "moe_strerror", "moe_resolve_path", "moe_sparse_workspace_size",
             "moe_forward_channel_sparse", "moe_forward_tables", "moe_route_workspace_size",
-            "moe_probe_read", "moe_probe_mfma_bf16", "moe_forward_noalloc")
+            "moe_probe_read", "moe_probe_mfma_bf16", "moe_forward_noalloc", "moe_cache_region_bytes",
+            "moe_cache_create", "moe_cache_destroy", "moe_forward_cached", "moe_cache_stats", "moe_cache_flush")
 
 
 class moe_shape_t(ctypes.Structure):
@@ -46,6 +48,15 @@ class moe_forward_tables_t(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_int32) for n in ("path", "tokens", "tile_m", "capacity", "n_tiles")] +
                 [(n, ctypes.c_size_t) for n in ("topk_ids", "topk_w", "counts", "offsets", "sorted_ids",
                                                 "tile_expert", "inv", "active", "status")])
+
+
+class moe_host_experts_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down")]
+
+
+class moe_cache_stats_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "lookups", "hits", "misses", "prefetches", "prefetch_hits", "bytes_copied")]
 
 
 class MoeError(RuntimeError):
@@ -97,6 +108,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_probe_read.restype = ctypes.c_int
     lib.moe_probe_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
     lib.moe_probe_mfma_bf16.restype = ctypes.c_int
+    lib.moe_cache_region_bytes.argtypes = [P(moe_shape_t), i32, P(sz)]
+    lib.moe_cache_region_bytes.restype = ctypes.c_int
+    lib.moe_cache_create.argtypes = [P(moe_shape_t), i32, P(moe_host_experts_t), vp, sz, i32, i32, i32, vp,
+                                     P(vp)]
+    lib.moe_cache_create.restype = ctypes.c_int
+    lib.moe_cache_destroy.argtypes = [vp]
+    lib.moe_cache_destroy.restype = ctypes.c_int
+    lib.moe_forward_cached.argtypes = [vp, i32, P(moe_shape_t), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward_cached.restype = ctypes.c_int
+    lib.moe_cache_stats.argtypes = [vp, P(moe_cache_stats_t), i32]
+    lib.moe_cache_stats.restype = ctypes.c_int
+    lib.moe_cache_flush.argtypes = [vp]
+    lib.moe_cache_flush.restype = ctypes.c_int
     lib.moe_resolve_path.argtypes = [P(moe_shape_t)]
     lib.moe_resolve_path.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
@@ -290,6 +314,61 @@ def moe_forward_profiled(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up
     if check and rc:
         raise MoeError(rc, "moe_forward_profiled")
     return rc
+
+
+def moe_cache_region_bytes(shape: moe_shape_t, n_slots: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().moe_cache_region_bytes(ctypes.byref(shape), n_slots, ctypes.byref(n))
+    if rc:
+        raise MoeError(rc, "moe_cache_region_bytes")
+    return n.value
+
+
+def moe_cache_create(shape: moe_shape_t, layers, region, n_slots: int, prefetch_depth: int, prefetch_shift: int,
+                     copy_stream, region_bytes=None, check=True):
+    """``layers``: sequence of (w_gate, w_up, w_down) pinned host buffers per layer.  Returns the
+    handle (an int), or the error code when ``check`` is false and the call fails."""
+    arr = (moe_host_experts_t * len(layers))(*[moe_host_experts_t(_ptr(g), _ptr(u), _ptr(d)) for g, u, d in layers])
+    h = ctypes.c_void_p(None)
+    nb = _nbytes(region) if region_bytes is None else region_bytes
+    rc = load_library().moe_cache_create(ctypes.byref(shape), len(layers), arr, _ptr(region), nb, n_slots,
+                                         prefetch_depth, prefetch_shift, _stream(copy_stream), ctypes.byref(h))
+    if rc:
+        if check:
+            raise MoeError(rc, "moe_cache_create")
+        return rc
+    return h.value
+
+
+def moe_cache_destroy(cache) -> None:
+    rc = load_library().moe_cache_destroy(cache)
+    if rc:
+        raise MoeError(rc, "moe_cache_destroy")
+
+
+def moe_forward_cached(cache, layer: int, shape: moe_shape_t, x, router_w, router_b, ws_gate, ws_up, ws_down, out,
+                       workspace, ws_bytes=None, stream=None, check=True) -> int:
+    nb = _nbytes(workspace) if ws_bytes is None else ws_bytes
+    rc = load_library().moe_forward_cached(cache, layer, ctypes.byref(shape), _ptr(x), _ptr(router_w),
+                                           _ptr(router_b), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(out),
+                                           _ptr(workspace), nb, _stream(stream))
+    if check and rc:
+        raise MoeError(rc, "moe_forward_cached")
+    return rc
+
+
+def moe_cache_stats(cache, reset: bool = False) -> dict:
+    st = moe_cache_stats_t()
+    rc = load_library().moe_cache_stats(cache, ctypes.byref(st), 1 if reset else 0)
+    if rc:
+        raise MoeError(rc, "moe_cache_stats")
+    return {n: getattr(st, n) for n, _ in moe_cache_stats_t._fields_}
+
+
+def moe_cache_flush(cache) -> None:
+    rc = load_library().moe_cache_flush(cache)
+    if rc:
+        raise MoeError(rc, "moe_cache_flush")
 
 
 def alloc_sparse_workspace(shape: moe_shape_t, budget: int, device="cuda"):

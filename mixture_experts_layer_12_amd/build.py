@@ -10,7 +10,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/api.cpp", "csrc/router.hip", "csrc/decode.hip", "csrc/decode_fused.hip", "csrc/sparse.hip",
-           "csrc/prefill.hip", "csrc/probe.hip", "csrc/noalloc.hip"]
+           "csrc/prefill.hip", "csrc/probe.hip", "csrc/noalloc.hip", "csrc/cache.cpp"]
 HEADERS = ["csrc/common.hpp", "csrc/router_items.hpp", "csrc/decode_items.hpp", "../include/moe.h",
            "../include/moe_probe.h"]
 OUT = os.path.join(HERE, "lib", "libmoe.so")

@@ -282,7 +282,10 @@ const char* moe_strerror(int code) {
     case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failure";
-    case MOE_ERR_TOO_LARGE: return "shape needs more workspace than the static scratch of moe_forward_noalloc";
+    case MOE_ERR_TOO_LARGE:
+      return "shape needs more workspace than the static scratch of moe_forward_noalloc, or more experts per "
+             "pass than the expert cache has slots";
+    case MOE_ERR_NOT_PINNED: return "host expert stack is not pinned host memory";
     default: return "unknown error code";
   }
 }
@@ -391,9 +394,11 @@ struct StageEvents : moe::StageMarker {
 int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
                  const void* w_gate, const void* w_up, const void* w_down,
                  const void* ws_gate, const void* ws_up, const void* ws_down,
-                 void* out, void* workspace, size_t ws_bytes, void* stream, void* const* events, int n_events) {
+                 void* out, void* workspace, size_t ws_bytes, void* stream, void* const* events, int n_events,
+                 moe::DecodeHook* hook = nullptr) {
   int rc = check_shape(s);
   if (rc) return rc;
+  if (hook && s->path != MOE_PATH_DECODE) return MOE_ERR_SHAPE;   // the hook runs between decode launches
   if (s->T == 0) return MOE_OK;
   if (!x || !router_w || !w_gate || !w_up || !w_down || !out || !workspace) return MOE_ERR_NULL;
   const bool has_shared = s->n_shared > 0;
@@ -506,7 +511,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     // Few assignments and a small gate/up grid: the router launch computes the logits only, and
     // every routed gate/up work-group selects and dispatches in its prologue (one launch fewer
     // on the critical path of a latency-bound layer; larger grids would repeat it too often).
-    const bool pro = Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
+    const bool pro = !hook && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
                      long(n_gu_rt) * (d.n_routed_slots + d.S) <= kRouteInGateUpMaxGroups;
     // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
     ra.logit_parts = (nblocks < 64 && (pro || nblocks > 1)) ? 4 : 1;
@@ -526,9 +531,13 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
         return e;
       sev.mark(st);
     }
+    if (hook)
+      if (int e = hook->before_experts(d, st)) return e;
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, s->router_dtype, n_gu_rt, st,
                                               events ? &sev : nullptr)))
       return e;
+    if (hook)
+      if (int e = hook->after_experts(st)) return e;
   }
   return MOE_OK;
 }
@@ -662,6 +671,17 @@ int moe_forward_channel_sparse(const moe_shape_t* s, int32_t budget, const float
 }
 
 }  // extern "C"
+
+namespace moe {
+// moe_forward on the decode path with a hook around each pass's expert launches.
+int forward_hooked(const moe_shape_t* s, const void* x, const void* router_w, const float* router_b,
+                   const void* w_gate, const void* w_up, const void* w_down,
+                   const void* ws_gate, const void* ws_up, const void* ws_down,
+                   void* out, void* workspace, size_t ws_bytes, void* stream, DecodeHook* hook) {
+  return forward_impl(s, x, router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, workspace,
+                      ws_bytes, stream, nullptr, 0, hook);
+}
+}  // namespace moe
 
 extern "C" {
 

@@ -358,6 +358,27 @@ struct DecodeArgs {
   RouterArgs route;     // ... with these arguments (logits in route.rb.logits)
   int shared_in_router; // with route_in_gu: the decode launches start with one for the router logits and
                         // the shared experts' gate/up together; the gate/up launch covers routed slots only
+  const int32_t* active_w;  // null: routed expert e's matrices are matrix e of wg/wu/wd (E of them);
+                            // else entry 1 + j is the matrix of the j-th active expert (an expert
+                            // cache's slot) in stacks of E_w matrices; needs route_in_gu == 0
+  int E_w;
+};
+
+// Longest host list launch_put_i32 writes (an active list of 256 experts and its count).
+constexpr int kPutMaxInts = 257;
+
+// Matrices in the routed stacks (E, or the slots of an expert cache).
+__device__ __forceinline__ long routed_mats(const DecodeArgs& a) { return a.active_w ? a.E_w : a.E; }
+
+// Host callbacks around the expert launches of each decode pass (the expert
+// cache): before_experts runs once the pass's routing is enqueued and may
+// point the routed stacks elsewhere (DecodeArgs wg/wu/wd, active_w, E_w);
+// after_experts runs once the pass's expert launches are enqueued.  A
+// nonzero return ends the call with that code.
+struct DecodeHook {
+  virtual int before_experts(DecodeArgs& d, hipStream_t st) = 0;
+  virtual int after_experts(hipStream_t st) = 0;
+  virtual ~DecodeHook() = default;
 };
 
 // Output rows per down item of the single-launch decode: two row tiles when

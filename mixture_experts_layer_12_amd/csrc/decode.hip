@@ -269,6 +269,7 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
   if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
+  if (a.active_w && (a.route_in_gu || a.E_w < 1)) return hipErrorInvalidValue;
   if (a.shared_in_router && (!a.route_in_gu || a.S == 0 || a.route.logit_parts != 4)) return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
@@ -291,6 +292,26 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_g
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// Small host lists written to device memory in stream order (a kernel
+// argument, so the host copy may change as soon as the launch returns).
+struct I32List {
+  int n;
+  int32_t v[kPutMaxInts];
+};
+
+__global__ void __launch_bounds__(256) put_i32_kernel(int32_t* dst, I32List l) {
+  for (int i = threadIdx.x; i < l.n; i += blockDim.x) dst[i] = l.v[i];
+}
+
+hipError_t launch_put_i32(int32_t* dst, const int32_t* v, int n, hipStream_t st) {
+  if (n < 0 || n > kPutMaxInts) return hipErrorInvalidValue;
+  I32List l;
+  l.n = n;
+  for (int i = 0; i < n; ++i) l.v[i] = v[i];
+  hipLaunchKernelGGL(put_i32_kernel, dim3(1), dim3(256), 0, st, dst, l);
   return hipGetLastError();
 }
 

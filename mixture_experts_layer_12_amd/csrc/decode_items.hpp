@@ -462,23 +462,24 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
   const uint8_t* bg = routed ? a.wg : a.sg;
   const uint8_t* bu = routed ? a.wu : a.su;
   const int N = routed ? a.I : a.Is;
-  const long n_mat = routed ? a.E : a.S;
-  int e, n_e, hrow0, seg = 0;
+  const long n_mat = routed ? routed_mats(a) : a.S;
+  int e, ew, n_e, hrow0, seg = 0;     // ew: the matrix of expert e in the stacks
   if (routed) {
     if constexpr (PRO) {
       if (slot >= R->s_na[0]) return false;
-      e = R->s_e[slot];
+      e = ew = R->s_e[slot];
       n_e = R->s_cnt[slot];
       seg = hrow0 = R->s_cpre[slot];
     } else {
       if (slot >= ld_i32<COH>(a.active)) return false;
       e = ld_i32<COH>(a.active + 1 + slot);
+      ew = a.active_w ? ld_i32<COH>(a.active_w + 1 + slot) : e;
       n_e = ld_i32<COH>(a.counts + e);
       seg = ld_i32<COH>(a.offsets + e);
       hrow0 = ld_i32<COH>(a.cprefix + e);
     }
   } else {
-    e = slot - a.n_routed_slots;
+    e = ew = slot - a.n_routed_slots;
     n_e = a.T;
     hrow0 = a.T * a.k + e * a.T;
   }
@@ -486,14 +487,14 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
   constexpr int F = Fam<WT>::v;
   const int K = a.H, g = lane >> 4;
   RowPtr<WT> rg, ru;
-  rg.init(bg, n_mat, N, K, e, rt * 16 + (lane & 15));
-  ru.init(bu, n_mat, N, K, e, rt * 16 + (lane & 15));
+  rg.init(bg, n_mat, N, K, ew, rt * 16 + (lane & 15));
+  ru.init(bu, n_mat, N, K, ew, rt * 16 + (lane & 15));
   // fp8: the row scales of this lane's output rows, fetched early and applied to the sums
   f32x4_t sg_rows = {1.f, 1.f, 1.f, 1.f}, su_rows = {1.f, 1.f, 1.f, 1.f};
   if constexpr (WT == DT_FP8) {
     if (wave == 0) {
-      sg_rows = fp8_row_scales(bg, n_mat, N, K, e, rt * 16 + (lane >> 4) * 4);
-      su_rows = fp8_row_scales(bu, n_mat, N, K, e, rt * 16 + (lane >> 4) * 4);
+      sg_rows = fp8_row_scales(bg, n_mat, N, K, ew, rt * 16 + (lane >> 4) * 4);
+      su_rows = fp8_row_scales(bu, n_mat, N, K, ew, rt * 16 + (lane >> 4) * 4);
     }
   }
 
@@ -705,15 +706,16 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
   const bool routed = slot < a.n_routed_slots;
   const uint8_t* base = routed ? a.wd : a.sd;     // selects, as in gateup_item
   const int K = routed ? a.I : a.Is;
-  const long n_mat = routed ? a.E : a.S;
-  int e, n_e, hrow0;
+  const long n_mat = routed ? routed_mats(a) : a.S;
+  int e, ew, n_e, hrow0;              // ew: the matrix of expert e in the stacks
   if (routed) {
     if (slot >= ld_i32<COH>(a.active)) return false;
     e = ld_i32<COH>(a.active + 1 + slot);
+    ew = a.active_w ? ld_i32<COH>(a.active_w + 1 + slot) : e;
     n_e = ld_i32<COH>(a.counts + e);
     hrow0 = ld_i32<COH>(a.cprefix + e);
   } else {
-    e = slot - a.n_routed_slots;
+    e = ew = slot - a.n_routed_slots;
     n_e = a.T;
     hrow0 = a.T * a.k + e * a.T;
   }
@@ -724,10 +726,10 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
   f32x4_t sd_rows[RPW];                         // fp8: row scales of this lane's output rows
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    rw[r].init(base, n_mat, H, K, e, row0 + r * 16 + (lane & 15));
+    rw[r].init(base, n_mat, H, K, ew, row0 + r * 16 + (lane & 15));
     sd_rows[r] = f32x4_t{1.f, 1.f, 1.f, 1.f};
     if constexpr (WT == DT_FP8) {
-      if (wave == 0) sd_rows[r] = fp8_row_scales(base, n_mat, H, K, e, row0 + r * 16 + (lane >> 4) * 4);
+      if (wave == 0) sd_rows[r] = fp8_row_scales(base, n_mat, H, K, ew, row0 + r * 16 + (lane >> 4) * 4);
     }
   }
   size_t hoff[NCT];
@@ -858,9 +860,11 @@ __device__ __forceinline__ void down_one_item(const DecodeArgs a, int rt, uint8_
   // expert, whose row is its prefix count; slot k + s is the shared expert s,
   // row k + s.  Lanes are read back with readlane (uniform slot index).
   const int A = ld_i32<false>(a.active);
-  int el = ld_i32<false>(a.active + 1 + (lane < a.k ? lane : a.k - 1));
+  const int jl = lane < a.k ? lane : a.k - 1;
+  int el = ld_i32<false>(a.active + 1 + jl);
   el = el < 0 ? 0 : (el >= a.E ? a.E - 1 : el);   // entries past A are stale
   const int hl = ld_i32<false>(a.cprefix + el);
+  const int wl = a.active_w ? ld_i32<false>(a.active_w + 1 + jl) : el;   // its matrix in the stacks
   // this wave's steps of every slot, all loads in flight at once
   const int nsteps = n_steps<WT>(K);
   const int s0 = wave * nsteps / 4, len = (wave + 1) * nsteps / 4 - s0;
@@ -873,8 +877,8 @@ __device__ __forceinline__ void down_one_item(const DecodeArgs a, int rt, uint8_
       const bool routed = j < a.k;
       if (routed && j >= A) continue;
       RowPtr<WT> rw;
-      rw.init(routed ? a.wd : a.sd, routed ? a.E : a.S, H, K, routed ? __builtin_amdgcn_readlane(el, j) : j - a.k,
-              rt * 16 + (lane & 15));
+      rw.init(routed ? a.wd : a.sd, routed ? routed_mats(a) : a.S, H, K,
+              routed ? __builtin_amdgcn_readlane(wl, j) : j - a.k, rt * 16 + (lane & 15));
       af[i] = load_a<WT>(rw, st, g, K);
     }
   }

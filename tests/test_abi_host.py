@@ -211,3 +211,63 @@ def test_route_workspace_is_at_most_the_forward_workspace(m):
     p = ctypes.addressof(buf)
     assert m.load_library().moe_route(ctypes.byref(s), p, p, None, ctypes.byref(out), p, need - 1,
                                       None) == m.MOE_ERR_WORKSPACE
+
+
+def _stack_bytes(w_dtype, n, N, K):
+    """Bytes of a stack of n matrices [N, K] in the layouts moe.h states."""
+    up = lambda v: -(-v // 256) * 256  # noqa: E731
+    if w_dtype == 0:
+        return n * N * K * 4
+    if w_dtype == 1:
+        return n * N * K * 2
+    if w_dtype == 2:
+        return up(n * N * K // 2) + n * N * (K // 32) * 2
+    if w_dtype == 3:
+        return up(n * N * K) + n * N * (K // 32) * 2
+    return up(n * N * K) + n * N * 4
+
+
+@pytest.mark.parametrize("w_dtype", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("n_slots", [1, 5, 64])
+def test_cache_region_bytes(m, w_dtype, n_slots):
+    up = lambda v: -(-v // 256) * 256  # noqa: E731
+    s = _shape(m, T=1, H=256, E=16, I=96, top_k=4, w_dtype=w_dtype)
+    want = up(4 * (s.E + 1))
+    for N, K in ((s.I, s.H), (s.I, s.H), (s.H, s.I)):
+        want += up(_stack_bytes(w_dtype, n_slots, N, K))
+    assert m.moe_cache_region_bytes(s, n_slots) == want
+
+
+def test_cache_argument_errors_on_the_host(m):
+    lib = m.load_library()
+    s = _shape(m, T=1)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_cache_region_bytes(ctypes.byref(s), 0, ctypes.byref(n)) == m.MOE_ERR_SHAPE
+    assert lib.moe_cache_region_bytes(ctypes.byref(_shape(m, H=100)), 4, ctypes.byref(n)) == m.MOE_ERR_SHAPE
+    h = ctypes.c_void_p(None)
+    layer = m.moe_host_experts_t(None, None, None)
+    big = m.moe_cache_region_bytes(s, 4)
+    buf = (ctypes.c_uint8 * (big + 256))()
+    region = (ctypes.addressof(buf) + 255) // 256 * 256
+    # no layers / no region / no handle
+    assert lib.moe_cache_create(ctypes.byref(s), 1, None, region, 512, 4, 0, 0, region, ctypes.byref(h)) == \
+        m.MOE_ERR_NULL
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), None, 512, 4, 0, 0, region,
+                                ctypes.byref(h)) == m.MOE_ERR_NULL
+    # a region below moe_cache_region_bytes, a prefetch depth of n_layers, no copy stream, NULL stacks
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), region, 512, 4, 0, 0, region,
+                                ctypes.byref(h)) == m.MOE_ERR_WORKSPACE
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), region + 16, big, 4, 0, 0, region,
+                                ctypes.byref(h)) == m.MOE_ERR_ALIGN
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), region, big, 4, 1, 0, region,
+                                ctypes.byref(h)) == m.MOE_ERR_SHAPE
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), region, big, 4, 0, 0, None,
+                                ctypes.byref(h)) == m.MOE_ERR_NULL
+    assert lib.moe_cache_create(ctypes.byref(s), 1, ctypes.byref(layer), region, big, 4, 0, 0, region,
+                                ctypes.byref(h)) == m.MOE_ERR_NULL
+    assert h.value is None
+    st = m.moe_cache_stats_t()
+    assert lib.moe_cache_stats(None, ctypes.byref(st), 0) == m.MOE_ERR_NULL
+    assert lib.moe_cache_flush(None) == m.MOE_ERR_NULL
+    assert lib.moe_cache_destroy(None) == m.MOE_ERR_NULL
+    assert lib.moe_forward_cached(None, 0, ctypes.byref(s), *([None] * 8), 0, None) == m.MOE_ERR_NULL
