@@ -19,7 +19,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdint>
+#include <cstring>
 #include <vector>
 
 #include "common.hpp"
@@ -30,6 +32,9 @@ int forward_hooked(const moe_shape_t* s, const void* x, const void* router_w, co
                    const void* ws_gate, const void* ws_up, const void* ws_down,
                    void* out, void* workspace, size_t ws_bytes, void* stream, DecodeHook* hook);
 hipError_t launch_put_i32(int32_t* dst, const int32_t* v, int n, hipStream_t st);
+hipError_t launch_gather_copy(const void* const* src, void* const* dst, const size_t* bytes, int n, hipStream_t st);
+hipError_t launch_export_list(const int32_t* src, int n, int32_t* dst, unsigned long long* flag,
+                              unsigned long long tag, hipStream_t st);
 void set_last_hip_error(int e);
 }  // namespace moe
 
@@ -38,6 +43,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxSlots = 65536;
 constexpr int kPassMaxT = 64;   // tokens per decode pass (as moe_forward's decode path)
+constexpr size_t kPinListOffset = 64;                 // pinned host buffer: tag, then the active list
+constexpr double kSpinSeconds = 0.2;                  // then the wait for a pass's routing blocks on the stream
 
 size_t roundup(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -101,7 +108,15 @@ int hip_fail(hipError_t e) {
 struct moe_expert_cache : moe::DecodeHook {
   moe_shape_t shape;
   int n_layers, n_slots, depth, shift;
-  std::vector<moe_host_experts_t> host;
+  std::vector<moe_host_experts_t> host;  // device-mapped addresses of the pinned host stacks
+  uint8_t* pin = nullptr;                // pinned, fine-grained host buffer: tag, then a pass's active list
+  uint8_t* pin_dev = nullptr;            // ... as the device addresses it
+  unsigned long long tag = 0;
+  // copies enqueued by fill and not yet launched (launch_copies)
+  std::vector<const void*> seg_src;
+  std::vector<void*> seg_dst;
+  std::vector<size_t> seg_bytes;
+  std::vector<int> seg_slots;
   uint8_t* region;
   Geoms geo;
   hipStream_t copy;
@@ -159,28 +174,67 @@ struct moe_expert_cache : moe::DecodeHook {
       const Geom& g = geo.m[m];
       const uint8_t* h = static_cast<const uint8_t*>(src[m]);
       uint8_t* dst = region + geo.off[m];
-      if (hipError_t r = hipMemcpyAsync(dst + size_t(s) * g.code(), h + size_t(e) * g.code(), g.code(),
-                                        hipMemcpyHostToDevice, copy))
-        return hip_fail(r);
-      if (g.scale()) {
-        if (hipError_t r = hipMemcpyAsync(dst + g.scale_offset(n_slots) + size_t(s) * g.scale(),
-                                          h + g.scale_offset(shape.E) + size_t(e) * g.scale(), g.scale(),
-                                          hipMemcpyHostToDevice, copy))
-          return hip_fail(r);
-      }
+      add_seg(h + size_t(e) * g.code(), dst + size_t(s) * g.code(), g.code());
+      if (g.scale())
+        add_seg(h + g.scale_offset(shape.E) + size_t(e) * g.scale(), dst + g.scale_offset(n_slots) +
+                size_t(s) * g.scale(), g.scale());
       stats.bytes_copied += g.code() + g.scale();
     }
-    if (hipError_t r = hipEventRecord(ready[s], copy)) return hip_fail(r);
+    seg_slots.push_back(s);
     wait_ready[s] = 1;
     stamp[s] = ++clock;
     return MOE_OK;
   }
 
+  void add_seg(const void* src, void* dst, size_t bytes) {
+    seg_src.push_back(src);
+    seg_dst.push_back(dst);
+    seg_bytes.push_back(bytes);
+  }
+
+  // Launch the pending copies on the copy stream (kCopyMaxSegs segments a
+  // launch), then mark each filled slot ready after them.
+  int launch_copies() {
+    for (size_t i = 0; i < seg_src.size(); i += moe::kCopyMaxSegs) {
+      const int n = int(std::min<size_t>(moe::kCopyMaxSegs, seg_src.size() - i));
+      if (hipError_t r = moe::launch_gather_copy(&seg_src[i], &seg_dst[i], &seg_bytes[i], n, copy))
+        return hip_fail(r);
+    }
+    for (int s : seg_slots)
+      if (hipError_t r = hipEventRecord(ready[s], copy)) return hip_fail(r);
+    seg_src.clear();
+    seg_dst.clear();
+    seg_bytes.clear();
+    seg_slots.clear();
+    return MOE_OK;
+  }
+
+  // The pass's active list, read back through the pinned buffer: a kernel
+  // writes it there after the routing, and the host polls the tag (then, past
+  // kSpinSeconds, blocks on the stream).
+  int read_active(const int32_t* active, hipStream_t st) {
+    const int n = shape.E + 1;
+    auto* flag = reinterpret_cast<unsigned long long*>(pin);
+    const unsigned long long want = ++tag;
+    if (hipError_t r = moe::launch_export_list(active, n, reinterpret_cast<int32_t*>(pin_dev + kPinListOffset),
+                                               reinterpret_cast<unsigned long long*>(pin_dev), want, st))
+      return hip_fail(r);
+    const auto t0 = std::chrono::steady_clock::now();
+    for (long it = 0; __atomic_load_n(flag, __ATOMIC_ACQUIRE) != want; ++it) {
+      if ((it & 1023) == 1023 &&
+          std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > kSpinSeconds) {
+        if (hipError_t r = hipStreamSynchronize(st)) return hip_fail(r);
+        if (__atomic_load_n(flag, __ATOMIC_ACQUIRE) != want) return hip_fail(hipErrorLaunchFailure);
+        break;
+      }
+    }
+    std::memcpy(act.data(), pin + kPinListOffset, size_t(n) * 4);
+    return MOE_OK;
+  }
+
   int before_experts(moe::DecodeArgs& d, hipStream_t st) override {
     const int E = shape.E;
-    if (hipError_t r = hipMemcpyAsync(act.data(), d.active, size_t(E + 1) * 4, hipMemcpyDeviceToHost, st))
-      return hip_fail(r);
-    if (hipError_t r = hipStreamSynchronize(st)) return hip_fail(r);
+    if (int rc = read_active(d.active, st)) return rc;
     const int A = act[0];
     if (A < 0 || A > E || A > n_slots) return MOE_ERR_TOO_LARGE;   // not reached: checked per call
     pass_slots.clear();
@@ -211,6 +265,7 @@ struct moe_expert_cache : moe::DecodeHook {
       stamp[s] = ++clock;
       pass_slots.push_back(s);
     }
+    if (int rc = launch_copies()) return rc;
     slot_list[0] = A;
     if (hipError_t r = moe::launch_put_i32(active_w(), slot_list.data(), A + 1, st)) return hip_fail(r);
     for (int s : pass_slots) {
@@ -254,7 +309,7 @@ struct moe_expert_cache : moe::DecodeHook {
     }
     for (int s : pass_slots) in_pass[s] = 0;
     pass_slots.clear();
-    return MOE_OK;
+    return launch_copies();
   }
 };
 
@@ -283,20 +338,39 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
   if (reinterpret_cast<uintptr_t>(region) % kAlign) return MOE_ERR_ALIGN;
   if (region_bytes < need) return MOE_ERR_WORKSPACE;
   if (!copy_stream) return MOE_ERR_NULL;
+  std::vector<moe_host_experts_t> mapped(layers, layers + n_layers);
   for (int l = 0; l < n_layers; ++l) {
-    const void* p[3] = {layers[l].w_gate, layers[l].w_up, layers[l].w_down};
-    for (const void* q : p) {
-      if (!q) return MOE_ERR_NULL;
+    const void** p[3] = {&mapped[l].w_gate, &mapped[l].w_up, &mapped[l].w_down};
+    for (const void** q : p) {
+      if (!*q) return MOE_ERR_NULL;
+      if (reinterpret_cast<uintptr_t>(*q) % 16) return MOE_ERR_ALIGN;
       hipPointerAttribute_t at{};
-      const hipError_t r = hipPointerGetAttributes(&at, q);
-      if (r != hipSuccess || at.type != hipMemoryTypeHost) {
+      void* dp = nullptr;
+      hipError_t r = hipPointerGetAttributes(&at, *q);
+      if (r == hipSuccess && at.type == hipMemoryTypeHost) r = hipHostGetDevicePointer(&dp, const_cast<void*>(*q), 0);
+      if (r != hipSuccess || at.type != hipMemoryTypeHost || !dp) {
         (void)hipGetLastError();
         return MOE_ERR_NOT_PINNED;
       }
+      *q = dp;
     }
   }
-  auto* c = new moe_expert_cache(s, n_layers, layers, region, n_slots, prefetch_depth, prefetch_shift,
+  auto* c = new moe_expert_cache(s, n_layers, mapped.data(), region, n_slots, prefetch_depth, prefetch_shift,
                                  static_cast<hipStream_t>(copy_stream));
+  {
+    void* pin = nullptr;
+    void* pin_dev = nullptr;
+    hipError_t r = hipHostMalloc(&pin, kPinListOffset + size_t(s->E + 1) * 4, hipHostMallocCoherent);
+    if (r == hipSuccess) r = hipHostGetDevicePointer(&pin_dev, pin, 0);
+    if (r != hipSuccess) {
+      if (pin) (void)hipHostFree(pin);
+      delete c;
+      return hip_fail(r);
+    }
+    c->pin = static_cast<uint8_t*>(pin);
+    c->pin_dev = static_cast<uint8_t*>(pin_dev);
+    *reinterpret_cast<unsigned long long*>(c->pin) = 0;
+  }
   for (int i = 0; i < n_slots; ++i) {
     hipError_t r = hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming);
     if (r == hipSuccess) r = hipEventCreateWithFlags(&c->released[i], hipEventDisableTiming);
@@ -316,6 +390,7 @@ int moe_cache_destroy(moe_expert_cache_t* c) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->released)
     if (e) (void)hipEventDestroy(e);
+  if (c->pin) (void)hipHostFree(c->pin);
   delete c;
   return r == hipSuccess ? MOE_OK : hip_fail(r);
 }

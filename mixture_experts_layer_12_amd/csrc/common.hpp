@@ -366,6 +366,8 @@ struct DecodeArgs {
 
 // Longest host list launch_put_i32 writes (an active list of 256 experts and its count).
 constexpr int kPutMaxInts = 257;
+// Segments of one launch_gather_copy (seven experts of three quantised matrices).
+constexpr int kCopyMaxSegs = 42;
 
 // Matrices in the routed stacks (E, or the slots of an expert cache).
 __device__ __forceinline__ long routed_mats(const DecodeArgs& a) { return a.active_w ? a.E_w : a.E; }

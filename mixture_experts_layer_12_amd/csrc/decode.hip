@@ -315,4 +315,78 @@ hipError_t launch_put_i32(int32_t* dst, const int32_t* v, int n, hipStream_t st)
   return hipGetLastError();
 }
 
+// Host-to-device copies of expert matrices by the GPU itself: work-group b
+// copies 64 KiB chunk b of the concatenated segments (16-byte loads from
+// device-mapped pinned host memory, 16 in flight per thread), so one launch
+// keeps PCIe busy however small each segment is.
+struct CopySeg {
+  const uint8_t* src;   // device-mapped pinned host memory
+  uint8_t* dst;
+  unsigned long long bytes;   // multiple of 16; src and dst 16-byte aligned
+  unsigned long long chunk0;  // first chunk of this segment
+};
+struct CopyList {
+  int n;
+  CopySeg s[kCopyMaxSegs];
+};
+
+constexpr int kCopyChunk = 65536;
+
+__global__ void __launch_bounds__(256) gather_copy_kernel(CopyList l) {
+  const unsigned long long b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < l.n && l.s[i + 1].chunk0 <= b) ++i;
+  const CopySeg sg = l.s[i];
+  const unsigned long long off = (b - sg.chunk0) * kCopyChunk;
+  if (off >= sg.bytes) return;
+  const unsigned long long len = sg.bytes - off < kCopyChunk ? sg.bytes - off : kCopyChunk;
+  const int n16 = int(len / 16);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(sg.src + off);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sg.dst + off);
+  u32x4_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = j * 256 + int(threadIdx.x);
+    if (q < n16) v[j] = __builtin_nontemporal_load(src + q);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = j * 256 + int(threadIdx.x);
+    if (q < n16) dst[q] = v[j];
+  }
+}
+
+hipError_t launch_gather_copy(const void* const* src, void* const* dst, const size_t* bytes, int n, hipStream_t st) {
+  if (n < 1 || n > kCopyMaxSegs) return hipErrorInvalidValue;
+  CopyList l;
+  l.n = n;
+  unsigned long long chunks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (bytes[i] % 16 || reinterpret_cast<uintptr_t>(src[i]) % 16 || reinterpret_cast<uintptr_t>(dst[i]) % 16)
+      return hipErrorInvalidValue;
+    l.s[i] = CopySeg{static_cast<const uint8_t*>(src[i]), static_cast<uint8_t*>(dst[i]), bytes[i], chunks};
+    chunks += (bytes[i] + kCopyChunk - 1) / kCopyChunk;
+  }
+  if (chunks == 0) return hipSuccess;
+  if (chunks > 0x7fffffffull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_copy_kernel, dim3(unsigned(chunks)), dim3(256), 0, st, l);
+  return hipGetLastError();
+}
+
+// A pass's active list written to (device-mapped, fine-grained) pinned host
+// memory, then `tag` into *flag once every element is visible to the host.
+__global__ void __launch_bounds__(256) export_list_kernel(const int32_t* src, int n, int32_t* dst,
+                                                          unsigned long long* flag, unsigned long long tag) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_export_list(const int32_t* src, int n, int32_t* dst, unsigned long long* flag,
+                              unsigned long long tag, hipStream_t st) {
+  hipLaunchKernelGGL(export_list_kernel, dim3(1), dim3(256), 0, st, src, n, dst, flag, tag);
+  return hipGetLastError();
+}
+
 }  // namespace moe
