@@ -464,6 +464,11 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
+    # residency: one untimed call per weight copy, so that no timed step is the
+    # first GPU access to a buffer (page-table set-up is not part of a step)
+    torch.cuda.synchronize()
+    for c in range(copies):
+        step(c)
     # eager warm-up (also performs the library's one-time set-up before any capture)
     torch.cuda.synchronize()
     for i in range(max(args.warmup, 1)):

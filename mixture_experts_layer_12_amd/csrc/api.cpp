@@ -31,7 +31,13 @@ namespace {
 #define MOE_EPILOGUE_MAX_SLOTS 16
 #endif
 constexpr int kEpilogueMaxSlots = MOE_EPILOGUE_MAX_SLOTS;   // decode: expert slots per output row group for the combine epilogue
-constexpr long kRouteInGateUpMaxGroups = 1024;   // decode: gate/up grids that select in their own prologue
+// decode: gate/up grids that select in their own prologue -- up to 1024
+// work-groups, or up to 8192 when the selection is tiny (tokens * experts <=
+// 128, as the Mixtral-shaped batch of 8: 3 us less per layer; a DeepSeek-
+// shaped batch of 8 over 64 experts loses 12 us at 4400 work-groups)
+constexpr long kRouteInGateUpMaxGroups = 1024;
+constexpr long kRouteInGateUpMaxGroupsTiny = 8192;
+constexpr long kTinySelection = 128;
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
 constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
@@ -508,11 +514,13 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       continue;
     }
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    // Few assignments and a small gate/up grid: the router launch computes the logits only, and
-    // every routed gate/up work-group selects and dispatches in its prologue (one launch fewer
-    // on the critical path of a latency-bound layer; larger grids would repeat it too often).
+    // Few assignments and a small gate/up grid (or a tiny selection): the router launch computes
+    // the logits only, and every routed gate/up work-group selects and dispatches in its prologue
+    // (one launch fewer on the critical path; larger grids would repeat a costly selection too often).
+    const long gu_groups = long(n_gu_rt) * (d.n_routed_slots + d.S);
     const bool pro = !hook && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
-                     long(n_gu_rt) * (d.n_routed_slots + d.S) <= kRouteInGateUpMaxGroups;
+                     gu_groups <= (long(Tc) * s->E <= kTinySelection ? kRouteInGateUpMaxGroupsTiny
+                                                                     : kRouteInGateUpMaxGroups);
     // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
     ra.logit_parts = (nblocks < 64 && (pro || nblocks > 1)) ? 4 : 1;
     if (d.dn_count) {             // the router launch clears the down launch's arrival counters
