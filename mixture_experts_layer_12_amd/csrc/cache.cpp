@@ -7,10 +7,11 @@
 // compute stream.  The expert kernels are the decode path's; they read the
 // routed matrices from the slot stacks through DecodeArgs::active_w.
 //
-// Region layout (device, caller-allocated):
-//   [0, 256 * ceil((E + 1) * 4 / 256))    active_w: count, then the slot of each active expert
-//   then three stacks of n_slots matrices in w_dtype's layout (gate, up, down),
-//   each starting at a multiple of 256 bytes.
+// Region layout (device, caller-allocated): three stacks of n_slots matrices
+// in w_dtype's layout (gate, up, down), each starting at a multiple of 256
+// bytes.  The slot of each active expert (DecodeArgs::active_w) lives in the
+// cache's pinned host buffer: the host writes it before the expert launches
+// and they read it through its device mapping.
 // Copying expert e of a layer into slot s copies matrix e of each host stack
 // to matrix s of the slot stack: its codes, and for the quantised formats its
 // scales, which sit after all codes of a stack.
@@ -31,7 +32,6 @@ int forward_hooked(const moe_shape_t* s, const void* x, const void* router_w, co
                    const void* w_gate, const void* w_up, const void* w_down,
                    const void* ws_gate, const void* ws_up, const void* ws_down,
                    void* out, void* workspace, size_t ws_bytes, void* stream, DecodeHook* hook);
-hipError_t launch_put_i32(int32_t* dst, const int32_t* v, int n, hipStream_t st);
 hipError_t launch_gather_copy(const void* const* src, void* const* dst, const size_t* bytes, int n, hipStream_t st);
 hipError_t launch_export_list(const int32_t* src, int n, int32_t* dst, unsigned long long* flag,
                               unsigned long long tag, hipStream_t st);
@@ -43,7 +43,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxSlots = 65536;
 constexpr int kPassMaxT = 64;   // tokens per decode pass (as moe_forward's decode path)
-constexpr size_t kPinListOffset = 64;                 // pinned host buffer: tag, then the active list
+constexpr size_t kPinListOffset = 64;                 // pinned host buffer: tag, active list, slot list
 constexpr double kSpinSeconds = 0.2;                  // then the wait for a pass's routing blocks on the stream
 
 size_t roundup(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -79,11 +79,10 @@ struct Geom {
 
 struct Geoms {
   Geom m[3];   // gate, up, down
-  size_t head, off[3], total;
+  size_t off[3], total;
   Geoms(const moe_shape_t* s, long n_slots)
       : m{{s->w_dtype, s->I, s->H}, {s->w_dtype, s->I, s->H}, {s->w_dtype, s->H, s->I}} {
-    head = roundup(size_t(s->E + 1) * 4, kAlign);
-    size_t o = head;
+    size_t o = 0;
     for (int i = 0; i < 3; ++i) {
       off[i] = o;
       o = roundup(o + m[i].stack(n_slots), kAlign);
@@ -144,7 +143,7 @@ struct moe_expert_cache : moe::DecodeHook {
         wait_ready(C, 0), wait_release(C, 0), in_pass(C, 0), ready(C, nullptr), released(C, nullptr),
         where(size_t(L) * s->E, -1), act(s->E + 1), slot_list(s->E + 1) {}
 
-  int32_t* active_w() const { return reinterpret_cast<int32_t*>(region); }
+  size_t pin_slot_offset() const { return kPinListOffset + roundup(size_t(shape.E + 1) * 4, 64); }
   const uint8_t* stack(int m) const { return region + geo.off[m]; }
 
   // Least recently used slot outside the current pass (and, for prefetches,
@@ -266,8 +265,9 @@ struct moe_expert_cache : moe::DecodeHook {
       pass_slots.push_back(s);
     }
     if (int rc = launch_copies()) return rc;
+    // the previous pass's launches, the last readers of the list, finished before its routing did
     slot_list[0] = A;
-    if (hipError_t r = moe::launch_put_i32(active_w(), slot_list.data(), A + 1, st)) return hip_fail(r);
+    std::memcpy(pin + pin_slot_offset(), slot_list.data(), size_t(A + 1) * 4);
     for (int s : pass_slots) {
       if (!wait_ready[s]) continue;
       if (hipError_t r = hipStreamWaitEvent(st, ready[s], 0)) return hip_fail(r);
@@ -276,7 +276,7 @@ struct moe_expert_cache : moe::DecodeHook {
     d.wg = stack(0);
     d.wu = stack(1);
     d.wd = stack(2);
-    d.active_w = active_w();
+    d.active_w = reinterpret_cast<const int32_t*>(pin_dev + pin_slot_offset());
     d.E_w = n_slots;
     return MOE_OK;
   }
@@ -360,7 +360,7 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
   {
     void* pin = nullptr;
     void* pin_dev = nullptr;
-    hipError_t r = hipHostMalloc(&pin, kPinListOffset + size_t(s->E + 1) * 4, hipHostMallocCoherent);
+    hipError_t r = hipHostMalloc(&pin, c->pin_slot_offset() + size_t(s->E + 1) * 4, hipHostMallocCoherent);
     if (r == hipSuccess) r = hipHostGetDevicePointer(&pin_dev, pin, 0);
     if (r != hipSuccess) {
       if (pin) (void)hipHostFree(pin);

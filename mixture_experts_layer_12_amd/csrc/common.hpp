@@ -364,8 +364,6 @@ struct DecodeArgs {
   int E_w;
 };
 
-// Longest host list launch_put_i32 writes (an active list of 256 experts and its count).
-constexpr int kPutMaxInts = 257;
 // Segments of one launch_gather_copy (seven experts of three quantised matrices).
 constexpr int kCopyMaxSegs = 42;
 

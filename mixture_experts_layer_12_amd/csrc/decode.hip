@@ -295,26 +295,6 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_g
   return hipGetLastError();
 }
 
-// Small host lists written to device memory in stream order (a kernel
-// argument, so the host copy may change as soon as the launch returns).
-struct I32List {
-  int n;
-  int32_t v[kPutMaxInts];
-};
-
-__global__ void __launch_bounds__(256) put_i32_kernel(int32_t* dst, I32List l) {
-  for (int i = threadIdx.x; i < l.n; i += blockDim.x) dst[i] = l.v[i];
-}
-
-hipError_t launch_put_i32(int32_t* dst, const int32_t* v, int n, hipStream_t st) {
-  if (n < 0 || n > kPutMaxInts) return hipErrorInvalidValue;
-  I32List l;
-  l.n = n;
-  for (int i = 0; i < n; ++i) l.v[i] = v[i];
-  hipLaunchKernelGGL(put_i32_kernel, dim3(1), dim3(256), 0, st, dst, l);
-  return hipGetLastError();
-}
-
 // Host-to-device copies of expert matrices by the GPU itself: work-group b
 // copies 64 KiB chunk b of the concatenated segments (16-byte loads from
 // device-mapped pinned host memory, 16 in flight per thread), so one launch
