@@ -130,11 +130,14 @@ def layer_bytes(wl):
             + wl.E * wl.H * act_bytes(wl.r_dtype))
 
 
-def gateup_alg_bytes(wl, n_active, T):
+def gateup_alg_bytes(wl, n_active, T, shared=True):
     """Algorithmic bytes of one decode gate/up launch: the engaged experts' gate
-    and up rows, the activations read and the intermediate rows written."""
-    return (n_active * 2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + wl.S * 2 * mat_bytes(wl.w_dtype, wl.Is, wl.H)
-            + T * wl.H * act_bytes(wl.x_dtype) + (T * wl.k * wl.I + wl.S * T * wl.Is) * h_elem_bytes(wl))
+    and up rows, the activations read and the intermediate rows written (the
+    shared experts' part only when the launch computes them: with
+    shared=False they run in the router launch)."""
+    S = wl.S if shared else 0
+    return (n_active * 2 * mat_bytes(wl.w_dtype, wl.I, wl.H) + S * 2 * mat_bytes(wl.w_dtype, wl.Is, wl.H)
+            + T * wl.H * act_bytes(wl.x_dtype) + (T * wl.k * wl.I + S * T * wl.Is) * h_elem_bytes(wl))
 
 
 def down_alg_bytes(wl, n_active, T):
@@ -569,7 +572,9 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
             klaunch = avg[0]
         else:
             kname = "decode_gateup"
-            alg = sum(gateup_alg_bytes(wl, n_active[c], wl.T) for c in steps_copies) / args.steps
+            # with the shared experts' gate/up in the router launch, the routed gate/up launch reads no shared rows
+            shared_here = not m.moe_forward_tables(shape)["shared_in_router"]
+            alg = sum(gateup_alg_bytes(wl, n_active[c], wl.T, shared_here) for c in steps_copies) / args.steps
             achieved = alg / (avg[1] * 1e-3) / 1e9
             klaunch = avg[1]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -47,7 +47,8 @@ class moe_route_out_t(ctypes.Structure):
 class moe_forward_tables_t(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_int32) for n in ("path", "tokens", "tile_m", "capacity", "n_tiles")] +
                 [(n, ctypes.c_size_t) for n in ("topk_ids", "topk_w", "counts", "offsets", "sorted_ids",
-                                                "tile_expert", "inv", "active", "status")])
+                                                "tile_expert", "inv", "active", "status")] +
+                [(n, ctypes.c_int32) for n in ("route_in_gateup", "shared_in_router")])
 
 
 class moe_host_experts_t(ctypes.Structure):

@@ -275,6 +275,36 @@ moe::RouterArgs router_args(const moe_shape_t* s, int T, const void* x, const vo
   return a;
 }
 
+// Launch plan of one multi-launch decode pass of Tc tokens.
+//  route_in_gu: few assignments and a small gate/up grid (or a tiny
+//    selection): the router launch computes the logits only, and every routed
+//    gate/up work-group selects and dispatches in its prologue (one launch
+//    fewer on the critical path; larger grids would repeat a costly selection
+//    too often).  Never with a hook, which needs the routing before the
+//    expert launches.
+//  logit_parts: few logit tiles are split over 4 work-groups each (partial
+//    planes) to spread the router read.
+//  shared_in_router: with route_in_gu and split logits, the shared experts'
+//    gate/up runs in the logits launch (it needs no routing).
+struct PassPlan {
+  bool route_in_gu, shared_in_router;
+  int logit_parts;
+};
+PassPlan pass_plan(const moe_shape_t* s, int Tc, bool hooked) {
+  const int n_routed_slots = std::min(s->E, Tc * s->top_k);
+  const int S = s->n_shared, Is = S > 0 ? s->I_shared : 0;
+  const long n_gu_rt = (std::max(s->I, Is) + 15) / 16;
+  const long gu_groups = n_gu_rt * (n_routed_slots + S);
+  const int nblocks = ((s->E + 15) / 16) * ((Tc + 15) / 16);
+  PassPlan p{};
+  p.route_in_gu = !hooked && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
+                  gu_groups <= (long(Tc) * s->E <= kTinySelection ? kRouteInGateUpMaxGroupsTiny
+                                                                  : kRouteInGateUpMaxGroups);
+  p.logit_parts = (nblocks < 64 && (p.route_in_gu || nblocks > 1)) ? 4 : 1;
+  p.shared_in_router = p.route_in_gu && S > 0 && p.logit_parts == 4;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,6 +369,9 @@ int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t) {
   t->inv = L.inv;
   t->active = L.active;
   t->status = L.path == MOE_PATH_DECODE_FUSED ? L.error : 0;
+  const PassPlan plan = pass_plan(s, last, false);
+  t->route_in_gateup = L.path == MOE_PATH_DECODE && last > 0 && plan.route_in_gu;
+  t->shared_in_router = L.path == MOE_PATH_DECODE && last > 0 && plan.shared_in_router;
   return MOE_OK;
 }
 
@@ -514,15 +547,9 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       continue;
     }
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    // Few assignments and a small gate/up grid (or a tiny selection): the router launch computes
-    // the logits only, and every routed gate/up work-group selects and dispatches in its prologue
-    // (one launch fewer on the critical path; larger grids would repeat a costly selection too often).
-    const long gu_groups = long(n_gu_rt) * (d.n_routed_slots + d.S);
-    const bool pro = !hook && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
-                     gu_groups <= (long(Tc) * s->E <= kTinySelection ? kRouteInGateUpMaxGroupsTiny
-                                                                     : kRouteInGateUpMaxGroups);
-    // few logit tiles: split each over 4 work-groups (partial planes) to spread the router read
-    ra.logit_parts = (nblocks < 64 && (pro || nblocks > 1)) ? 4 : 1;
+    const PassPlan plan = pass_plan(s, Tc, hook != nullptr);
+    const bool pro = plan.route_in_gu;
+    ra.logit_parts = plan.logit_parts;
     if (d.dn_count) {             // the router launch clears the down launch's arrival counters
       ra.zero_f32 = reinterpret_cast<float*>(d.dn_count);
       ra.zero_n = roundup(s->H / 16, 4);
@@ -530,9 +557,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     if (pro) {
       d.route_in_gu = 1;
       d.route = ra;
-      // the shared experts' gate/up runs in the logits launch (it needs no routing), which
-      // launch_decode makes itself
-      d.shared_in_router = d.S > 0 && ra.logit_parts == 4 ? 1 : 0;
+      d.shared_in_router = plan.shared_in_router;
     }
     if (!d.shared_in_router) {
       if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st, pro)))
