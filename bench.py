@@ -727,7 +727,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the memory clocks settle within a few dozen steps)")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed loop for the spread")
     ap.add_argument("--workload", default=None, choices=sorted(synth.WORKLOADS),
                     help="time this workload only (default: the headline with the metric's other workloads nested)")

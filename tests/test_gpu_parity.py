@@ -91,6 +91,9 @@ SMALL = {
     "t1_one_f32": W("t1_one_f32", T=1, H=96, E=6, k=2, I=96, S=1, Is=96,
                     x_dtype="f32", w_dtype="f32", r_dtype="f32"),
     "t1_pairs_over": W("t1_pairs_over", T=1, H=128, E=32, k=8, I=256, S=2, Is=256),
+    # four 16-token column tiles with the combine in the down epilogue (9 slots): output row groups
+    # of 16 (64 bytes), two to a 128-byte line, 10 of them (lines shared across work-groups)
+    "epi_nct4_h160_t40": W("epi_nct4_h160_t40", T=40, H=160, E=8, k=2, I=64, S=1, Is=64),
 }
 BF16_BOTH_PATHS = ["mixtral_small_bf16", "deepseek_small_t8", "deepseek_small_t40", "prefill_small_zipf",
                    "k_equals_E", "t1_k1", "prefill_ksplit2", "prefill_ksplit4_shared", "prefill_ksplit4_ragged"]
