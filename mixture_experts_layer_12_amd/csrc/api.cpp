@@ -32,9 +32,10 @@ namespace {
 #endif
 constexpr int kEpilogueMaxSlots = MOE_EPILOGUE_MAX_SLOTS;   // decode: expert slots per output row group for the combine epilogue
 // decode: gate/up grids that select in their own prologue -- up to 1024
-// work-groups, or up to 8192 when the selection is tiny (tokens * experts <=
-// 128, as the Mixtral-shaped batch of 8: 3 us less per layer; a DeepSeek-
-// shaped batch of 8 over 64 experts loses 12 us at 4400 work-groups)
+// work-groups, or up to 8192 with bf16 or fp32 weights when the selection is
+// tiny (tokens * experts <= 128: the Mixtral-shaped batches of 1 and 8 gain
+// 2.5-3 us per layer; with fp8 weights the batch of 8 loses 48 us, and a
+// DeepSeek-shaped batch of 8 over 64 experts loses 12 us at 4400 work-groups)
 constexpr long kRouteInGateUpMaxGroups = 1024;
 constexpr long kRouteInGateUpMaxGroupsTiny = 8192;
 constexpr long kTinySelection = 128;
@@ -297,9 +298,9 @@ PassPlan pass_plan(const moe_shape_t* s, int Tc, bool hooked) {
   const long gu_groups = n_gu_rt * (n_routed_slots + S);
   const int nblocks = ((s->E + 15) / 16) * ((Tc + 15) / 16);
   PassPlan p{};
+  const bool tiny = long(Tc) * s->E <= kTinySelection && (s->w_dtype == MOE_BF16 || s->w_dtype == MOE_F32);
   p.route_in_gu = !hooked && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
-                  gu_groups <= (long(Tc) * s->E <= kTinySelection ? kRouteInGateUpMaxGroupsTiny
-                                                                  : kRouteInGateUpMaxGroups);
+                  gu_groups <= (tiny ? kRouteInGateUpMaxGroupsTiny : kRouteInGateUpMaxGroups);
   p.logit_parts = (nblocks < 64 && (p.route_in_gu || nblocks > 1)) ? 4 : 1;
   p.shared_in_router = p.route_in_gu && S > 0 && p.logit_parts == 4;
   return p;

@@ -276,6 +276,7 @@ def test_cache_argument_errors_on_the_host(m):
 @pytest.mark.parametrize("kw, route_in_gateup, shared_in_router", [
     (dict(T=1, H=2048, E=256, I=512, top_k=8, n_shared=1, I_shared=512, w_dtype=2), 1, 1),  # Qwen-A3B-shaped
     (dict(T=8, H=4096, E=8, I=14336, top_k=2), 1, 0),          # tiny selection on a large grid
+    (dict(T=8, H=4096, E=8, I=14336, top_k=2, w_dtype=4), 0, 0),   # ... but not with fp8 weights
     (dict(T=8, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 0),   # too many groups
     (dict(T=40, E=16, top_k=2), 0, 0),                         # more than 16 tokens
     (dict(T=4096, H=4096, E=8, I=14336, top_k=2), 0, 0),       # prefill
