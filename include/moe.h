@@ -88,7 +88,8 @@ enum {
                               static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES);
                               moe_forward_cached: a pass can engage more experts than
                               the cache has slots */
-  MOE_ERR_NOT_PINNED = -8  /* moe_cache_create: a host expert stack is not pinned host memory */
+  MOE_ERR_NOT_PINNED = -8, /* moe_cache_create: a host expert stack is not pinned host memory */
+  MOE_ERR_HOST_ALLOC = -9  /* moe_cache_create: its host bookkeeping could not be allocated */
 };
 
 /*

@@ -24,6 +24,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
     0, -1, -2, -3, -4, -5, -6)
 MOE_ERR_TOO_LARGE = -7
 MOE_ERR_NOT_PINNED = -8
+MOE_ERR_HOST_ALLOC = -9
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "q4_0": MOE_Q4_0, "q8_0": MOE_Q8_0, "fp8_e4m3": MOE_FP8_E4M3}

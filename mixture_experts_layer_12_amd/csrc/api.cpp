@@ -323,6 +323,7 @@ const char* moe_strerror(int code) {
       return "shape needs more workspace than the static scratch of moe_forward_noalloc, or more experts per "
              "pass than the expert cache has slots";
     case MOE_ERR_NOT_PINNED: return "host expert stack is not pinned host memory";
+    case MOE_ERR_HOST_ALLOC: return "host memory for the expert cache's bookkeeping could not be allocated";
     default: return "unknown error code";
   }
 }

@@ -132,6 +132,8 @@ struct moe_expert_cache : moe::DecodeHook {
   std::vector<int32_t> act;          // host copy of a pass's active list
   std::vector<int32_t> slot_list;    // count, then the slot of each active expert
   std::vector<int> pass_slots;
+  std::vector<char> taken;           // scratch of after_experts (slots placed by this prefetch round)
+  std::vector<char> none;            // all zero: no slot excluded beyond the pass's own
   uint64_t clock = 0;
   int layer = 0;                     // layer of the call in progress
   moe_cache_stats_t stats{};
@@ -141,7 +143,14 @@ struct moe_expert_cache : moe::DecodeHook {
       : shape(*s), n_layers(L), n_slots(C), depth(d), shift(sh), host(layers, layers + L),
         region(static_cast<uint8_t*>(reg)), geo(s, C), copy(cs), key(C, -1), stamp(C, 0), prefetched(C, 0),
         wait_ready(C, 0), wait_release(C, 0), in_pass(C, 0), ready(C, nullptr), released(C, nullptr),
-        where(size_t(L) * s->E, -1), act(s->E + 1), slot_list(s->E + 1) {}
+        where(size_t(L) * s->E, -1), act(s->E + 1), slot_list(s->E + 1), taken(C, 0), none(C, 0) {
+    pass_slots.reserve(size_t(s->E));
+    const size_t segs = size_t(C) * 6;
+    seg_src.reserve(segs);
+    seg_dst.reserve(segs);
+    seg_bytes.reserve(segs);
+    seg_slots.reserve(size_t(C));
+  }
 
   size_t pin_slot_offset() const { return kPinListOffset + roundup(size_t(shape.E + 1) * 4, 64); }
   const uint8_t* stack(int m) const { return region + geo.off[m]; }
@@ -245,7 +254,6 @@ struct moe_expert_cache : moe::DecodeHook {
       slot_list[1 + j] = s;
       if (s >= 0) in_pass[s] = 1;
     }
-    std::vector<char> none(n_slots, 0);
     for (int j = 0; j < A; ++j) {
       ++stats.lookups;
       int s = slot_list[1 + j];
@@ -288,7 +296,7 @@ struct moe_expert_cache : moe::DecodeHook {
     }
     // prefetch the predicted experts of the next layers into slots this pass does not use
     const int E = shape.E, A = act[0];
-    std::vector<char> taken(n_slots, 0);
+    std::fill(taken.begin(), taken.end(), 0);
     for (int dd = 1; dd <= depth; ++dd) {
       const int l = (layer + dd) % n_layers;
       const int off = int(((long(dd) * shift) % E + E) % E);
@@ -338,7 +346,12 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
   if (reinterpret_cast<uintptr_t>(region) % kAlign) return MOE_ERR_ALIGN;
   if (region_bytes < need) return MOE_ERR_WORKSPACE;
   if (!copy_stream) return MOE_ERR_NULL;
-  std::vector<moe_host_experts_t> mapped(layers, layers + n_layers);
+  std::vector<moe_host_experts_t> mapped;
+  try {
+    mapped.assign(layers, layers + n_layers);
+  } catch (...) {
+    return MOE_ERR_HOST_ALLOC;
+  }
   for (int l = 0; l < n_layers; ++l) {
     const void** p[3] = {&mapped[l].w_gate, &mapped[l].w_up, &mapped[l].w_down};
     for (const void** q : p) {
@@ -355,8 +368,13 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
       *q = dp;
     }
   }
-  auto* c = new moe_expert_cache(s, n_layers, mapped.data(), region, n_slots, prefetch_depth, prefetch_shift,
-                                 static_cast<hipStream_t>(copy_stream));
+  moe_expert_cache* c = nullptr;
+  try {       // no exception crosses the C ABI: host allocation failure is reported as MOE_ERR_HOST_ALLOC
+    c = new moe_expert_cache(s, n_layers, mapped.data(), region, n_slots, prefetch_depth, prefetch_shift,
+                             static_cast<hipStream_t>(copy_stream));
+  } catch (...) {
+    return MOE_ERR_HOST_ALLOC;
+  }
   {
     void* pin = nullptr;
     void* pin_dev = nullptr;
