@@ -636,11 +636,12 @@ def measure_cache(args, m, wl, dev, n_layers=4, calls=48):
     call waits for its routing anyway):
       resident   moe_forward with the layer's experts on the device (no cache);
       hit        every expert resident in the cache (slots >= all layers' experts);
-      miss       the cache flushed before every call: top_k copies per call;
+      miss       the cache flushed before every call: every expert is read from
+                 host memory by the kernels;
       no_prefetch  2 * top_k slots, no prefetch: each call's experts were
                  evicted by the two layers before it, so all miss;
       prefetch   2 * top_k slots, depth 1, shift 1: each call's experts were
-                 copied in during the previous call;
+                 predicted by the previous call and copied in meanwhile;
       prefetch_random  as prefetch, but the routing of each call is the
                  router's own (random) choice, so the prediction rarely holds.
     """
@@ -670,7 +671,7 @@ def measure_cache(args, m, wl, dev, n_layers=4, calls=48):
     copy = torch.cuda.Stream()
 
     def run(n_slots, depth, biased, flush=False, resident=False):
-        region = torch.empty(m.moe_cache_region_bytes(shape, n_slots), dtype=torch.uint8, device=dev)
+        region = torch.empty(m.moe_cache_region_bytes(shape, n_layers, n_slots), dtype=torch.uint8, device=dev)
         c = m.moe_cache_create(shape, host, region, n_slots, depth, 1, copy)
         try:
             def call(i):
@@ -684,10 +685,14 @@ def measure_cache(args, m, wl, dev, n_layers=4, calls=48):
                     m.moe_cache_flush(c)
                 m.moe_forward_cached(c, l, shape, xs[i], one("router_w", l), b, one("ws_gate", l), one("ws_up", l),
                                      one("ws_down", l), out, ws)
-            for i in range(2 * n_layers):      # warm-up: fills the cache for the hit scenario
-                call(i)
-            torch.cuda.synchronize()
-            copy.synchronize()
+            # warm-up: three rounds over the layers, the host reading each round's routing (an
+            # expert is copied in at its second miss), so the hit scenario starts all resident
+            for r in range(3):
+                for i in range(n_layers):
+                    call(r * n_layers + i)
+                torch.cuda.synchronize()
+                copy.synchronize()
+                m.moe_cache_stats(c)
             m.moe_cache_stats(c, reset=True)
             t0 = time.perf_counter()
             for i in range(calls):

@@ -85,9 +85,7 @@ enum {
   MOE_ERR_WORKSPACE = -5,  /* workspace smaller than moe_workspace_size() */
   MOE_ERR_HIP = -6,        /* a HIP launch failed (hipGetLastError) */
   MOE_ERR_TOO_LARGE = -7,  /* moe_forward_noalloc: the shape needs more workspace than its
-                              static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES);
-                              moe_forward_cached: a pass can engage more experts than
-                              the cache has slots */
+                              static scratch array holds (MOE_NOALLOC_SCRATCH_BYTES) */
   MOE_ERR_NOT_PINNED = -8, /* moe_cache_create: a host expert stack is not pinned host memory */
   MOE_ERR_HOST_ALLOC = -9  /* moe_cache_create: its host bookkeeping could not be allocated */
 };
@@ -305,26 +303,33 @@ int moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* router_
  *
  * The routed experts of n_layers layers stay in pinned host memory (in the
  * layouts above, one stack per matrix and layer).  A device region the caller
- * allocates holds n_slots expert slots shared by all layers.  Each decode
- * pass of moe_forward_cached routes on the GPU, reads the engaged experts back
- * (the call waits for that), and looks each up in the cache: a hit uses the
- * resident copy, a miss copies the expert into the least recently used slot
- * that the pass does not need, on copy_stream.  The expert launches wait for
- * those copies only.  Then, for each of the next prefetch_depth layers d
- * (cyclically: after the last layer comes layer 0 of the next token), the
- * experts (e + d * prefetch_shift) mod E of every engaged expert e are
- * copied in ahead of time on copy_stream, overlapping with the compute of
- * this layer and the routing of the next; the page's example predicts, from
- * experts 3 and 7 in one layer, experts 4 and 8 in the next (shift 1).  A
- * slot is overwritten only after every launch that reads it has finished.
+ * allocates holds n_slots expert slots shared by all layers and a slot map.
+ * In moe_forward_cached the expert kernels look each engaged expert up in the
+ * map: a resident expert is read from its slot (HBM), any other straight from
+ * the host stacks over PCIe -- the same bytes, so the output never depends on
+ * what is resident.  The host learns each pass's engaged experts from a list
+ * the GPU writes into pinned memory after the pass; it counts hits and misses,
+ * copies an expert missed a second time (since it was last resident) into the
+ * least recently used slot on copy_stream,
+ * and, for each of the next prefetch_depth layers d (cyclically: after the
+ * last layer comes layer 0 of the next token), copies in the experts
+ * (e + d * prefetch_shift) mod E of every engaged e.  The page's example
+ * predicts, from experts 3 and 7 in one layer, experts 4 and 8 in the next
+ * (shift 1).  With prefetch_depth 0 no call waits for anything on the host;
+ * with prefetching each call waits, after enqueueing its launches, for its
+ * own engaged experts (the GPU finishes the pass meanwhile) and starts the
+ * predicted copies at once, and a pass waits for the copies of its own
+ * layer's experts that are in flight.  Slot-map changes run on the compute
+ * stream, so no launch sees a slot change under it; a slot is overwritten
+ * only after every launch that could read its old contents has finished.
  *
- * Results are those of moe_forward on the decode path (MOE_PATH_DECODE) with
- * the same weights on the device: the same kernels read the same bytes.
- * Shared experts and router weights stay device-resident and are passed per
- * call.  A cache is used from one host thread and one compute stream at a
- * time; calls through it synchronise that stream once per decode pass.  The
- * library allocates no device memory; moe_cache_create allocates the host
- * bookkeeping and HIP events, which moe_cache_destroy frees.
+ * Results equal moe_forward on the decode path (MOE_PATH_DECODE) with the
+ * same weights on the device up to the order of fp32 sums (bit for bit when
+ * both take the same launch structure).  Shared experts and router weights
+ * stay device-resident and are passed per call.  A cache is used from one
+ * host thread and one compute stream at a time.  The library allocates no
+ * device memory; moe_cache_create allocates the host bookkeeping, HIP events
+ * and a pinned host ring of 64 active lists, which moe_cache_destroy frees.
  */
 typedef struct {
   const void* w_gate;   /* (host, pinned) [E, I, H] in w_dtype's layout */
@@ -343,17 +348,19 @@ typedef struct {
 
 typedef struct moe_expert_cache moe_expert_cache_t;
 
-/* Device bytes of a cache region of n_slots slots for the shape's routed
- * experts (its T and path are ignored). Host call. */
-int moe_cache_region_bytes(const moe_shape_t* s, int32_t n_slots, size_t* bytes /* (host) */);
+/* Device bytes of a cache region for n_layers layers and n_slots slots of
+ * the shape's routed experts (its T and path are ignored); 1 <= n_layers <=
+ * 65536, 1 <= n_slots <= 65536. Host call. */
+int moe_cache_region_bytes(const moe_shape_t* s, int32_t n_layers, int32_t n_slots, size_t* bytes /* (host) */);
 
 /* Creates a cache over `layers` (host array of n_layers entries, each stack
- * pinned: MOE_ERR_NOT_PINNED otherwise) in `region` (device, 256-byte
- * aligned, at least moe_cache_region_bytes; it must outlive the cache).
- * 1 <= n_slots <= 65536; 0 <= prefetch_depth < n_layers (0: no prefetch);
+ * pinned and 16-byte aligned: MOE_ERR_NOT_PINNED / MOE_ERR_ALIGN otherwise)
+ * in `region` (device, 256-byte aligned, at least moe_cache_region_bytes; it
+ * must outlive the cache).  0 <= prefetch_depth < n_layers (0: no prefetch);
  * prefetch_shift is any integer (taken mod E).  copy_stream: a hipStream_t
- * of default priority, not the compute stream.  Nothing is copied yet.
- * *out receives the handle (host). */
+ * of default priority, not the compute stream.  The map starts empty (the
+ * call waits until it is cleared); nothing is copied yet.  *out receives the
+ * handle (host). */
 int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_experts_t* layers,
                      void* region, size_t region_bytes, int32_t n_slots, int32_t prefetch_depth,
                      int32_t prefetch_shift, void* copy_stream, moe_expert_cache_t** out);
@@ -363,20 +370,24 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
 int moe_cache_destroy(moe_expert_cache_t* c);
 
 /* Layer `layer`'s forward, as moe_forward with the routed experts read from
- * the cache.  s must equal the shape given to moe_cache_create except for T
- * and path (the call always takes the decode path); workspace as
- * moe_workspace_size for s with path MOE_PATH_DECODE.  Each pass of at most
- * 64 tokens needs n_slots >= min(E, tokens * top_k) (MOE_ERR_TOO_LARGE,
- * checked before anything is enqueued).  Synchronises `stream` once per pass. */
+ * the cache or from host memory.  s must equal the shape given to
+ * moe_cache_create except for T and path (the call always takes the decode
+ * path); workspace as moe_workspace_size for s with path MOE_PATH_DECODE.
+ * Any cache size works (a pass may engage more experts than there are
+ * slots).  With prefetch_depth > 0 the call returns once its pass's engaged
+ * experts are known (after the pass has finished on the GPU). */
 int moe_forward_cached(moe_expert_cache_t* c, int32_t layer, const moe_shape_t* s, const void* x,
                        const void* router_w, const float* router_b,
                        const void* ws_gate, const void* ws_up, const void* ws_down,
                        void* out, void* workspace, size_t ws_bytes, void* stream);
 
-/* Counters since creation or the last reset (reset != 0 zeroes them after the read). */
+/* Counters since creation or the last reset (reset != 0 zeroes them after
+ * the read), over the passes whose engaged experts have reached the host
+ * (all of them once the compute stream has been synchronised). */
 int moe_cache_stats(moe_expert_cache_t* c, moe_cache_stats_t* out /* (host) */, int32_t reset);
 
-/* Forgets every resident expert (the next lookups miss); copies in flight still complete. */
+/* Forgets every resident expert: the next call's launches find none (the map
+ * is cleared on its stream first); copies in flight still complete. */
 int moe_cache_flush(moe_expert_cache_t* c);
 
 /* The hipError_t value behind the most recent MOE_ERR_HIP returned to the

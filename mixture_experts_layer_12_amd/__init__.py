@@ -110,7 +110,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_probe_read.restype = ctypes.c_int
     lib.moe_probe_mfma_bf16.argtypes = [i32, vp, P(ctypes.c_double), vp]
     lib.moe_probe_mfma_bf16.restype = ctypes.c_int
-    lib.moe_cache_region_bytes.argtypes = [P(moe_shape_t), i32, P(sz)]
+    lib.moe_cache_region_bytes.argtypes = [P(moe_shape_t), i32, i32, P(sz)]
     lib.moe_cache_region_bytes.restype = ctypes.c_int
     lib.moe_cache_create.argtypes = [P(moe_shape_t), i32, P(moe_host_experts_t), vp, sz, i32, i32, i32, vp,
                                      P(vp)]
@@ -318,9 +318,9 @@ def moe_forward_profiled(shape: moe_shape_t, x, router_w, router_b, w_gate, w_up
     return rc
 
 
-def moe_cache_region_bytes(shape: moe_shape_t, n_slots: int) -> int:
+def moe_cache_region_bytes(shape: moe_shape_t, n_layers: int, n_slots: int) -> int:
     n = ctypes.c_size_t(0)
-    rc = load_library().moe_cache_region_bytes(ctypes.byref(shape), n_slots, ctypes.byref(n))
+    rc = load_library().moe_cache_region_bytes(ctypes.byref(shape), n_layers, n_slots, ctypes.byref(n))
     if rc:
         raise MoeError(rc, "moe_cache_region_bytes")
     return n.value

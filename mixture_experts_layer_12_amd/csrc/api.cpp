@@ -281,8 +281,7 @@ moe::RouterArgs router_args(const moe_shape_t* s, int T, const void* x, const vo
 //    selection): the router launch computes the logits only, and every routed
 //    gate/up work-group selects and dispatches in its prologue (one launch
 //    fewer on the critical path; larger grids would repeat a costly selection
-//    too often).  Never with a hook, which needs the routing before the
-//    expert launches.
+//    too often).
 //  logit_parts: few logit tiles are split over 4 work-groups each (partial
 //    planes) to spread the router read.
 //  shared_in_router: with route_in_gu and split logits, the shared experts'
@@ -291,7 +290,7 @@ struct PassPlan {
   bool route_in_gu, shared_in_router;
   int logit_parts;
 };
-PassPlan pass_plan(const moe_shape_t* s, int Tc, bool hooked) {
+PassPlan pass_plan(const moe_shape_t* s, int Tc) {
   const int n_routed_slots = std::min(s->E, Tc * s->top_k);
   const int S = s->n_shared, Is = S > 0 ? s->I_shared : 0;
   const long n_gu_rt = (std::max(s->I, Is) + 15) / 16;
@@ -299,7 +298,7 @@ PassPlan pass_plan(const moe_shape_t* s, int Tc, bool hooked) {
   const int nblocks = ((s->E + 15) / 16) * ((Tc + 15) / 16);
   PassPlan p{};
   const bool tiny = long(Tc) * s->E <= kTinySelection && (s->w_dtype == MOE_BF16 || s->w_dtype == MOE_F32);
-  p.route_in_gu = !hooked && Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
+  p.route_in_gu = Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
                   gu_groups <= (tiny ? kRouteInGateUpMaxGroupsTiny : kRouteInGateUpMaxGroups);
   p.logit_parts = (nblocks < 64 && (p.route_in_gu || nblocks > 1)) ? 4 : 1;
   p.shared_in_router = p.route_in_gu && S > 0 && p.logit_parts == 4;
@@ -319,9 +318,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failure";
-    case MOE_ERR_TOO_LARGE:
-      return "shape needs more workspace than the static scratch of moe_forward_noalloc, or more experts per "
-             "pass than the expert cache has slots";
+    case MOE_ERR_TOO_LARGE: return "shape needs more workspace than the static scratch of moe_forward_noalloc";
     case MOE_ERR_NOT_PINNED: return "host expert stack is not pinned host memory";
     case MOE_ERR_HOST_ALLOC: return "host memory for the expert cache's bookkeeping could not be allocated";
     default: return "unknown error code";
@@ -371,7 +368,7 @@ int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t) {
   t->inv = L.inv;
   t->active = L.active;
   t->status = L.path == MOE_PATH_DECODE_FUSED ? L.error : 0;
-  const PassPlan plan = pass_plan(s, last, false);
+  const PassPlan plan = pass_plan(s, last);
   t->route_in_gateup = L.path == MOE_PATH_DECODE && last > 0 && plan.route_in_gu;
   t->shared_in_router = L.path == MOE_PATH_DECODE && last > 0 && plan.shared_in_router;
   return MOE_OK;
@@ -533,6 +530,8 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     d.dn_count = d.n_routed_slots + d.S <= kEpilogueMaxSlots ? reinterpret_cast<unsigned*>(ws + L.dn_count) : nullptr;
     const int n_gu_rt = (std::max(s->I, d.Is) + 15) / 16;
     d.n_row_tiles = n_gu_rt;
+    if (hook)
+      if (int e = hook->before_pass(d, st)) return e;
     sev.mark(st);
     if (fused) {
       moe::FusedArgs f = fused_plan(s, Tc);
@@ -549,7 +548,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       continue;
     }
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
-    const PassPlan plan = pass_plan(s, Tc, hook != nullptr);
+    const PassPlan plan = pass_plan(s, Tc);
     const bool pro = plan.route_in_gu;
     ra.logit_parts = plan.logit_parts;
     if (d.dn_count) {             // the router launch clears the down launch's arrival counters
@@ -566,13 +565,11 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
         return e;
       sev.mark(st);
     }
-    if (hook)
-      if (int e = hook->before_experts(d, st)) return e;
     if (int e = hip_status(moe::launch_decode(d, s->w_dtype, s->x_dtype, s->router_dtype, n_gu_rt, st,
                                               events ? &sev : nullptr)))
       return e;
     if (hook)
-      if (int e = hook->after_experts(st)) return e;
+      if (int e = hook->after_pass(d, st)) return e;
   }
   return MOE_OK;
 }

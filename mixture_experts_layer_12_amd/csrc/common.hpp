@@ -358,26 +358,43 @@ struct DecodeArgs {
   RouterArgs route;     // ... with these arguments (logits in route.rb.logits)
   int shared_in_router; // with route_in_gu: the decode launches start with one for the router logits and
                         // the shared experts' gate/up together; the gate/up launch covers routed slots only
-  const int32_t* active_w;  // null: routed expert e's matrices are matrix e of wg/wu/wd (E of them);
-                            // else entry 1 + j is the matrix of the j-th active expert (an expert
-                            // cache's slot) in stacks of E_w matrices; needs route_in_gu == 0
+  // Expert cache: null, or the slot of each routed expert e in the cache's stacks wg/wu/wd
+  // (E_w matrices each), -1 for an expert that is not resident, whose matrices are then read
+  // from the host stacks wg_h/wu_h/wd_h (E matrices, device-mapped pinned host memory).
+  const int32_t* slot_of;
+  const uint8_t* wg_h; const uint8_t* wu_h; const uint8_t* wd_h;
   int E_w;
 };
 
-// Segments of one launch_gather_copy (seven experts of three quantised matrices).
-constexpr int kCopyMaxSegs = 42;
+// Segments of one launch_gather_copy (sixteen experts of three quantised
+// matrices; the list is a kernel argument of 3 KiB).
+constexpr int kCopyMaxSegs = 96;
+// Slot-map entries one launch_map_update writes.
+constexpr int kMapMaxPairs = 240;
 
-// Matrices in the routed stacks (E, or the slots of an expert cache).
-__device__ __forceinline__ long routed_mats(const DecodeArgs& a) { return a.active_w ? a.E_w : a.E; }
+// Where routed expert e's matrices are: matrix `idx` of stacks of `n_mat`
+// matrices, in the host stacks when `host`.
+struct RoutedAt {
+  int idx;
+  long n_mat;
+  bool host;
+};
+template <bool COH>
+__device__ __forceinline__ RoutedAt routed_at(const DecodeArgs& a, int e) {
+  if (!a.slot_of) return RoutedAt{e, a.E, false};
+  const int s = ld_i32<COH>(a.slot_of + e);
+  return s >= 0 ? RoutedAt{s, a.E_w, false} : RoutedAt{e, a.E, true};
+}
 
-// Host callbacks around the expert launches of each decode pass (the expert
-// cache): before_experts runs once the pass's routing is enqueued and may
-// point the routed stacks elsewhere (DecodeArgs wg/wu/wd, active_w, E_w);
-// after_experts runs once the pass's expert launches are enqueued.  A
-// nonzero return ends the call with that code.
+// Host callbacks of an expert cache around each decode pass: before_pass
+// runs before the pass's first launch and points the routed stacks at the
+// cache (DecodeArgs wg/wu/wd, slot_of, wg_h/wu_h/wd_h, E_w), enqueueing its
+// slot-map updates on the stream first; after_pass runs once the pass's
+// launches are enqueued (d.active then holds the pass's active list in stream
+// order).  A nonzero return ends the call with that code.
 struct DecodeHook {
-  virtual int before_experts(DecodeArgs& d, hipStream_t st) = 0;
-  virtual int after_experts(hipStream_t st) = 0;
+  virtual int before_pass(DecodeArgs& d, hipStream_t st) = 0;
+  virtual int after_pass(const DecodeArgs& d, hipStream_t st) = 0;
   virtual ~DecodeHook() = default;
 };
 

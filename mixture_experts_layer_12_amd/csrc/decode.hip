@@ -269,7 +269,7 @@ hipError_t launch_decode_shared(const DecodeArgs& a, int wdt, int xdt, hipStream
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark) {
   if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
-  if (a.active_w && (a.route_in_gu || a.E_w < 1)) return hipErrorInvalidValue;
+  if (a.slot_of && (a.E_w < 1 || !a.wg_h || !a.wu_h || !a.wd_h)) return hipErrorInvalidValue;
   if (a.shared_in_router && (!a.route_in_gu || a.S == 0 || a.route.logit_parts != 4)) return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
@@ -366,6 +366,43 @@ __global__ void __launch_bounds__(256) export_list_kernel(const int32_t* src, in
 hipError_t launch_export_list(const int32_t* src, int n, int32_t* dst, unsigned long long* flag,
                               unsigned long long tag, hipStream_t st) {
   hipLaunchKernelGGL(export_list_kernel, dim3(1), dim3(256), 0, st, src, n, dst, flag, tag);
+  return hipGetLastError();
+}
+
+// Slot-map updates of the expert cache, in stream order: entry idx[i] of
+// `map` becomes val[i] (indices distinct within one launch), or every entry
+// becomes -1.
+struct MapPairs {
+  int n;
+  int32_t idx[kMapMaxPairs];
+  int32_t val[kMapMaxPairs];
+};
+
+__global__ void __launch_bounds__(256) map_update_kernel(int32_t* map, MapPairs p) {
+  for (int i = threadIdx.x; i < p.n; i += blockDim.x) map[p.idx[i]] = p.val[i];
+}
+
+__global__ void __launch_bounds__(256) map_clear_kernel(int32_t* map, long n) {
+  for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += long(gridDim.x) * blockDim.x) map[i] = -1;
+}
+
+hipError_t launch_map_update(int32_t* map, const int32_t* idx, const int32_t* val, int n, hipStream_t st) {
+  if (n < 0 || n > kMapMaxPairs) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  MapPairs p;
+  p.n = n;
+  for (int i = 0; i < n; ++i) {
+    p.idx[i] = idx[i];
+    p.val[i] = val[i];
+  }
+  hipLaunchKernelGGL(map_update_kernel, dim3(1), dim3(256), 0, st, map, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_map_clear(int32_t* map, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long blocks = std::min<long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(map_clear_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, map, n);
   return hipGetLastError();
 }
 

@@ -468,22 +468,26 @@ __device__ __forceinline__ bool gateup_item(const DecodeArgs a, int rt, int slot
   const uint8_t* bg = routed ? a.wg : a.sg;
   const uint8_t* bu = routed ? a.wu : a.su;
   const int N = routed ? a.I : a.Is;
-  const long n_mat = routed ? routed_mats(a) : a.S;
-  int e, ew, n_e, hrow0, seg = 0;     // ew: the matrix of expert e in the stacks
+  long n_mat = routed ? a.E : a.S;
+  int e, ew, n_e, hrow0, seg = 0;     // ew: the matrix of expert e in its stacks
   if (routed) {
     if constexpr (PRO) {
       if (slot >= R->s_na[0]) return false;
-      e = ew = R->s_e[slot];
+      e = R->s_e[slot];
       n_e = R->s_cnt[slot];
       seg = hrow0 = R->s_cpre[slot];
     } else {
       if (slot >= ld_i32<COH>(a.active)) return false;
       e = ld_i32<COH>(a.active + 1 + slot);
-      ew = a.active_w ? ld_i32<COH>(a.active_w + 1 + slot) : e;
       n_e = ld_i32<COH>(a.counts + e);
       seg = ld_i32<COH>(a.offsets + e);
       hrow0 = ld_i32<COH>(a.cprefix + e);
     }
+    const RoutedAt w = routed_at<COH>(a, e);    // an expert cache's slot, or the host stacks
+    ew = w.idx;
+    n_mat = w.n_mat;
+    bg = w.host ? a.wg_h : bg;
+    bu = w.host ? a.wu_h : bu;
   } else {
     e = ew = slot - a.n_routed_slots;
     n_e = a.T;
@@ -712,14 +716,17 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
   const bool routed = slot < a.n_routed_slots;
   const uint8_t* base = routed ? a.wd : a.sd;     // selects, as in gateup_item
   const int K = routed ? a.I : a.Is;
-  const long n_mat = routed ? routed_mats(a) : a.S;
-  int e, ew, n_e, hrow0;              // ew: the matrix of expert e in the stacks
+  long n_mat = routed ? a.E : a.S;
+  int e, ew, n_e, hrow0;              // ew: the matrix of expert e in its stacks
   if (routed) {
     if (slot >= ld_i32<COH>(a.active)) return false;
     e = ld_i32<COH>(a.active + 1 + slot);
-    ew = a.active_w ? ld_i32<COH>(a.active_w + 1 + slot) : e;
     n_e = ld_i32<COH>(a.counts + e);
     hrow0 = ld_i32<COH>(a.cprefix + e);
+    const RoutedAt w = routed_at<COH>(a, e);    // an expert cache's slot, or the host stacks
+    ew = w.idx;
+    n_mat = w.n_mat;
+    base = w.host ? a.wd_h : base;
   } else {
     e = ew = slot - a.n_routed_slots;
     n_e = a.T;
@@ -870,7 +877,7 @@ __device__ __forceinline__ void down_one_item(const DecodeArgs a, int rt, uint8_
   int el = ld_i32<false>(a.active + 1 + jl);
   el = el < 0 ? 0 : (el >= a.E ? a.E - 1 : el);   // entries past A are stale
   const int hl = ld_i32<false>(a.cprefix + el);
-  const int wl = a.active_w ? ld_i32<false>(a.active_w + 1 + jl) : el;   // its matrix in the stacks
+  const int sl = a.slot_of ? ld_i32<false>(a.slot_of + el) : el;   // an expert cache's slot (-1: host stacks)
   // this wave's steps of every slot, all loads in flight at once
   const int nsteps = n_steps<WT>(K);
   const int s0 = wave * nsteps / 4, len = (wave + 1) * nsteps / 4 - s0;
@@ -882,9 +889,11 @@ __device__ __forceinline__ void down_one_item(const DecodeArgs a, int rt, uint8_
       const int j = i / len, st = s0 + i % len;
       const bool routed = j < a.k;
       if (routed && j >= A) continue;
+      const int ej = __builtin_amdgcn_readlane(el, j), sj = __builtin_amdgcn_readlane(sl, j);
+      const bool host = a.slot_of && sj < 0, cached = a.slot_of && sj >= 0;
       RowPtr<WT> rw;
-      rw.init(routed ? a.wd : a.sd, routed ? routed_mats(a) : a.S, H, K,
-              routed ? __builtin_amdgcn_readlane(wl, j) : j - a.k, rt * 16 + (lane & 15));
+      rw.init(routed ? (host ? a.wd_h : a.wd) : a.sd, routed ? (cached ? long(a.E_w) : long(a.E)) : long(a.S), H, K,
+              routed ? (cached ? sj : ej) : j - a.k, rt * 16 + (lane & 15));
       af[i] = load_a<WT>(rw, st, g, K);
     }
   }

@@ -228,25 +228,26 @@ def _stack_bytes(w_dtype, n, N, K):
 
 
 @pytest.mark.parametrize("w_dtype", [0, 1, 2, 3, 4])
-@pytest.mark.parametrize("n_slots", [1, 5, 64])
-def test_cache_region_bytes(m, w_dtype, n_slots):
+@pytest.mark.parametrize("n_layers, n_slots", [(1, 1), (3, 5), (48, 64)])
+def test_cache_region_bytes(m, w_dtype, n_layers, n_slots):
     up = lambda v: -(-v // 256) * 256  # noqa: E731
     s = _shape(m, T=1, H=256, E=16, I=96, top_k=4, w_dtype=w_dtype)
-    want = 0
+    want = up(4 * n_layers * s.E)                   # the slot map
     for N, K in ((s.I, s.H), (s.I, s.H), (s.H, s.I)):
         want += up(_stack_bytes(w_dtype, n_slots, N, K))
-    assert m.moe_cache_region_bytes(s, n_slots) == want
+    assert m.moe_cache_region_bytes(s, n_layers, n_slots) == want
 
 
 def test_cache_argument_errors_on_the_host(m):
     lib = m.load_library()
     s = _shape(m, T=1)
     n = ctypes.c_size_t(0)
-    assert lib.moe_cache_region_bytes(ctypes.byref(s), 0, ctypes.byref(n)) == m.MOE_ERR_SHAPE
-    assert lib.moe_cache_region_bytes(ctypes.byref(_shape(m, H=100)), 4, ctypes.byref(n)) == m.MOE_ERR_SHAPE
+    assert lib.moe_cache_region_bytes(ctypes.byref(s), 1, 0, ctypes.byref(n)) == m.MOE_ERR_SHAPE
+    assert lib.moe_cache_region_bytes(ctypes.byref(s), 0, 4, ctypes.byref(n)) == m.MOE_ERR_SHAPE
+    assert lib.moe_cache_region_bytes(ctypes.byref(_shape(m, H=100)), 1, 4, ctypes.byref(n)) == m.MOE_ERR_SHAPE
     h = ctypes.c_void_p(None)
     layer = m.moe_host_experts_t(None, None, None)
-    big = m.moe_cache_region_bytes(s, 4)
+    big = m.moe_cache_region_bytes(s, 1, 4)
     buf = (ctypes.c_uint8 * (big + 256))()
     region = (ctypes.addressof(buf) + 255) // 256 * 256
     # no layers / no region / no handle
