@@ -310,8 +310,8 @@ int moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* router_
  * what is resident.  The host learns each pass's engaged experts from a list
  * the GPU writes into pinned memory after the pass; it counts hits and misses,
  * copies an expert missed a second time (since it was last resident) into the
- * least recently used slot on copy_stream,
- * and, for each of the next prefetch_depth layers d (cyclically: after the
+ * least recently used slot on copy_stream, and, for each of the next
+ * prefetch_depth layers d (cyclically: after the
  * last layer comes layer 0 of the next token), copies in the experts
  * (e + d * prefetch_shift) mod E of every engaged e.  The page's example
  * predicts, from experts 3 and 7 in one layer, experts 4 and 8 in the next
@@ -340,10 +340,10 @@ typedef struct {
 typedef struct {
   uint64_t lookups;        /* engaged (pass, expert) pairs looked up */
   uint64_t hits;           /* ... found resident (prefetched ones included) */
-  uint64_t misses;         /* ... copied in on demand */
+  uint64_t misses;         /* ... not resident: read from host memory by the kernels */
   uint64_t prefetches;     /* experts copied in ahead of time */
   uint64_t prefetch_hits;  /* hits on a prefetched expert, its first use */
-  uint64_t bytes_copied;   /* host-to-device bytes enqueued (misses and prefetches) */
+  uint64_t bytes_copied;   /* host-to-device bytes enqueued (copies after misses, and prefetches) */
 } moe_cache_stats_t;
 
 typedef struct moe_expert_cache moe_expert_cache_t;
@@ -365,8 +365,9 @@ int moe_cache_create(const moe_shape_t* s, int32_t n_layers, const moe_host_expe
                      void* region, size_t region_bytes, int32_t n_slots, int32_t prefetch_depth,
                      int32_t prefetch_shift, void* copy_stream, moe_expert_cache_t** out);
 
-/* Waits for the cache's copies, then frees its bookkeeping and events.  The
- * caller must have synchronised every stream that ran moe_forward_cached. */
+/* Waits for the cache's copies, then frees its bookkeeping, events and
+ * pinned ring.  The caller must have synchronised the compute stream that
+ * ran moe_forward_cached (its last launches write into the ring). */
 int moe_cache_destroy(moe_expert_cache_t* c);
 
 /* Layer `layer`'s forward, as moe_forward with the routed experts read from
