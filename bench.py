@@ -525,7 +525,7 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
     for e in evs:
         hip.destroy(e)
     avg = [sum(s_[j] for s_ in stage) / len(stage) for j in range(n_ev - 1)]
-    names = (["router", "prefill_gateup", "prefill_down", "cast"] if prefill
+    names = (["router", "prefill_gateup", "prefill_down", "combine"] if prefill
              else (["decode_fused"] if fused else ["router", "decode_gateup", "decode_down"]))
     log("[bench] stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, avg)))
 

@@ -195,8 +195,9 @@ int moe_forward(const moe_shape_t* s, const void* x, const void* router_w, const
  * events[0] before the first launch, events[i] after launch i.  Launches of
  * one pass: decode path 1 router+dispatch, 2 gate/up, 3 down+combine;
  * single-launch decode 1 the whole pass;
- * prefill path 1 router+dispatch, 2 gate/up GEMM, 3 down GEMM + combine,
- * 4 cast.  A decode call with T > 64 makes several passes; the events then
+ * prefill path 1 router+dispatch, 2 gate/up GEMM, 3 down GEMM (weighted
+ * partial rows), 4 combine (fixed-order sum per token, cast to the output
+ * dtype).  A decode call with T > 64 makes several passes; the events then
  * hold the last pass.  Entries beyond n_events, or NULL entries, are skipped.
  * Returns MOE_ERR_NULL when events is NULL or n_events < 1; otherwise as
  * moe_forward.  Meant for stage timing (hipEventElapsedTime). */

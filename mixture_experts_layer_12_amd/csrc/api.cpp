@@ -20,6 +20,7 @@ hipError_t launch_router(const RouterArgs& a, int rdt, int xdt, int NW, hipStrea
 hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_gu_row_tiles, hipStream_t st,
                          StageMarker* mark);
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark);
+int prefill_k_split(int capacity, int S, int t_pad, int H, int nmax);
 hipError_t launch_decode_fused(const FusedArgs& f, int wdt, int xdt, hipStream_t st);
 hipError_t launch_sparse(const SparseArgs& a, int wdt, int xdt, hipStream_t st, StageMarker* mark);
 hipError_t launch_sparse_route_select(const RouterArgs& ra, const SparseArgs& a, int rdt, int xdt, hipStream_t st);
@@ -55,7 +56,8 @@ struct Layout {
   int tile_m;          // padding multiple of the expert-sorted order
   int cap, n_tiles;    // sorted-order capacity and tiles for Tr tokens
   size_t logits, topk_ids, topk_w, counts, offsets, cprefix, active, sorted_ids, tile_expert, inv;
-  size_t h, partials, acc;
+  size_t h, partials;
+  int pf_ksplit;        // prefill: k ranges of the down GEMM (partial planes)
   size_t dn_count;     // multi-launch decode: down arrival counters [H / 16, rounded up to 4]
   size_t flags, error;  // single-launch decode: completion flags [n_items], error tag
   long n_items;
@@ -221,7 +223,9 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     const long rows = long(L.cap) + long(S) * L.t_pad;
     L.h_plane = rows * L.h_stride;
     L.h = take(size_t(L.h_plane) * 2);
-    L.acc = take(size_t(T) * H * 4);
+    // routing-weighted rows of the down GEMM: one plane per k range
+    L.pf_ksplit = moe::prefill_k_split(L.cap, S, L.t_pad, H, std::max(I, Is));
+    L.partials = take(size_t(L.pf_ksplit) * rows * H * 4);
   }
   L.total = off;
   return L;
@@ -458,8 +462,6 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     StageEvents sev{events, n_events};
     sev.mark(st);
     moe::RouterArgs ra = router_args(s, s->T, x, router_w, router_b, rb, L.tile_m);
-    ra.zero_f32 = reinterpret_cast<float*>(ws + L.acc);
-    ra.zero_n = long(s->T) * s->H;
     const int nblocks = ra.n_row_tiles * ra.n_col_tiles;
     if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st))) return e;
     sev.mark(st);
@@ -475,7 +477,9 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     p.tile_expert = rb.tile_expert; p.sorted_ids = rb.sorted_ids; p.topk_w = rb.topk_w; p.offsets = rb.offsets;
     p.h = reinterpret_cast<uint16_t*>(ws + L.h);
     p.h_stride = L.h_stride;
-    p.acc = reinterpret_cast<float*>(ws + L.acc);
+    p.partials = reinterpret_cast<float*>(ws + L.partials);
+    p.part_plane = (long(L.cap) + long(p.S) * L.t_pad) * s->H;
+    p.inv = rb.inv;
     p.out = out;
     return hip_status(moe::launch_prefill(p, s->x_dtype, st, events ? &sev : nullptr));
   }

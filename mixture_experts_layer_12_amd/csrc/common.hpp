@@ -447,11 +447,13 @@ struct PrefillArgs {
   int T, H, E, I, k, S, Is;
   int capacity, tile_m, t_pad;        // routed rows, padding tile, shared rows per expert
   int n_row_tiles, n_col_tiles;
-  int k_split;           // down projection: k ranges per output tile (partial sums add up in acc)
+  int k_split;           // down projection: k ranges per output tile (one partial plane each)
   const int32_t* tile_expert; const int32_t* sorted_ids; const float* topk_w; const int32_t* offsets;
   uint16_t* h;           // [capacity + S*t_pad, h_stride] bf16
   int h_stride;
-  float* acc;            // [T, H] fp32
+  float* partials;       // [k_split][capacity + S*t_pad, H] fp32 routing-weighted rows of the down GEMM
+  long part_plane;       // elements per partial plane
+  const int32_t* inv;    // [T*k] position of each assignment in the sorted order
   void* out;
 };
 

@@ -11,8 +11,12 @@
 //                 they are staged into LDS; the epilogue applies silu(g) * u
 //                 and stores bf16 activations;
 //   down GEMM     one launch; its epilogue multiplies by the routing weight
-//                 and adds into an fp32 [T, H] accumulator (the combine);
-//   cast          fp32 accumulator -> output dtype.
+//                 and stores fp32 partial rows (one per sorted row and k
+//                 range);
+//   combine       each token's routed and shared rows added in one fixed
+//                 order and cast to the output dtype (deterministic: no
+//                 float atomics, so the bits do not depend on which tile
+//                 finished first).
 //
 // Both GEMMs run one work-group per 256 x 256 output tile (256 sorted token
 // rows by 256 weight rows: for gate/up 128 gate + 128 up rows of the same
@@ -476,19 +480,24 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_gateup_kernel(PrefillAr
 }
 
 // ------------------------------------------------------------------ down --
+
+// k per range when a reduction of K is cut into ks ranges: whole 64-deep
+// stages except maybe at the end; ranges that start at or past K are empty.
+__host__ __device__ inline int down_k_chunk(int K, int ks) { return (K + 64 * ks - 1) / (64 * ks) * 64; }
+
 // Tile: 256 sorted rows x 256 hidden columns.  Staged A rows are activation
 // rows (sorted order, contiguous), B rows the down-projection rows of the
 // hidden outputs.  Full tile: wave (wm, wn) multiplies rows [128 wm, +128)
 // with columns [128 wn, +128).  Half tile (rows [0, 128) only): wave w
 // multiplies them with columns [64 w, +64).  Register q of a lane holds one
 // hidden column of 16 sorted rows, which it scales by the routing weight
-// and adds into the fp32 accumulator with hardware float atomics (lanes
+// and stores into the sorted row of this k range's partial plane (lanes
 // 0-31 cover 32 consecutive columns of one row).  Each wave stages a
 // quarter of each operand.
 
 template <bool HALF>
 __device__ __forceinline__ void down_tile(const PrefillArgs& a, uint16_t* smem, const uint16_t* Wd, int K, int rt,
-                                          int n_routed_tiles, int n0, int k_begin, int k_len) {
+                                          int n_routed_tiles, int n0, int kr, int k_begin, int k_len) {
   constexpr int NI = 4, NJ = HALF ? 2 : 4, NF = HALF ? 4 : 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(int(tid >> 6));
@@ -542,8 +551,9 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& a, uint16_t* smem, 
     }
   }
 
-  // epilogue: acc[t][n] += w * y
+  // epilogue: partial row (plane kr, sorted row) = w * y
   const int l32 = lane & 31, hi = lane >> 5;
+  float* const prow = a.partials + size_t(kr) * a.part_plane + size_t(hrow0) * H;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn * WC + j * 32 + l32;
@@ -553,8 +563,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& a, uint16_t* smem, 
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int m = wm * 128 + i * 32 + (q >> 2) * 8 + hi * 4 + (q & 3);
-        const int t = tok_s[m];
-        if (t >= 0) unsafeAtomicAdd(a.acc + size_t(t) * H + n, w_s[m] * acc[i][j][q]);
+        if (tok_s[m] >= 0) prow[size_t(m) * H + n] = w_s[m] * acc[i][j][q];
       }
   }
 }
@@ -582,23 +591,41 @@ __global__ void __launch_bounds__(64 * MM_WAVES) prefill_down_kernel(PrefillArgs
   }
   const int n0 = ct * MM_TN;
   // this work-group's k range [k_begin, k_begin + k_len): whole 64-deep stages except maybe the end
-  const int k_chunk = (K + 64 * a.k_split - 1) / (64 * a.k_split) * 64;
+  const int k_chunk = down_k_chunk(K, a.k_split);
   const int k_begin = kr * k_chunk;
   const int k_len = min(k_chunk, K - k_begin);
   if (k_len <= 0) return;
-  if (half_tile(a, rt, n_routed_tiles)) down_tile<true>(a, smem, Wd, K, rt, n_routed_tiles, n0, k_begin, k_len);
-  else down_tile<false>(a, smem, Wd, K, rt, n_routed_tiles, n0, k_begin, k_len);
+  if (half_tile(a, rt, n_routed_tiles)) down_tile<true>(a, smem, Wd, K, rt, n_routed_tiles, n0, kr, k_begin, k_len);
+  else down_tile<false>(a, smem, Wd, K, rt, n_routed_tiles, n0, kr, k_begin, k_len);
 }
 
-// ------------------------------------------------------------------ cast --
-
+// --------------------------------------------------------------- combine --
+// out[t] = the k routed partial rows of token t (located through the
+// dispatch's inverse permutation), each summed over its k-range planes in
+// order, then its shared-expert rows the same way; one fixed order, so the
+// output does not depend on the order in which the down tiles finished.
+// Planes of k ranges that start past a matrix's own K (a short shared or
+// routed reduction) are never written and are not read.  A thread per 4
+// outputs.
 template <int OT>
-__global__ void __launch_bounds__(256) cast_kernel(const float* __restrict__ acc, void* out, long n) {
+__global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
   const long i4 = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i4 * 4 >= n) return;
-  f32x4_t v = reinterpret_cast<const f32x4_t*>(acc)[i4];
-  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(out)[i4] = v;
-  else reinterpret_cast<u32x2_t*>(out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+  const int H4 = a.H / 4;
+  if (i4 >= long(a.T) * H4) return;
+  const int t = int(i4 / H4), h = int(i4 - long(t) * H4) * 4;
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  auto add_row = [&](long row, int planes) {
+    const float* p = a.partials + row * a.H + h;
+    for (int q = 0; q < planes; ++q) v += *reinterpret_cast<const f32x4_t*>(p + q * a.part_plane);
+  };
+  const int pr = (a.I + down_k_chunk(a.I, a.k_split) - 1) / down_k_chunk(a.I, a.k_split);
+  for (int j = 0; j < a.k; ++j) add_row(a.inv[t * a.k + j], pr);
+  if (a.S > 0) {
+    const int ps = (a.Is + down_k_chunk(a.Is, a.k_split) - 1) / down_k_chunk(a.Is, a.k_split);
+    for (int s = 0; s < a.S; ++s) add_row(long(a.capacity) + long(s) * a.t_pad + t, ps);
+  }
+  if constexpr (OT == DT_F32) reinterpret_cast<f32x4_t*>(a.out)[i4] = v;
+  else reinterpret_cast<u32x2_t*>(a.out)[i4] = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
 }
 
 // ---------------------------------------------------------------- launch --
@@ -613,6 +640,12 @@ int down_k_split(int tiles, int K) {
   int s = 1;
   while (s < 4 && tiles * s < 4 * 256 && K / (2 * s) >= 1024) s *= 2;
   return s;
+}
+
+// k ranges of the down GEMM for a shape (the host sizes the partial planes by it).
+int prefill_k_split(int capacity, int S, int t_pad, int H, int nmax) {
+  const int n_rt = capacity / MM_TM + S * (t_pad / MM_TM);
+  return down_k_split(n_rt * ((H + MM_TN - 1) / MM_TN), nmax);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, StageMarker* mark) {
@@ -645,8 +678,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int out_dt, hipStream_t st, Stag
   if (mark) mark->mark(st);
   const long n = long(a.T) * a.H;
   const int blocks = int((n / 4 + 255) / 256);
-  if (out_dt == DT_F32) hipLaunchKernelGGL(cast_kernel<DT_F32>, dim3(blocks), dim3(256), 0, st, a.acc, a.out, n);
-  else hipLaunchKernelGGL(cast_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, st, a.acc, a.out, n);
+  if (out_dt == DT_F32) hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(blocks), dim3(256), 0, st, d);
+  else hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, st, d);
   if (mark) mark->mark(st);
   return hipGetLastError();
 }
