@@ -529,6 +529,24 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
              else (["decode_fused"] if fused else ["router", "decode_gateup", "decode_down"]))
     log("[bench] stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, avg)))
 
+    # isolated calls: the stream idle before each one (synchronised), the next
+    # weight copy (cold), HIP events around the single call -- what one layer
+    # costs when nothing is queued behind or ahead of it
+    n_iso = min(10, max(2, copies))
+    iso_ev = hip.create(2 * n_iso)
+    for i in range(n_iso):
+        torch.cuda.synchronize()
+        hip.record(iso_ev[2 * i], sh)
+        step(args.warmup + args.steps + i)
+        hip.record(iso_ev[2 * i + 1], sh)
+    torch.cuda.synchronize()
+    iso = sorted(hip.elapsed_ms(iso_ev[2 * i], iso_ev[2 * i + 1]) for i in range(n_iso))
+    hip.destroy(iso_ev)
+    isolated = {"calls": n_iso, "median_ms": round(iso[len(iso) // 2], 5), "min_ms": round(iso[0], 5),
+                "max_ms": round(iso[-1], 5)}
+    log(f"[bench] isolated cold calls: median {isolated['median_ms'] * 1e3:.1f} us "
+        f"(min {isolated['min_ms'] * 1e3:.1f}, max {isolated['max_ms'] * 1e3:.1f})")
+
     # engaged experts per weight copy (from the run's own routing)
     n_active = []
     rws = torch.empty(m.moe_route_workspace_size(shape), dtype=torch.uint8, device=dev)
@@ -614,6 +632,7 @@ def measure(args, m, wl, dev, hip, probes=None, cpu_seconds=5.0):
                    "router": wl.r_dtype, "path": path_name, "weight_copies": copies,
                    "timing": timing, "parallelism": "single-gpu"},
         "spread": spread,
+        "isolated_call": isolated,
         "roofline": roof,
         "layer": layer,
         "cpu_baseline": cpu,

@@ -331,7 +331,7 @@ struct RouterArgs {
   int tile_m, capacity;
   int n_row_tiles, n_col_tiles;
   int logit_parts;      // 1: rb.logits holds the logits; 4: four group planes [4][T][E] without the bias
-  float* zero_f32;      // optional buffer to clear (prefill accumulator), or null
+  float* zero_f32;      // optional buffer to clear (the decode down launch's arrival counters), or null
   long zero_n;          // its length in floats (multiple of 4)
   RouteBufs rb;
 };

@@ -4,8 +4,8 @@
 
 namespace moe {
 
-// Side job of the prefill path: clear the fp32 combine accumulator, spread
-// over the router's grid.
+// Side job: clear a buffer the later launches of the same pass need zeroed
+// (the decode down launch's arrival counters), spread over the router's grid.
 __device__ __forceinline__ void clear_accumulator(const RouterArgs& a) {
   if (!a.zero_f32) return;
   const long n4 = a.zero_n / 4;

@@ -128,8 +128,9 @@ def test_workspace_size_and_dims(m):
     tile_m, cap, n_tiles = m.moe_dispatch_dims(s)
     assert tile_m == 128 and cap == (4096 * 2 + 8 * 127 + 127) // 128 * 128 and n_tiles * tile_m == cap
     big = m.moe_workspace_size(s)
-    # prefill needs the bf16 activations and the fp32 accumulator
-    assert big >= cap * 14336 * 2 + 4096 * 4096 * 4
+    # prefill needs the bf16 activations and the down GEMM's fp32 partial rows: two k ranges
+    # (planes) of at least the T*k routed rows
+    assert big >= cap * 14336 * 2 + 2 * (4096 * 2) * 4096 * 4
     small = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2))
     assert 0 < small < big
 
