@@ -527,6 +527,7 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       const moe::DownShape ds = pass_down_shape(s, Tc);
       d.dn_ksplit = ds.ks;
       d.dn_rpw = ds.rpw;
+      d.dn_waves = ds.waves;
     }
     d.out = oc;
     // combine in the down launch's epilogue when few work-groups write each output row group

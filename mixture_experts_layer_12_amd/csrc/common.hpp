@@ -295,15 +295,23 @@ __host__ __device__ inline bool decode_one_col_tile(int T, int k, int E) { retur
 #define MOE_DN_MIN_WAVE_STEPS 8
 #endif
 constexpr int kDownMaxKs = MOE_DN_MAX_KS;
-struct DownShape { int rpw, ks; };
+#ifndef MOE_DN_W8_MIN_GRID
+#define MOE_DN_W8_MIN_GRID 2048
+#endif
+// waves: 8 (each range cut over eight waves, two work-groups per CU) for
+// grids of two-row-tile work-groups with at least MOE_DN_W8_MIN_GRID of them
+// (Mixtral-shaped batch of 8: down 164 -> 159 us), else 4; smaller grids
+// lose with eight (batch of 1: 46.6 -> 48.7 us).
+struct DownShape { int rpw, ks, waves; };
 __host__ inline DownShape decode_down_shape(bool one_col_tile, int H, int n_slots, int steps) {
-  DownShape d{1, 1};
+  DownShape d{1, 1, 4};
   if (!one_col_tile) return d;
   if (H % 64 == 0 && (H / 64) * n_slots >= MOE_DN_RPW4_MIN_GRID) d.rpw = 4;
   else if (H % 32 == 0) d.rpw = 2;
   const long grid = long(H / (16 * d.rpw)) * n_slots;
   while (d.ks < kDownMaxKs && grid * d.ks * 2 <= MOE_DN_GRID_TARGET && steps / (4 * d.ks * 2) >= MOE_DN_MIN_WAVE_STEPS)
     d.ks *= 2;
+  if (d.rpw == 2 && grid * d.ks >= MOE_DN_W8_MIN_GRID) d.waves = 8;
   return d;
 }
 
@@ -352,6 +360,7 @@ struct DecodeArgs {
   long part_plane;      // floats per plane of partials
   int dn_ksplit;        // down: ranges the reduction over I is cut into (1 or 2), one work-group each
   int dn_rpw;           // down: row tiles of 16 outputs per work-group (1, 2 or 4; 1 with NCT 4)
+  int dn_waves;         // down: waves per work-group splitting each k range (8 with dn_rpw 2 only; else 4)
   void* out;            // [T, H]
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
   int route_in_gu;      // 1: the routed gate/up work-groups select and dispatch from the logits themselves

@@ -103,18 +103,20 @@ __global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a)
 // OT >= 0: with the combine epilogue, outputs of dtype OT (partials stored
 // with device-scope stores); OT < 0: partials only.
 // Work-group (x, slot): k range x / n_rt of row group x % n_rt.
-template <int WT, int NCT, int RPW, int OT, bool PASSES>
-__global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
-  __shared__ f32x4_t red[4][RPW * NCT][64];
+// NW waves split each k range (4, or 8 for large grids of two-row-tile
+// work-groups).
+template <int WT, int NCT, int RPW, int OT, bool PASSES, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) decode_down_kernel(DecodeArgs a) {
+  __shared__ f32x4_t red[NW][RPW * NCT][64];
   const int slot = grid_slot(a);
   const int n_rt = a.H / (16 * RPW);
   const int rt = blockIdx.x % n_rt, kr = blockIdx.x / n_rt;
   if constexpr (PASSES) {
-    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0)>(a, rt, slot, red, c0, kr, a.dn_ksplit);
+    for (int c0 = 0; down_item<WT, NCT, false, RPW, (OT >= 0), NW>(a, rt, slot, red, c0, kr, a.dn_ksplit);
          c0 += 16 * NCT)
       __syncthreads();
   } else {
-    down_item<WT, NCT, false, RPW, (OT >= 0)>(a, rt, slot, red, 0, kr, a.dn_ksplit);
+    down_item<WT, NCT, false, RPW, (OT >= 0), NW>(a, rt, slot, red, 0, kr, a.dn_ksplit);
   }
   if constexpr (OT >= 0) down_combine<OT>(a, rt, slot, RPW * 16);
 }
@@ -125,14 +127,26 @@ __global__ void __launch_bounds__(256) decode_down_kernel(DecodeArgs a) {
 // with at most 16 KiB of its own that caps the kernel at 3 work-groups per
 // CU.  Fewer concurrent weight streams per CU read HBM faster here (the
 // Mixtral-shaped batch of 8: 4 per CU 179 us, 3 per CU 176, 2 per CU 171,
-// 1 per CU 200, before the other down settings above).
+// 1 per CU 200, before the other down settings above).  Eight-wave
+// work-groups (dn_waves 8) are capped at two per CU (three: 160 us, two:
+// 159, one: 167, against 164 with four waves).
 #ifndef MOE_DN_LDS_PAD
 #define MOE_DN_LDS_PAD 36864
+#endif
+#ifndef MOE_DN_W8_LDS_PAD
+#define MOE_DN_W8_LDS_PAD 61440            // eight-wave work-groups: 16 KiB of their own, two per CU
 #endif
 template <int WT, int NCT, int OT, bool PASSES>
 static void launch_down(const DecodeArgs& a, int n_slots, hipStream_t st) {
   const dim3 b(256);
   const size_t pad = MOE_DN_LDS_PAD;
+  if constexpr (NCT == 1) {
+    if (a.dn_rpw == 2 && a.dn_waves == 8) {   // eight waves; the padding keeps two work-groups per CU
+      hipLaunchKernelGGL((decode_down_kernel<WT, 1, 2, OT, PASSES, 8>), dim3(a.H / 32 * a.dn_ksplit, n_slots), dim3(512),
+                         size_t(MOE_DN_W8_LDS_PAD), st, a);
+      return;
+    }
+  }
   if (NCT == 1 && a.dn_rpw == 4)
     hipLaunchKernelGGL((decode_down_kernel<WT, NCT, 4, OT, PASSES>), dim3(a.H / 64 * a.dn_ksplit, n_slots), b, pad, st, a);
   else if (NCT == 1 && a.dn_rpw == 2)

@@ -709,7 +709,7 @@ struct DNStep { AFrag<WT> a[RPW]; HFrag<Fam<WT>::v> h[NCT]; };
 // [4 waves][RPW * NCT][64] accumulators.
 // CST: the partial rows are stored with device-scope stores (read by another
 // work-group of the same launch); COH implies it.
-template <int WT, int NCT, bool COH, int RPW = 1, bool CST = COH>
+template <int WT, int NCT, bool COH, int RPW = 1, bool CST = COH, int NW = 4>
 __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, f32x4_t (*red)[RPW * NCT][64],
                                           int c0 = 0, int kr = 0, int ks = 1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -756,7 +756,7 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
   const int nct = (n_e - c0 + 15) >> 4;
   const int nsteps = n_steps<WT>(K);
   const int kb = kr * nsteps / ks, ke = (kr + 1) * nsteps / ks;
-  const int s0 = kb + wave * (ke - kb) / 4, s1 = kb + (wave + 1) * (ke - kb) / 4;
+  const int s0 = kb + wave * (ke - kb) / NW, s1 = kb + (wave + 1) * (ke - kb) / NW;
   f32x4_t acc[RPW][NCT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -801,7 +801,7 @@ __device__ __forceinline__ bool down_item(const DecodeArgs a, int rt, int slot, 
       if (!(NCT == 1 || ct < nct)) continue;
       f32x4_t v = red[0][r * NCT + ct][lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v += red[w][r * NCT + ct][lane];
+      for (int w = 1; w < NW; ++w) v += red[w][r * NCT + ct][lane];
       const int c = c0 + ct * 16 + (lane & 15);
       if (c >= n_e) continue;
       // lane holds rows 4*(lane/16) + 0..3 of row tile r for token column c
