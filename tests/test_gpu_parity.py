@@ -91,6 +91,11 @@ SMALL = {
     "t1_one_f32": W("t1_one_f32", T=1, H=96, E=6, k=2, I=96, S=1, Is=96,
                     x_dtype="f32", w_dtype="f32", r_dtype="f32"),
     "t1_pairs_over": W("t1_pairs_over", T=1, H=128, E=32, k=8, I=256, S=2, Is=256),
+    # down projection with each k range cut over eight waves (grids of >= 2048 two-row-tile work-groups):
+    # 16 slots with the combine in the down epilogue, and 33 slots (a shared expert) with column passes
+    # and a combine launch
+    "dn_w8_epi_t8": W("dn_w8_epi_t8", T=8, H=4096, E=16, k=2, I=128),
+    "dn_w8_passes_t32": W("dn_w8_passes_t32", T=32, H=2048, E=32, k=2, I=128, S=1, Is=128),
     # four 16-token column tiles with the combine in the down epilogue (9 slots): output row groups
     # of 16 (64 bytes), two to a 128-byte line, 10 of them (lines shared across work-groups)
     "epi_nct4_h160_t40": W("epi_nct4_h160_t40", T=40, H=160, E=8, k=2, I=64, S=1, Is=64),
