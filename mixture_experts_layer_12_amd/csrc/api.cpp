@@ -40,6 +40,9 @@ constexpr int kEpilogueMaxSlots = MOE_EPILOGUE_MAX_SLOTS;   // decode: expert sl
 constexpr long kRouteInGateUpMaxGroups = 1024;
 constexpr long kRouteInGateUpMaxGroupsTiny = 8192;
 constexpr long kTinySelection = 128;
+#ifndef MOE_SHARED_IN_LOGITS_MIN_T
+#define MOE_SHARED_IN_LOGITS_MIN_T 17
+#endif
 constexpr int kTileM = 128;          // padding multiple of the expert-sorted order (moe_route, decode)
 constexpr int kPrefillTileM = 256;   // padding multiple of the prefill path (its GEMM row tile)
 constexpr int kDecodeMaxT = 64;      // tokens per decode pass
@@ -305,7 +308,11 @@ PassPlan pass_plan(const moe_shape_t* s, int Tc) {
   p.route_in_gu = Tc <= 16 && moe::small_route(Tc, s->E, s->top_k) &&
                   gu_groups <= (tiny ? kRouteInGateUpMaxGroupsTiny : kRouteInGateUpMaxGroups);
   p.logit_parts = (nblocks < 64 && (p.route_in_gu || nblocks > 1)) ? 4 : 1;
-  p.shared_in_router = p.route_in_gu && S > 0 && p.logit_parts == 4;
+  // shared experts' gate/up in the logits launch: with the routing in the gate/up prologue, or, for
+  // one-column-tile passes of at least MOE_SHARED_IN_LOGITS_MIN_T tokens, next to a selection launch
+  p.shared_in_router = S > 0 && p.logit_parts == 4 &&
+                       (p.route_in_gu || (Tc >= MOE_SHARED_IN_LOGITS_MIN_T &&
+                                          moe::decode_one_col_tile(Tc, s->top_k, s->E)));
   return p;
 }
 
@@ -560,8 +567,8 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
       ra.zero_f32 = reinterpret_cast<float*>(d.dn_count);
       ra.zero_n = roundup(s->H / 16, 4);
     }
-    if (pro) {
-      d.route_in_gu = 1;
+    if (pro) d.route_in_gu = 1;
+    if (pro || plan.shared_in_router) {
       d.route = ra;
       d.shared_in_router = plan.shared_in_router;
     }

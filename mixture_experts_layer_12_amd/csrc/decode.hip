@@ -4,6 +4,8 @@
 
 namespace moe {
 
+void launch_router_select(const RouterArgs& a, hipStream_t st);   // router.hip
+
 // ------------------------------------------------------------- kernels --
 
 // Slot of a work-group row: the shared experts' rows of the grid come first,
@@ -12,6 +14,12 @@ namespace moe {
 __device__ __forceinline__ int grid_slot(const DecodeArgs& a) {
   const int y = blockIdx.y;
   return y < a.S ? a.n_routed_slots + y : y - a.S;
+}
+
+// Slot of a gate/up work-group row: as grid_slot, or the routed slots only
+// when the shared experts' gate/up ran in the logits launch.
+__device__ __forceinline__ int gu_slot(const DecodeArgs& a) {
+  return a.shared_in_router ? int(blockIdx.y) : grid_slot(a);
 }
 
 // PASSES: slots with more tokens than the NCT column tiles take further
@@ -31,7 +39,7 @@ __device__ __forceinline__ int grid_slot(const DecodeArgs& a) {
 template <int WT, int XT, int NCT, bool PASSES, bool PRO, bool XS = false>
 __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * NCT][64];
-  const int slot = PRO ? int(blockIdx.y) : grid_slot(a);
+  const int slot = PRO ? int(blockIdx.y) : gu_slot(a);
   if constexpr (PRO) {
     extern __shared__ __attribute__((aligned(16))) int lds[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds + small_route_ints(256, a.route.T, a.route.E, a.route.k));
@@ -70,9 +78,11 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
 // [0, 4 * tiles) compute the logits (four partial planes per 16 x 16 tile,
 // as router_logits_kernel), the rest one shared row tile each; the grid also
 // clears route.zero_f32.  XS: the shared work-groups stage the activations.
-template <int RT, int WT, int XT, bool XS>
+// SNCT: 16-token column tiles of the shared rows (4 for more than 16 tokens:
+// the shared weight rows are read once for every token).
+template <int RT, int WT, int XT, bool XS, int SNCT = 1>
 __global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a) {
-  __shared__ f32x4_t red[4][2][64];
+  __shared__ f32x4_t red[4][2 * SNCT][64];
   extern __shared__ __attribute__((aligned(16))) int lds[];
   const RouterArgs& r = a.route;
   if (r.zero_f32) {
@@ -96,7 +106,7 @@ __global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a)
     __syncthreads();
     gateup_item<WT, XT, 1, false, false, true>(a, rt, slot, red, 0, nullptr, xs);
   } else {
-    gateup_item<WT, XT, 1, false>(a, rt, slot, red);
+    for (int c0 = 0; gateup_item<WT, XT, SNCT, false>(a, rt, slot, red, c0); c0 += 16 * SNCT) __syncthreads();
   }
 }
 
@@ -191,6 +201,10 @@ static void launch_router_shared(const DecodeArgs& a, bool stage, hipStream_t st
   const int grid = 4 * a.route.n_row_tiles * a.route.n_col_tiles + a.S * ((a.Is + 15) / 16);
   const size_t logit_lds = size_t(4) * 64 * 4 * sizeof(float);
   const size_t x_lds = size_t(a.T) * a.H * 2;
+  if (a.T > 16) {
+    hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false, 4>), dim3(grid), dim3(256), logit_lds, st, a);
+    return;
+  }
   if constexpr (Fam<WT>::v == DT_Q4) {
     if (stage) {
       hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, true>), dim3(grid), dim3(256),
@@ -206,10 +220,14 @@ static void launch_decode_t(const DecodeArgs& a, int rdt, int n_gu_row_tiles, hi
   constexpr bool fp16_family = Fam<WT>::v == DT_Q4;
   // activations staged in LDS: at most kStageX8 rounds of 8 values per thread
   const bool stage = fp16_family && long(a.T) * a.H <= long(kStageX8) * 256 * 8;
-  const bool srouter = NCT == 1 && !PASSES && a.route_in_gu && a.shared_in_router;
+  // the shared experts' gate/up in the logits launch; without the routing in
+  // the gate/up prologue the selection and dispatch follow in a launch of
+  // their own
+  const bool srouter = NCT == 1 && a.shared_in_router;
   if (srouter) {
-    if (rdt == DT_F32) launch_router_shared<DT_F32, WT, XT>(a, stage, st);
-    else launch_router_shared<DT_BF16, WT, XT>(a, stage, st);
+    if (rdt == DT_F32) launch_router_shared<DT_F32, WT, XT>(a, stage && a.route_in_gu, st);
+    else launch_router_shared<DT_BF16, WT, XT>(a, stage && a.route_in_gu, st);
+    if (!a.route_in_gu) launch_router_select(a.route, st);
     if (mark) mark->mark(st);
   }
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + (srouter ? 0 : a.S)), b(256);
@@ -284,7 +302,9 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_g
                          StageMarker* mark) {
   if (a.route_in_gu && (a.T > 16 || !small_route(a.T, a.E, a.k) || a.route.tile_m != 1)) return hipErrorInvalidValue;
   if (a.slot_of && (a.E_w < 1 || !a.wg_h || !a.wu_h || !a.wd_h)) return hipErrorInvalidValue;
-  if (a.shared_in_router && (!a.route_in_gu || a.S == 0 || a.route.logit_parts != 4)) return hipErrorInvalidValue;
+  if (a.shared_in_router &&
+      (a.S == 0 || a.route.logit_parts != 4 || !decode_one_col_tile(a.T, a.k, a.E) || (a.route_in_gu && a.T > 16)))
+    return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
     return hipErrorInvalidValue;

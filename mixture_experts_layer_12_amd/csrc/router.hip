@@ -75,6 +75,18 @@ static void launch_select(const RouterArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(router_select_kernel<MODE>, dim3(1), dim3(1024), router_lds_bytes(16, a.E, a.T * a.k, true), st, a);
 }
 
+// The selection and dispatch alone, from logits already in rb.logits (one
+// plane, or four partial planes with logit_parts 4).
+void launch_router_select(const RouterArgs& a, hipStream_t st) {
+  switch (topk_mode(a.E, a.k)) {
+    case kTopkT8: launch_select<kTopkT8>(a, st); break;
+    case kTopkT16: launch_select<kTopkT16>(a, st); break;
+    case kTopkT32: launch_select<kTopkT32>(a, st); break;
+    case kTopkRow16: launch_select<kTopkRow16>(a, st); break;
+    default: launch_select<kTopkWave>(a, st); break;
+  }
+}
+
 template <int RT, int XT, int CPW>
 static void launch_logits(const RouterArgs& a, int grid, int NW, hipStream_t st) {
   hipLaunchKernelGGL((router_logits_kernel<RT, XT, CPW>), dim3(grid), dim3(NW * 64),
