@@ -264,9 +264,12 @@ typedef struct {
    * equal exactly when some wait of the last pass gave up: `out` is then not
    * valid (its affected elements hold NaN) although the call returned MOE_OK. */
   size_t status;
-  /* MOE_PATH_DECODE, last pass: 1 when the routed gate/up work-groups select
-   * and dispatch in their own prologue (the router launch computes logits
-   * only), and when the shared experts' gate/up runs in that logits launch. */
+  /* MOE_PATH_DECODE, last pass: route_in_gateup 1 when the routed gate/up
+   * work-groups select and dispatch in their own prologue (the router launch
+   * computes logits only); shared_in_router 1 when the shared experts'
+   * gate/up runs in the logits launch (with the routing in the gate/up
+   * prologue, or, for passes of more than 16 tokens with one column tile per
+   * routed slot, followed by a selection launch). */
   int32_t route_in_gateup, shared_in_router;
 } moe_forward_tables_t;
 int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t /* host */);
