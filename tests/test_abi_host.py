@@ -281,6 +281,11 @@ def test_cache_argument_errors_on_the_host(m):
     (dict(T=8, H=4096, E=8, I=14336, top_k=2, w_dtype=4), 0, 0),   # ... but not with fp8 weights
     (dict(T=8, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 0),   # too many groups
     (dict(T=40, E=16, top_k=2), 0, 0),                         # more than 16 tokens
+    # more than 16 tokens, one column tile per routed slot, shared experts: their gate/up in the
+    # logits launch, the selection in a launch of its own
+    (dict(T=64, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 1),
+    (dict(T=40, E=32, top_k=2, n_shared=1, I_shared=64), 0, 1),
+    (dict(T=40, E=16, top_k=6, n_shared=2, I_shared=64), 0, 0),   # four column tiles per slot
     (dict(T=4096, H=4096, E=8, I=14336, top_k=2), 0, 0),       # prefill
 ])
 def test_forward_tables_pass_plan(m, kw, route_in_gateup, shared_in_router):
