@@ -256,13 +256,17 @@ typedef struct {
   int32_t capacity;    /* entries of sorted_ids */
   int32_t n_tiles;     /* entries of tile_expert (0: not written) */
   size_t topk_ids, topk_w, counts, offsets, sorted_ids, tile_expert, inv, active;
-  /* MOE_PATH_DECODE_FUSED only (0 on the other paths): two uint64 words.  The
-   * single launch relies on its work-groups running at the same time; every
-   * wait between them is bounded (about a second; the environment variable
-   * MOE_FUSED_WAIT_ROUNDS, read on each call, sets the number of polling
-   * rounds).  After the call has completed on its stream the two words are
-   * equal exactly when some wait of the last pass gave up: `out` is then not
-   * valid (its affected elements hold NaN) although the call returned MOE_OK. */
+  /* MOE_PATH_DECODE_FUSED, and MOE_PATH_DECODE when the last pass selects
+   * inside its logits launch (shared_in_router without route_in_gateup; not
+   * in a captured graph, which takes a separate selection launch); 0
+   * otherwise: two uint64 words.  These forms rely on work-groups of one
+   * launch running at the same time; every wait between them is bounded
+   * (about a second; the environment variable MOE_FUSED_WAIT_ROUNDS, read on
+   * each call, sets the number of polling rounds).  After the call has
+   * completed on its stream the two words are equal exactly when some wait
+   * of the last pass gave up: `out` is then not valid (on the single-launch
+   * decode its affected elements hold NaN) although the call returned
+   * MOE_OK. */
   size_t status;
   /* MOE_PATH_DECODE, last pass: route_in_gateup 1 when the routed gate/up
    * work-groups select and dispatch in their own prologue (the router launch

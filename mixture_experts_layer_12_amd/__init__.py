@@ -250,13 +250,15 @@ def moe_forward_tables(shape: moe_shape_t) -> dict:
 
 
 def fused_status_ok(shape: moe_shape_t, workspace) -> bool:
-    """After a completed MOE_PATH_DECODE_FUSED call: True unless a wait gave up
-    (the two status words of moe_forward_tables_t are equal).  Reads 16 bytes
-    of the workspace back to the host; the caller synchronises first."""
+    """After a completed call whose shape has status words (the single-launch
+    decode, or a decode pass whose selection runs inside the logits launch):
+    True unless a wait gave up (the two status words of moe_forward_tables_t
+    are equal).  Reads 16 bytes of the workspace back to the host; the caller
+    synchronises first."""
     import torch
     o = moe_forward_tables(shape)["status"]
-    if moe_forward_tables(shape)["path"] != MOE_PATH_DECODE_FUSED:
-        raise ValueError("status words exist on the single-launch decode path only")
+    if o == 0:
+        raise ValueError("no status words for this shape and path")
     w = workspace[o:o + 16].view(torch.int64).cpu()
     return int(w[0]) != int(w[1])
 

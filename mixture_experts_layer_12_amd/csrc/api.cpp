@@ -62,7 +62,9 @@ struct Layout {
   size_t h, partials;
   int pf_ksplit;        // prefill: k ranges of the down GEMM (partial planes)
   size_t dn_count;     // multi-launch decode: down arrival counters [H / 16, rounded up to 4]
-  size_t flags, error;  // single-launch decode: completion flags [n_items], error tag
+  size_t flags, error;  // single-launch decode: completion flags [n_items]; status pair (also the decode
+                        // path's, for a selection inside the logits launch)
+  size_t sel_flags;     // multi-launch decode: completion flags of the logit work-groups
   long n_items;
   long h_plane;
   int h_stride;
@@ -215,6 +217,10 @@ Layout make_layout(const moe_shape_t* s, bool route_only) {
     }
     L.partials = take(size_t(planes) * rows * H * 4);
     L.dn_count = take(size_t(roundup(H / 16, 4)) * 4);
+    if (L.path == MOE_PATH_DECODE) {
+      L.sel_flags = take(size_t(4) * ((E + 15) / 16) * ((Tr + 15) / 16) * 8);
+      L.error = take(16);
+    }
     if (L.path == MOE_PATH_DECODE_FUSED) {
       L.n_items = fused_plan(s, Tr).n_items;
       L.flags = take(size_t(L.n_items) * 8);
@@ -378,8 +384,9 @@ int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t) {
   t->tile_expert = prefill ? L.tile_expert : 0;
   t->inv = L.inv;
   t->active = L.active;
-  t->status = L.path == MOE_PATH_DECODE_FUSED ? L.error : 0;
   const PassPlan plan = pass_plan(s, last);
+  const bool sel = L.path == MOE_PATH_DECODE && last > 0 && plan.shared_in_router && !plan.route_in_gu;
+  t->status = (L.path == MOE_PATH_DECODE_FUSED || sel) ? L.error : 0;
   t->route_in_gateup = L.path == MOE_PATH_DECODE && last > 0 && plan.route_in_gu;
   t->shared_in_router = L.path == MOE_PATH_DECODE && last > 0 && plan.shared_in_router;
   return MOE_OK;
@@ -493,15 +500,18 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
 
   // decode: passes of at most kDecodeMaxT tokens (each token's output depends on that token only).
   // The single-launch form is not captured into graphs: a replay would reuse the capture's tags.
+  // The same holds for the selection inside the logits launch (its waits compare epochs).
   bool fused = L.path == MOE_PATH_DECODE_FUSED;
-  if (fused) {
+  bool capturing = false;
+  {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
       (void)hipGetLastError();
       cs = hipStreamCaptureStatusActive;
     }
-    fused = cs == hipStreamCaptureStatusNone;
+    capturing = cs != hipStreamCaptureStatusNone;
   }
+  fused = fused && !capturing;
   for (int t0 = 0; t0 < s->T; t0 += kDecodeMaxT) {
     const int Tc = std::min(kDecodeMaxT, s->T - t0);
     const uint8_t* xc = static_cast<const uint8_t*>(x) + size_t(t0) * s->H * xb;
@@ -571,6 +581,12 @@ int forward_impl(const moe_shape_t* s, const void* x, const void* router_w, cons
     if (pro || plan.shared_in_router) {
       d.route = ra;
       d.shared_in_router = plan.shared_in_router;
+    }
+    if (plan.shared_in_router && !pro && Tc > 16 && !capturing && L.path == MOE_PATH_DECODE) {
+      d.sel_flags = reinterpret_cast<unsigned long long*>(ws + L.sel_flags);
+      d.sel_status = reinterpret_cast<unsigned long long*>(ws + L.error);
+      d.sel_epoch = next_epoch();
+      d.sel_spin = fused_spin_rounds();
     }
     if (!d.shared_in_router) {
       if (int e = hip_status(moe::launch_router(ra, s->router_dtype, s->x_dtype, router_waves(nblocks), st, pro)))

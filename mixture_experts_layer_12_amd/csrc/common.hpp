@@ -365,8 +365,15 @@ struct DecodeArgs {
   unsigned* dn_count;   // down with the combine epilogue: arrivals per output row group [H / 16]; else null
   int route_in_gu;      // 1: the routed gate/up work-groups select and dispatch from the logits themselves
   RouterArgs route;     // ... with these arguments (logits in route.rb.logits)
-  int shared_in_router; // with route_in_gu: the decode launches start with one for the router logits and
-                        // the shared experts' gate/up together; the gate/up launch covers routed slots only
+  int shared_in_router; // the decode launches start with one for the router logits and the shared
+                        // experts' gate/up together; the gate/up launch covers routed slots only
+  // shared_in_router without route_in_gu, outside graph capture (else null): the selection and
+  // dispatch run in one more work-group of that launch, which waits for the logit work-groups'
+  // completion flags (the call's epoch) for at most sel_spin polling rounds
+  unsigned long long* sel_flags;    // [logit work-groups]
+  unsigned long long* sel_status;   // status pair: this call's tag, the tag of the last call whose wait gave up
+  unsigned long long sel_epoch;
+  int sel_spin;
   // Expert cache: null, or the slot of each routed expert e in the cache's stacks wg/wu/wd
   // (E_w matrices each), -1 for an expert that is not resident, whose matrices are then read
   // from the host stacks wg_h/wu_h/wd_h (E matrices, device-mapped pinned host memory).

@@ -5,6 +5,7 @@
 namespace moe {
 
 void launch_router_select(const RouterArgs& a, hipStream_t st);   // router.hip
+size_t router_lds_bytes(int NW, int E, int n, bool stage);         // router.hip
 
 // ------------------------------------------------------------- kernels --
 
@@ -79,8 +80,14 @@ __global__ void __launch_bounds__(256) decode_gateup_kernel(DecodeArgs a) {
 // as router_logits_kernel), the rest one shared row tile each; the grid also
 // clears route.zero_f32.  XS: the shared work-groups stage the activations.
 // SNCT: 16-token column tiles of the shared rows (4 for more than 16 tokens:
-// the shared weight rows are read once for every token).
-template <int RT, int WT, int XT, bool XS, int SNCT = 1>
+// the shared weight rows are read once for every token).  SEL: the last
+// work-group selects and dispatches once every logit work-group has
+// published its planes (device-scope stores, then its flag at the call's
+// epoch); it waits at most a.sel_spin polling rounds, and after a wait that
+// gave up it stores the epoch into the error word and still selects from the
+// logits as they are (the routing tables stay well formed, the output is then
+// not valid).
+template <int RT, int WT, int XT, bool XS, int SNCT = 1, bool SEL = false>
 __global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a) {
   __shared__ f32x4_t red[4][2 * SNCT][64];
   extern __shared__ __attribute__((aligned(16))) int lds[];
@@ -93,9 +100,46 @@ __global__ void __launch_bounds__(256) decode_router_shared_kernel(DecodeArgs a)
   const int n_logit = 4 * r.n_row_tiles * r.n_col_tiles;
   if (int(blockIdx.x) < n_logit) {
     const int tile = blockIdx.x >> 2, q = blockIdx.x & 3;
-    logits_tile<RT, XT, false, 1>(r, tile % r.n_row_tiles, tile / r.n_row_tiles, 4 * q, 4,
-                                  reinterpret_cast<float*>(lds), r.rb.logits + size_t(q) * r.T * r.E);
+    logits_tile<RT, XT, SEL, 1>(r, tile % r.n_row_tiles, tile / r.n_row_tiles, 4 * q, 4,
+                                reinterpret_cast<float*>(lds), r.rb.logits + size_t(q) * r.T * r.E);
+    if constexpr (SEL) {          // the planes have reached memory, then the flag
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.sel_flags + blockIdx.x, a.sel_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
+  }
+  if constexpr (SEL) {
+    if (blockIdx.x == gridDim.x - 1) {
+      __shared__ int s_ok;
+      if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        if (lane == 0) __hip_atomic_store(a.sel_status, a.sel_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool done = false;
+        for (int it = 0; it < a.sel_spin && !done; ++it) {
+          bool mine = true;
+          for (int i = lane; i < n_logit; i += 64)
+            mine = mine && __hip_atomic_load(a.sel_flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.sel_epoch;
+          done = __all(mine);
+          if (!done) __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) {
+          s_ok = done ? 1 : 0;
+          if (!done) __hip_atomic_store(a.sel_status + 1, a.sel_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+      (void)s_ok;
+      switch (topk_mode(r.E, r.k)) {
+        case kTopkT8: select_and_dispatch<true, kTopkT8>(r, r.rb.logits, false, lds); break;
+        case kTopkT16: select_and_dispatch<true, kTopkT16>(r, r.rb.logits, false, lds); break;
+        case kTopkT32: select_and_dispatch<true, kTopkT32>(r, r.rb.logits, false, lds); break;
+        case kTopkRow16: select_and_dispatch<true, kTopkRow16>(r, r.rb.logits, false, lds); break;
+        default: select_and_dispatch<true, kTopkWave>(r, r.rb.logits, false, lds); break;
+      }
+      return;
+    }
   }
   const int j = blockIdx.x - n_logit, gu_rt = (a.Is + 15) / 16;
   const int slot = a.n_routed_slots + j / gu_rt, rt = j % gu_rt;
@@ -202,7 +246,20 @@ static void launch_router_shared(const DecodeArgs& a, bool stage, hipStream_t st
   const size_t logit_lds = size_t(4) * 64 * 4 * sizeof(float);
   const size_t x_lds = size_t(a.T) * a.H * 2;
   if (a.T > 16) {
-    hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false, 4>), dim3(grid), dim3(256), logit_lds, st, a);
+    if (a.sel_flags) {            // one more work-group selects and dispatches
+      static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(decode_router_shared_kernel<RT, WT, XT, false, 4, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  int(router_lds_bytes(4, 256, kRouterIdsLds, true)));
+        return true;
+      }();
+      (void)attr;
+      const size_t sel_lds = router_lds_bytes(4, a.E, a.T * a.k, true);
+      hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false, 4, true>), dim3(grid + 1), dim3(256),
+                         sel_lds > logit_lds ? sel_lds : logit_lds, st, a);
+    } else {
+      hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false, 4>), dim3(grid), dim3(256), logit_lds, st, a);
+    }
     return;
   }
   if constexpr (Fam<WT>::v == DT_Q4) {
@@ -227,7 +284,7 @@ static void launch_decode_t(const DecodeArgs& a, int rdt, int n_gu_row_tiles, hi
   if (srouter) {
     if (rdt == DT_F32) launch_router_shared<DT_F32, WT, XT>(a, stage && a.route_in_gu, st);
     else launch_router_shared<DT_BF16, WT, XT>(a, stage && a.route_in_gu, st);
-    if (!a.route_in_gu) launch_router_select(a.route, st);
+    if (!a.route_in_gu && !a.sel_flags) launch_router_select(a.route, st);
     if (mark) mark->mark(st);
   }
   dim3 g1(n_gu_row_tiles, a.n_routed_slots + (srouter ? 0 : a.S)), b(256);
@@ -305,6 +362,7 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_g
   if (a.shared_in_router &&
       (a.S == 0 || a.route.logit_parts != 4 || !decode_one_col_tile(a.T, a.k, a.E) || (a.route_in_gu && a.T > 16)))
     return hipErrorInvalidValue;
+  if (a.sel_flags && (!a.shared_in_router || a.route_in_gu || a.T <= 16 || !a.sel_status)) return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
     return hipErrorInvalidValue;

@@ -111,10 +111,12 @@ def test_resolve_path(m):
 def test_single_launch_decode_workspace(m):
     """The single-launch decode adds completion flags to the decode workspace;
     the multi-launch decode of the same shape cuts its down projection into 2
-    k ranges instead and holds one more plane of partial rows."""
+    k ranges instead and holds one more plane of partial rows, and the flags
+    and status pair of a selection inside the logits launch (one aligned
+    block each)."""
     fused = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE_FUSED))
     multi = m.moe_workspace_size(m.make_shape(8, 4096, 8, 14336, 2, path=m.MOE_PATH_DECODE))
-    plane = 16 * 4096 * 4              # T*k = 16 partial rows of H = 4096 floats
+    plane = 16 * 4096 * 4 + 2 * 256    # T*k = 16 partial rows of H = 4096 floats; selection flags, status
 
     # work list: 4 logits planes, 1 selection, 8 x 896 gate/up tiles, 8 x 128 down row groups (32 outputs
     # each), 32 combine blocks

@@ -487,6 +487,41 @@ def test_graph_replay_matches_eager(m, name, path):
                            eager.view(torch.int16) if eager.dtype == torch.bfloat16 else eager), r
 
 
+@pytest.mark.parametrize("name", ["e32_t40_passes", "dn_w8_passes_t32"])
+def test_selection_in_logits_launch_reports_a_wait_that_gives_up(m, name):
+    """A decode pass of more than 16 tokens with shared experts selects inside
+    the logits launch, in a work-group that waits for the logit work-groups'
+    flags.  With the wait bound forced to 0 from the host the wait gives up at
+    once: every kernel still exits, the routing tables stay well formed (the
+    selection runs on whatever logits are there) and the status words report
+    it; a normal call afterwards reports success and matches the oracle."""
+    import os
+    import torch
+    wl = SMALL[name]
+    shape = H.shape_of(m, wl, 1)
+    assert m.moe_forward_tables(shape)["shared_in_router"] == 1
+    t = synth.to_torch(_inputs(wl, 13))
+    ws = m.alloc_workspace(shape)
+    ws.fill_(0x3C)
+    old = os.environ.get("MOE_FUSED_WAIT_ROUNDS")
+    os.environ["MOE_FUSED_WAIT_ROUNDS"] = "0"
+    try:
+        H.run_forward(m, wl, t, path=1, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["MOE_FUSED_WAIT_ROUNDS"]
+        else:
+            os.environ["MOE_FUSED_WAIT_ROUNDS"] = old
+    assert not m.fused_status_ok(shape, ws)
+    out = H.run_forward(m, wl, t, path=1, ws=ws)
+    torch.cuda.synchronize()
+    assert m.fused_status_ok(shape, ws)
+    inp = _inputs(wl, 13)
+    ref = H.oracle_layer(wl, inp)
+    assert H.relerr(H.to_f64(out), ref["out"]) <= H.tolerance(wl)
+
+
 @pytest.mark.parametrize("name", ["deepseek_small_t8", "qwen_small_q4_t1", "e32_t40_passes"])
 def test_single_launch_decode_reports_a_wait_that_gives_up(m, name):
     """The single-launch decode with its wait bound forced to 0 from the host:
