@@ -458,7 +458,9 @@ def test_full_size_decode_paths_agree(m, full_inputs, name):
 
 
 @pytest.mark.parametrize("name, path", [("deepseek_small_t40", 1), ("qwen_small_q4_t5", 0),
-                                        ("deepseek_small_t8", 3), ("prefill_small_zipf", 2)])
+                                        ("deepseek_small_t8", 3), ("prefill_small_zipf", 2),
+                                        # eager: selection inside the logits launch; captured: its own launch
+                                        ("e32_t40_passes", 1)])
 def test_graph_replay_matches_eager(m, name, path):
     """The layer captured into a HIP graph: several replays, with eager work and
     synchronisations between them, each equal to the eager result.  (A captured
