@@ -272,8 +272,8 @@ typedef struct {
    * work-groups select and dispatch in their own prologue (the router launch
    * computes logits only); shared_in_router 1 when the shared experts'
    * gate/up runs in the logits launch (with the routing in the gate/up
-   * prologue, or, for passes of more than 16 tokens with one column tile per
-   * routed slot, followed by a selection launch). */
+   * prologue, or, for one column tile per routed slot, with the selection in
+   * one more work-group of that launch). */
   int32_t route_in_gateup, shared_in_router;
 } moe_forward_tables_t;
 int moe_forward_tables(const moe_shape_t* s, moe_forward_tables_t* t /* host */);

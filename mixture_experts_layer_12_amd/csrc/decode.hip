@@ -262,6 +262,19 @@ static void launch_router_shared(const DecodeArgs& a, bool stage, hipStream_t st
     }
     return;
   }
+  if (a.sel_flags) {              // one column tile per shared row, one more work-group selects
+    static const bool attr = [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(decode_router_shared_kernel<RT, WT, XT, false, 1, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(router_lds_bytes(4, 256, kRouterIdsLds, true)));
+      return true;
+    }();
+    (void)attr;
+    const size_t sel_lds = router_lds_bytes(4, a.E, a.T * a.k, true);
+    hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, false, 1, true>), dim3(grid + 1), dim3(256),
+                       sel_lds > logit_lds ? sel_lds : logit_lds, st, a);
+    return;
+  }
   if constexpr (Fam<WT>::v == DT_Q4) {
     if (stage) {
       hipLaunchKernelGGL((decode_router_shared_kernel<RT, WT, XT, true>), dim3(grid), dim3(256),
@@ -362,7 +375,7 @@ hipError_t launch_decode(const DecodeArgs& a, int wdt, int xdt, int rdt, int n_g
   if (a.shared_in_router &&
       (a.S == 0 || a.route.logit_parts != 4 || !decode_one_col_tile(a.T, a.k, a.E) || (a.route_in_gu && a.T > 16)))
     return hipErrorInvalidValue;
-  if (a.sel_flags && (!a.shared_in_router || a.route_in_gu || a.T <= 16 || !a.sel_status)) return hipErrorInvalidValue;
+  if (a.sel_flags && (!a.shared_in_router || a.route_in_gu || !a.sel_status)) return hipErrorInvalidValue;
   if (a.dn_ksplit < 1 || a.dn_ksplit > kDownMaxKs || (a.dn_rpw != 1 && a.dn_rpw != 2 && a.dn_rpw != 4) ||
       a.H % (16 * a.dn_rpw) != 0)
     return hipErrorInvalidValue;

@@ -281,10 +281,12 @@ def test_cache_argument_errors_on_the_host(m):
     (dict(T=1, H=2048, E=256, I=512, top_k=8, n_shared=1, I_shared=512, w_dtype=2), 1, 1),  # Qwen-A3B-shaped
     (dict(T=8, H=4096, E=8, I=14336, top_k=2), 1, 0),          # tiny selection on a large grid
     (dict(T=8, H=4096, E=8, I=14336, top_k=2, w_dtype=4), 0, 0),   # ... but not with fp8 weights
-    (dict(T=8, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 0),   # too many groups
+    # too many groups for the routing in the gate/up prologue: the shared gate/up and the selection
+    # in the logits launch
+    (dict(T=8, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 1),
     (dict(T=40, E=16, top_k=2), 0, 0),                         # more than 16 tokens
-    # more than 16 tokens, one column tile per routed slot, shared experts: their gate/up in the
-    # logits launch, the selection in a launch of its own
+    # more than 16 tokens, one column tile per routed slot, shared experts: their gate/up and the
+    # selection in the logits launch
     (dict(T=64, H=2048, E=64, I=1408, top_k=6, n_shared=2, I_shared=1408), 0, 1),
     (dict(T=40, E=32, top_k=2, n_shared=1, I_shared=64), 0, 1),
     (dict(T=40, E=16, top_k=6, n_shared=2, I_shared=64), 0, 0),   # four column tiles per slot
